@@ -1,0 +1,211 @@
+"""Benchmark: dispatch + combine per layer on one MI355X.
+
+One step = one pass of the high-throughput hot path over one batch:
+get_dispatch_layout (counts, is_token_in_rank, prefix offsets) -> dispatch
+(rank-deduplicated pack + expert-major permute) -> combine (top-k weighted
+fp32 reduction back to bf16), on the prefill workload T=4096, h=7168, E=256,
+R=32 (8 experts per logical rank), topk=8, bf16. Buffers are preallocated at
+worst-case capacity, so the timed region holds no host wait and no
+allocation. Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. ``value`` is HBM GB/s over the compulsory bytes of the
+step (each required input read once, each required output written once);
+``ms_per_step`` is the wall time per step. ``roofline`` covers the dominant
+kernel (dispatch) timed with HIP events on its stream; ``cpu_baseline``
+times the CPU oracle (single thread) on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "dispatch+combine µs/layer and HBM GB/s (% peak) at T=4096,h=7168,topk=8"
+
+
+def step_bytes(T, h, K, R, n_rank, n_exp):
+    """Compulsory bytes per kernel (bf16 rows of 2h bytes)."""
+    row = 2 * h
+    layout = 8 * T * K + T * R + 4 * T * R + 4 * T * K
+    dispatch = (T * row + 8 * T * K + 4 * T * K          # x, topk_idx, topk_w
+                + 4 * T * K + 4 * n_rank                  # slot_in_expert, the pos_in_rank hits
+                + n_rank * row + n_exp * row              # send_x, recv_x
+                + 4 * n_rank + 12 * n_rank * K            # send_src, send_topk_idx/w
+                + 4 * n_exp + 4 * T * K)                  # recv_src, pos_exp
+    combine = n_exp * row + 8 * T * K + T * row          # rows, pos + weights, out
+    return dict(layout=layout, dispatch=dispatch, combine=combine)
+
+
+def survey_bmin(T, h, K, R, n_rank, n_exp):
+    """The whole-step compulsory byte count used for `value`."""
+    row = 2 * h
+    disp = T * row + 12 * T * K + n_rank * row + n_exp * row + (
+        T * R + 4 * (T * R + T * K) + 4 * (n_rank + n_exp) + 12 * n_rank * K)
+    comb = n_exp * row + 16 * T * K + T * row
+    return disp + comb
+
+
+def cpu_baseline(inp, wl, target_s=12.0, max_reps=5):
+    """Time the oracle (single-threaded C) on the same workload: layout,
+    dispatch and combine, repeated until about `target_s` seconds of work."""
+    import numpy as np
+
+    import oracle
+
+    y = np.random.default_rng(9).integers(0, 1 << 16, (wl.T * wl.K, wl.h), dtype=np.uint16)
+    y &= np.uint16(0xBFFF)  # keep values finite (exponent below all-ones)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_reps:
+        t0 = time.perf_counter()
+        lay = oracle.layout(inp["topk_idx"], wl.E, wl.R)
+        d = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, lay=lay)
+        oracle.combine(y[: int(lay["totals"][1])], inp["topk_w"], d["pos_exp"])
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > target_s:
+            break
+    n_rank, n_exp = (int(v) for v in lay["totals"])
+    med = statistics.median(times)
+    return med, n_rank, n_exp, len(times)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="MALL flush size for the labelled cold-cache figure (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the one-GPU share of the path; runs on more than one GPU "
+              "are not part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_get_dispatch_counts_amd as epx
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    inp = synth.make_inputs(3)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    tk = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    cap_send, cap_recv = T * min(K, R), T * K
+    bufs = epx.alloc_dispatch(T, h, K, cap_send, cap_recv, False, dev)
+    ws = torch.empty(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    expert_out = synth.expert_outputs(cap_recv, h, seed=4242, device="cuda")
+    out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        lay = epx.get_dispatch_layout(tk, E, R, workspace=ws)
+        if ev:
+            ev[1].record()
+        d = epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs)
+        if ev:
+            ev[2].record()
+        epx.combine(expert_out, d.pos_exp, w, out=out)
+        if ev:
+            ev[3].record()
+        return lay
+
+    for _ in range(args.warmup):
+        lay = step()
+    torch.cuda.synchronize()
+    assert epx.get_error() == 0
+    n_rank, n_exp = (int(v) for v in lay.totals.cpu())
+
+    # timed region: K back-to-back steps, events around each kernel group
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    phase = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3
+             for j, name in enumerate(["layout", "dispatch", "combine"])}
+    assert epx.get_error() == 0
+
+    # labelled cold-cache figure: flush the 256 MB MALL before each step
+    cold_us = None
+    if args.flush_mb > 0:
+        scratch = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for i in range(min(args.steps, 20)):
+            scratch.fill_(i & 0xFF)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            step(e)
+            torch.cuda.synchronize()
+            cold.append(e[0].elapsed_time(e[3]) * 1e3)
+        cold_us = statistics.median(cold)
+        del scratch
+
+    by = step_bytes(T, h, K, R, n_rank, n_exp)
+    bmin = survey_bmin(T, h, K, R, n_rank, n_exp)
+    gbs = bmin / (ms_per_step * 1e-3) / 1e9
+    disp_gbs = by["dispatch"] / (phase["dispatch"] * 1e-6) / 1e9
+    comb_gbs = by["combine"] / (phase["combine"] * 1e-6) / 1e9
+    b_flow = bmin + n_rank * 2 * h
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        med, nr, ne, reps = cpu_baseline(inp, wl)
+        cpu = {"value": round(survey_bmin(T, h, K, R, nr, ne) / med / 1e9, 3), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"the full prefill workload (T={T}, one layer: layout+dispatch+combine), "
+                         f"median of {reps} single-threaded runs, {med * 1e3:.0f} ms each"}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill T={T} h={h} E={E} R={R} topk={K} bf16, "
+                               "high-throughput layout+dispatch+combine",
+                   "T": T, "hidden": h, "num_experts": E, "num_ranks": R, "topk": K,
+                   "n_rank_rows": n_rank, "n_expert_rows": n_exp},
+        "us_per_layer": round(ms_per_step * 1e3, 2),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "b_min_bytes": bmin,
+        "b_flow_gbs": round(b_flow / (ms_per_step * 1e-3) / 1e9, 1),
+        "phase_us": {k: round(v, 2) for k, v in phase.items()},
+        "phase_gbs": {"dispatch": round(disp_gbs, 1), "combine": round(comb_gbs, 1)},
+        "cold_cache_us_per_layer": round(cold_us, 2) if cold_us else None,
+        "roofline": {"bound": "hbm", "achieved": round(disp_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(disp_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "dispatch_kernel<bf16>",
+                     "bytes_per_launch": by["dispatch"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

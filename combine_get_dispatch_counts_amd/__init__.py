@@ -1,0 +1,30 @@
+"""MI355X-native single-GPU hot path of DeepEP-style MoE dispatch / combine.
+
+The work runs in hand-written HIP kernels for gfx950 behind the C ABI of
+``libepx.so`` (include/epx.h); this package is the torch binding. Every call
+loads the library first and raises ImportError if it has not been built --
+there is no fallback implementation. (Importing the package itself does not
+need the library, so ``python -m combine_get_dispatch_counts_amd.build`` can
+run before it exists.)
+"""
+from ._lib import EpxError
+
+from .api import (  # noqa: E402
+    Dispatched,
+    Layout,
+    LowLatency,
+    alloc_dispatch,
+    alloc_ll,
+    combine,
+    dispatch,
+    get_dispatch_layout,
+    get_error,
+    ll_dispatch,
+    ll_reset,
+    ll_size_hint,
+    workspace_size,
+)
+
+__all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
+           "get_error", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
+           "ll_reset", "alloc_ll", "ll_dispatch"]

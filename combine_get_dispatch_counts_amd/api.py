@@ -1,0 +1,262 @@
+"""Thin torch binding over libepx: tensors in, tensors out.
+
+Every step of the path runs in the HIP kernels behind the C ABI; this module
+only allocates output tensors with torch (device memory), takes the current
+HIP stream, and marshals pointers and sizes. Names follow the C ABI
+(epx_get_dispatch_layout -> get_dispatch_layout, and so on).
+
+Shapes: x [T,h] bf16; topk_idx [T,K] int64 (-1 = no route); topk_weights
+[T,K] fp32. Destination ranks are logical partitions of the experts:
+rank r holds experts [r*L, (r+1)*L), L = num_experts // num_ranks.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import EpxError, check
+
+_contexts: dict[int, ctypes.c_void_p] = {}
+
+
+def _ctx(device: torch.device) -> ctypes.c_void_p:
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _contexts:
+        h = ctypes.c_void_p()
+        check(_lib.load().epx_create(ctypes.byref(h), idx), "epx_create")
+        _contexts[idx] = h
+    return _contexts[idx]
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _p(t: torch.Tensor | None) -> ctypes.c_void_p | None:
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def workspace_size(T: int, K: int, E: int, R: int) -> int:
+    n = ctypes.c_size_t()
+    check(_lib.load().epx_workspace_size(T, K, E, R, ctypes.byref(n)), "epx_workspace_size")
+    return n.value
+
+
+def ll_size_hint(max_tokens_per_rank: int, h: int, R: int, E: int, fp8: bool) -> int:
+    return int(_lib.load().epx_ll_size_hint(max_tokens_per_rank, h, R, E, int(fp8)))
+
+
+def get_error(device: torch.device | None = None) -> int:
+    """Synchronise the current stream, return and clear the device error bits."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    flags = ctypes.c_int()
+    rc = _lib.load().epx_get_error(_ctx(device), ctypes.byref(flags), _stream(device))
+    if rc not in (_lib.EPX_OK, _lib.EPX_EDEVICE):
+        check(rc, "epx_get_error")
+    return flags.value
+
+
+@dataclass
+class Layout:
+    num_tokens_per_expert: torch.Tensor  # [E] int32
+    num_tokens_per_rank: torch.Tensor    # [R] int32
+    is_token_in_rank: torch.Tensor       # [T,R] uint8
+    rank_off: torch.Tensor               # [R+1] int32
+    exp_off: torch.Tensor                # [E+1] int32
+    pos_in_rank: torch.Tensor            # [T,R] int32
+    slot_in_expert: torch.Tensor         # [T,K] int32
+    channel_prefix: torch.Tensor | None  # [R,C] int32
+    totals: torch.Tensor                 # [2] int32 (send rows, recv rows)
+    num_experts: int
+    num_ranks: int
+
+
+def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                        num_channels: int | None = None, workspace: torch.Tensor | None = None,
+                        totals_host: torch.Tensor | None = None) -> Layout:
+    _need(topk_idx, torch.int64, "topk_idx", 2)
+    dev = topk_idx.device
+    T, K = topk_idx.shape
+    E, R = num_experts, num_ranks
+    i32 = dict(dtype=torch.int32, device=dev)
+    lay = Layout(
+        num_tokens_per_expert=torch.empty(E, **i32),
+        num_tokens_per_rank=torch.empty(R, **i32),
+        is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
+        rank_off=torch.empty(R + 1, **i32),
+        exp_off=torch.empty(E + 1, **i32),
+        pos_in_rank=torch.empty((T, R), **i32),
+        slot_in_expert=torch.empty((T, K), **i32),
+        channel_prefix=torch.empty((R, num_channels), **i32) if num_channels else None,
+        totals=torch.empty(2, **i32),
+        num_experts=E, num_ranks=R)
+    need = workspace_size(T, K, E, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if totals_host is not None and not (totals_host.is_pinned() and totals_host.numel() >= 2
+                                        and totals_host.dtype == torch.int32):
+        raise ValueError("totals_host must be a pinned int32 tensor of >= 2 elements")
+    rc = _lib.load().epx_get_dispatch_layout(
+        _ctx(dev), _p(topk_idx), T, K, E, R, num_channels or 0,
+        _p(lay.num_tokens_per_expert), _p(lay.num_tokens_per_rank), _p(lay.is_token_in_rank),
+        _p(lay.rank_off), _p(lay.exp_off), _p(lay.pos_in_rank), _p(lay.slot_in_expert),
+        _p(lay.channel_prefix), _p(lay.totals), _p(totals_host), _p(workspace),
+        workspace.numel(), _stream(dev))
+    check(rc, "epx_get_dispatch_layout")
+    return lay
+
+
+@dataclass
+class Dispatched:
+    send_x: torch.Tensor          # [rows, h] bf16, or uint8 codes with fp8
+    send_scales: torch.Tensor | None
+    send_src: torch.Tensor        # [rows] int32
+    send_topk_idx: torch.Tensor   # [rows, K] int64
+    send_topk_w: torch.Tensor     # [rows, K] fp32
+    recv_x: torch.Tensor          # [rows, h] expert-major
+    recv_scales: torch.Tensor | None
+    recv_src: torch.Tensor        # [rows] int32
+    pos_exp: torch.Tensor         # [T, K] int32 -- the handle for combine
+    layout: Layout
+
+
+def alloc_dispatch(T: int, h: int, K: int, send_rows: int, recv_rows: int, fp8: bool,
+                   device: torch.device) -> dict:
+    """Output buffers for dispatch with the given row capacities."""
+    dt = torch.uint8 if fp8 else torch.bfloat16
+    f32 = dict(dtype=torch.float32, device=device)
+    return dict(
+        send_x=torch.empty((send_rows, h), dtype=dt, device=device),
+        send_scales=torch.empty((send_rows, h // 128), **f32) if fp8 else None,
+        send_src=torch.empty(send_rows, dtype=torch.int32, device=device),
+        send_topk_idx=torch.empty((send_rows, K), dtype=torch.int64, device=device),
+        send_topk_w=torch.empty((send_rows, K), **f32),
+        recv_x=torch.empty((recv_rows, h), dtype=dt, device=device),
+        recv_scales=torch.empty((recv_rows, h // 128), **f32) if fp8 else None,
+        recv_src=torch.empty(recv_rows, dtype=torch.int32, device=device),
+        pos_exp=torch.empty((T, K), dtype=torch.int32, device=device))
+
+
+def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
+             num_experts: int, num_ranks: int, fp8: bool = False, layout: Layout | None = None,
+             out: dict | None = None, exact: bool = True) -> Dispatched:
+    """Rank-deduplicated pack + expert-major permute (+ FP8).
+
+    Buffers: ``out`` (from alloc_dispatch) if given; else, with ``exact``,
+    one host wait on the layout totals sizes them exactly (the pages' CPU
+    wait before allocating the receive tensor); otherwise worst-case sizes
+    T*min(K,R) and T*K rows are used and no wait happens."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(topk_idx, torch.int64, "topk_idx", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    dev = x.device
+    T, h = x.shape
+    K = topk_idx.shape[1]
+    if topk_idx.shape[0] != T or tuple(topk_weights.shape) != (T, K):
+        raise ValueError("x, topk_idx and topk_weights disagree on T or K")
+    if layout is None:
+        layout = get_dispatch_layout(topk_idx, num_experts, num_ranks)
+    if out is None:
+        if exact:
+            n_send, n_recv = (int(v) for v in layout.totals.cpu())
+        else:
+            n_send, n_recv = T * min(K, num_ranks), T * K
+        out = alloc_dispatch(T, h, K, n_send, n_recv, fp8, dev)
+    rc = _lib.load().epx_dispatch(
+        _ctx(dev), _p(x), h, _p(topk_idx), _p(topk_weights), T, K, num_experts, num_ranks,
+        _p(layout.rank_off), _p(layout.exp_off), _p(layout.pos_in_rank),
+        _p(layout.slot_in_expert), int(fp8),
+        _p(out["send_x"]), _p(out["send_scales"]), _p(out["send_src"]),
+        _p(out["send_topk_idx"]), _p(out["send_topk_w"]), out["send_x"].shape[0],
+        _p(out["recv_x"]), _p(out["recv_scales"]), _p(out["recv_src"]), out["recv_x"].shape[0],
+        _p(out["pos_exp"]), _stream(dev))
+    check(rc, "epx_dispatch")
+    return Dispatched(layout=layout, **out)
+
+
+def combine(expert_out: torch.Tensor, pos: torch.Tensor, topk_weights: torch.Tensor,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """out[t] = bf16(sum over valid k, in k order, of w[t,k] * expert_out[pos[t,k]])."""
+    _need(expert_out, torch.bfloat16, "expert_out", 2)
+    _need(pos, torch.int32, "pos", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    dev = expert_out.device
+    T, K = pos.shape
+    h = expert_out.shape[1]
+    if out is None:
+        out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    rc = _lib.load().epx_combine(_ctx(dev), _p(expert_out), expert_out.shape[0], h,
+                                 _p(topk_weights), _p(pos), T, K, _p(out), _stream(dev))
+    check(rc, "epx_combine")
+    return out
+
+
+def ll_reset(ll_count: torch.Tensor) -> None:
+    _need(ll_count, torch.int32, "ll_count")
+    dev = ll_count.device
+    check(_lib.load().epx_ll_reset(_ctx(dev), _p(ll_count), ll_count.numel(), _stream(dev)),
+          "epx_ll_reset")
+
+
+@dataclass
+class LowLatency:
+    ll_x: torch.Tensor              # [E*R_buf*cap, h] bf16 or uint8
+    ll_scales: torch.Tensor | None  # [E*R_buf*cap, h/128] fp32
+    ll_src: torch.Tensor            # [E*R_buf*cap] int32
+    ll_count: torch.Tensor          # [E*R_buf] int32
+    pos_ll: torch.Tensor            # [T,K] int32 -- the handle for combine
+
+
+def alloc_ll(E: int, R_buf: int, cap: int, h: int, T: int, K: int, fp8: bool,
+             device: torch.device) -> LowLatency:
+    rows = E * R_buf * cap
+    buf = LowLatency(
+        ll_x=torch.empty((rows, h), dtype=torch.uint8 if fp8 else torch.bfloat16, device=device),
+        ll_scales=torch.empty((rows, h // 128), dtype=torch.float32, device=device) if fp8 else None,
+        ll_src=torch.empty(rows, dtype=torch.int32, device=device),
+        ll_count=torch.empty(E * R_buf, dtype=torch.int32, device=device),
+        pos_ll=torch.empty((T, K), dtype=torch.int32, device=device))
+    ll_reset(buf.ll_count)
+    return buf
+
+
+def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                src_rank: int, cap: int, R_buf: int | None = None, fp8: bool = True,
+                buf: LowLatency | None = None) -> LowLatency:
+    """Fixed-slot low-latency dispatch (one launch, no host wait). ``buf``
+    must come from alloc_ll (its counts start at -1)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(topk_idx, torch.int64, "topk_idx", 2)
+    dev = x.device
+    T, h = x.shape
+    K = topk_idx.shape[1]
+    R_buf = num_ranks if R_buf is None else R_buf
+    if buf is None:
+        buf = alloc_ll(num_experts, R_buf, cap, h, T, K, fp8, dev)
+    rc = _lib.load().epx_ll_dispatch(
+        _ctx(dev), _p(x), h, _p(topk_idx), T, K, num_experts, num_ranks, src_rank, cap, R_buf,
+        int(fp8), _p(buf.ll_x), _p(buf.ll_scales), _p(buf.ll_src), _p(buf.ll_count),
+        _p(buf.pos_ll), _stream(dev))
+    check(rc, "epx_ll_dispatch")
+    return buf
+
+
+__all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
+           "get_error", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
+           "ll_reset", "alloc_ll", "ll_dispatch"]

@@ -1,0 +1,306 @@
+// epx_api.hip -- the C ABI declared in include/epx.h: argument checks, then
+// kernel launches on the caller's stream. No call here allocates device
+// memory except epx_create (the 4-byte device error word), and no call waits
+// for the GPU except epx_get_error.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <hip/hip_runtime.h>
+
+#include "epx.h"
+#include "epx_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_routing(int T, int K, int E, int R)
+{
+    if (T < 0 || K < 1 || K > EPX_MAX_TOPK || E < 1 || E > EPX_MAX_EXPERTS || R < 1 ||
+        R > EPX_MAX_RANKS || E % R != 0)
+        return EPX_EINVAL;
+    if ((int64_t)T * K > INT32_MAX)
+        return EPX_EINVAL;
+    return EPX_OK;
+}
+
+int check_hidden(int h, int fp8)
+{
+    if (h < 8 || h % 8 != 0)
+        return EPX_EINVAL;
+    if (fp8 && h % 128 != 0)
+        return EPX_EUNSUPPORTED;
+    return EPX_OK;
+}
+
+// The context's device must be the current one: kernels launch there.
+int check_ctx(const epx_ctx *ctx)
+{
+    if (!ctx)
+        return EPX_EINVAL;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return EPX_EHIP;
+    return cur == ctx->device ? EPX_OK : EPX_EINVAL;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? EPX_OK : EPX_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int epx_create(epx_ctx **out, int device)
+{
+    if (!out)
+        return EPX_EINVAL;
+    *out = nullptr;
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess)
+        return EPX_EHIP;
+    if (device < 0 || device >= n)
+        return EPX_EINVAL;
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess)
+        return EPX_EHIP;
+    epx_ctx *c = static_cast<epx_ctx *>(calloc(1, sizeof(epx_ctx)));
+    int rc = EPX_OK;
+    if (!c) {
+        rc = EPX_EHIP;
+    } else {
+        c->device = device;
+        if (hipMalloc(reinterpret_cast<void **>(&c->d_err), sizeof(int)) != hipSuccess ||
+            hipMemset(c->d_err, 0, sizeof(int)) != hipSuccess) {
+            if (c->d_err)
+                (void)hipFree(c->d_err);
+            free(c);
+            c = nullptr;
+            rc = EPX_EHIP;
+        }
+    }
+    (void)hipSetDevice(prev);
+    *out = c;
+    return rc;
+}
+
+int epx_destroy(epx_ctx *ctx)
+{
+    if (!ctx)
+        return EPX_EINVAL;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(ctx->device);
+    const hipError_t e = hipFree(ctx->d_err);
+    (void)hipSetDevice(prev);
+    free(ctx);
+    return e == hipSuccess ? EPX_OK : EPX_EHIP;
+}
+
+const char *epx_strerror(int code)
+{
+    switch (code) {
+    case EPX_OK: return "ok";
+    case EPX_EINVAL: return "invalid argument (shape, parameter, pointer or device)";
+    case EPX_ECAPACITY: return "capacity exceeded (T > cap, or workspace too small)";
+    case EPX_EUNSUPPORTED: return "unsupported (FP8 needs h % 128 == 0)";
+    case EPX_EHIP: return "HIP runtime or launch error";
+    case EPX_EDEVICE: return "a kernel reported an error (see the device flags)";
+    default: return "unknown error code";
+    }
+}
+
+int epx_workspace_size(int T, int K, int E, int R, size_t *bytes)
+{
+    if (!bytes)
+        return EPX_EINVAL;
+    const int rc = check_routing(T, K, E, R);
+    if (rc != EPX_OK)
+        return rc;
+    *bytes = epx::layout_workspace_bytes(T, E, R);
+    return EPX_OK;
+}
+
+size_t epx_ll_size_hint(int max_tokens_per_rank, int h, int R, int E, int fp8)
+{
+    if (max_tokens_per_rank < 1 || check_hidden(h, fp8) != EPX_OK || R < 1 || E < 1 ||
+        E % R != 0)
+        return 0;
+    // every array of the layout starts on a 128-byte boundary
+    const auto up = [](size_t n) { return (n + 127) / 128 * 128; };
+    const size_t rows = (size_t)E * R * max_tokens_per_rank;
+    size_t total = up(rows * (fp8 ? (size_t)h : (size_t)h * 2));
+    if (fp8)
+        total += up(rows * (size_t)(h / 128) * sizeof(float));
+    total += up(rows * sizeof(int32_t));                 // source index per row
+    total += up((size_t)E * R * sizeof(int32_t));        // count per region
+    return up(total);
+}
+
+int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int E, int R,
+                            int C, int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                            uint8_t *is_token_in_rank, int32_t *rank_off, int32_t *exp_off,
+                            int32_t *pos_in_rank, int32_t *slot_in_expert,
+                            int32_t *channel_prefix, int32_t *totals,
+                            int32_t *totals_host_mapped, void *ws, size_t ws_bytes,
+                            hipStream_t stream)
+{
+    int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if ((rc = check_routing(T, K, E, R)) != EPX_OK)
+        return rc;
+    if (channel_prefix && (C < 1 || C > (1 << 20)))
+        return EPX_EINVAL;
+    if (!num_tokens_per_expert || !num_tokens_per_rank || !rank_off || !exp_off || !totals)
+        return EPX_EINVAL;
+    if (T > 0 && (!topk_idx || !is_token_in_rank || !pos_in_rank || !slot_in_expert))
+        return EPX_EINVAL;
+    const size_t need = epx::layout_workspace_bytes(T, E, R);
+    if (ws_bytes < need)
+        return EPX_ECAPACITY;
+    if (need > 0 && !ws)
+        return EPX_EINVAL;
+    epx::LayoutArgs a{};
+    a.topk_idx = topk_idx;
+    a.T = T; a.K = K; a.E = E; a.R = R; a.L = E / R;
+    a.C = channel_prefix ? C : 0;
+    a.ntiles = (T + epx::kLayoutTile - 1) / epx::kLayoutTile;
+    a.tile_cnt = static_cast<int32_t *>(ws);
+    a.num_tokens_per_expert = num_tokens_per_expert;
+    a.num_tokens_per_rank = num_tokens_per_rank;
+    a.is_token_in_rank = is_token_in_rank;
+    a.rank_off = rank_off;
+    a.exp_off = exp_off;
+    a.pos_in_rank = pos_in_rank;
+    a.slot_in_expert = slot_in_expert;
+    a.channel_prefix = channel_prefix;
+    a.totals = totals;
+    a.totals_host_mapped = totals_host_mapped;
+    a.err = ctx->d_err;
+    return launched(epx::launch_layout(a, stream));
+}
+
+int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
+                 const float *topk_w, int T, int K, int E, int R, const int32_t *rank_off,
+                 const int32_t *exp_off, const int32_t *pos_in_rank,
+                 const int32_t *slot_in_expert, int fp8, void *send_x, float *send_scales,
+                 int32_t *send_src, int64_t *send_topk_idx, float *send_topk_w,
+                 int64_t send_cap_rows, void *recv_x, float *recv_scales, int32_t *recv_src,
+                 int64_t recv_cap_rows, int32_t *pos_exp, hipStream_t stream)
+{
+    int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if ((rc = check_routing(T, K, E, R)) != EPX_OK)
+        return rc;
+    if ((rc = check_hidden(h, fp8)) != EPX_OK)
+        return rc;
+    if (send_cap_rows < 0 || recv_cap_rows < 0)
+        return EPX_EINVAL;
+    if (T > 0) {
+        if (!x || !topk_idx || !topk_w || !rank_off || !exp_off || !pos_in_rank ||
+            !slot_in_expert || !pos_exp || !send_x || !send_src || !send_topk_idx ||
+            !send_topk_w || !recv_x || !recv_src)
+            return EPX_EINVAL;
+        if (fp8 && (!send_scales || !recv_scales))
+            return EPX_EINVAL;
+        if (!aligned16(x) || !aligned16(send_x) || !aligned16(recv_x))
+            return EPX_EINVAL;
+    }
+    epx::DispatchArgs a{};
+    a.x = x; a.topk_idx = topk_idx; a.topk_w = topk_w;
+    a.h = h; a.T = T; a.K = K; a.E = E; a.R = R; a.L = E / R;
+    a.rank_off = rank_off; a.exp_off = exp_off;
+    a.pos_in_rank = pos_in_rank; a.slot_in_expert = slot_in_expert;
+    a.send_x = send_x; a.send_scales = send_scales; a.send_src = send_src;
+    a.send_topk_idx = send_topk_idx; a.send_topk_w = send_topk_w; a.send_cap = send_cap_rows;
+    a.recv_x = recv_x; a.recv_scales = recv_scales; a.recv_src = recv_src;
+    a.recv_cap = recv_cap_rows; a.pos_exp = pos_exp;
+    a.err = ctx->d_err;
+    return launched(epx::launch_dispatch(a, fp8 != 0, stream));
+}
+
+int epx_combine(epx_ctx *ctx, const uint16_t *expert_out, int64_t n_rows, int h,
+                const float *topk_w, const int32_t *pos, int T, int K, uint16_t *out,
+                hipStream_t stream)
+{
+    int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if (T < 0 || K < 1 || K > EPX_MAX_TOPK || n_rows < 0 || (int64_t)T * K > INT32_MAX)
+        return EPX_EINVAL;
+    if ((rc = check_hidden(h, 0)) != EPX_OK)
+        return rc;
+    if (T > 0) {
+        if (!topk_w || !pos || !out || (n_rows > 0 && !expert_out))
+            return EPX_EINVAL;
+        if (!aligned16(out) || !aligned16(expert_out))
+            return EPX_EINVAL;
+    }
+    epx::CombineArgs a{};
+    a.y = expert_out; a.n_rows = n_rows; a.h = h; a.T = T; a.K = K;
+    a.topk_w = topk_w; a.pos = pos; a.out = out; a.err = ctx->d_err;
+    return launched(epx::launch_combine(a, stream));
+}
+
+int epx_ll_reset(epx_ctx *ctx, int32_t *ll_count, int64_t n, hipStream_t stream)
+{
+    const int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if (n < 0 || (n > 0 && !ll_count))
+        return EPX_EINVAL;
+    return launched(epx::launch_fill_i32(ll_count, n, -1, stream));
+}
+
+int epx_ll_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx, int T,
+                    int K, int E, int R, int src_rank, int cap, int R_buf, int fp8, void *ll_x,
+                    float *ll_scales, int32_t *ll_src, int32_t *ll_count, int32_t *pos_ll,
+                    hipStream_t stream)
+{
+    int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if ((rc = check_routing(T, K, E, R)) != EPX_OK)
+        return rc;
+    if ((rc = check_hidden(h, fp8)) != EPX_OK)
+        return rc;
+    if (cap < 1 || src_rank < 0 || src_rank >= R || (R_buf != R && R_buf != 1))
+        return EPX_EINVAL;
+    if ((int64_t)E * R_buf * cap > INT32_MAX)
+        return EPX_EINVAL;
+    if (T > cap)
+        return EPX_ECAPACITY;
+    if (!ll_count || (T > 0 && (!x || !topk_idx || !ll_x || !ll_src || !pos_ll)))
+        return EPX_EINVAL;
+    if (T > 0 && fp8 && !ll_scales)
+        return EPX_EINVAL;
+    if (T > 0 && (!aligned16(x) || !aligned16(ll_x)))
+        return EPX_EINVAL;
+    epx::LLArgs a{};
+    a.x = x; a.topk_idx = topk_idx; a.h = h; a.T = T; a.K = K; a.E = E; a.R = R;
+    a.src_rank = src_rank; a.cap = cap; a.R_buf = R_buf;
+    a.ll_x = ll_x; a.ll_scales = ll_scales; a.ll_src = ll_src; a.ll_count = ll_count;
+    a.pos_ll = pos_ll; a.err = ctx->d_err;
+    return launched(epx::launch_ll_dispatch(a, fp8 != 0, stream));
+}
+
+int epx_get_error(epx_ctx *ctx, int *device_flags, hipStream_t stream)
+{
+    const int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if (!device_flags)
+        return EPX_EINVAL;
+    int v = 0;
+    if (hipMemcpyAsync(&v, ctx->d_err, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return EPX_EHIP;
+    if (epx::launch_fill_i32(ctx->d_err, 1, 0, stream) != hipSuccess)
+        return EPX_EHIP;
+    if (hipStreamSynchronize(stream) != hipSuccess)
+        return EPX_EHIP;
+    *device_flags = v;
+    return v ? EPX_EDEVICE : EPX_OK;
+}
+
+}  // extern "C"

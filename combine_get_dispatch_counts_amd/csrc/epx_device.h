@@ -1,0 +1,108 @@
+// epx_device.h -- device-side helpers shared by the libepx kernels (gfx950).
+//
+// Number formats are written from their definitions:
+//   bf16: the top half of an fp32 pattern, rounded to nearest even;
+//   e4m3: OCP E4M3FN, 1/4/3 bits, bias 7, no infinities, max 448.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "epx.h"
+
+namespace epx {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, nearest even. Adding 0x7FFF plus the lowest kept bit
+// carries into the kept half exactly when the dropped half is above the
+// midpoint, or at it with an odd kept half. NaN -> canonical 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp32 -> OCP E4M3FN code, nearest even, saturating to 448.
+//  * |v| > 464 (the midpoint between 448 and the NaN pattern's 480): 0x7E|sign.
+//  * |v| >= 2^-6: a normal e4m3 keeps 3 of fp32's 23 mantissa bits, so round
+//    the magnitude pattern at bit 20 (add 0x7FFFF plus the lowest kept bit);
+//    a carry out of the mantissa bumps the exponent by itself. The fp32
+//    exponent (bias 127) becomes the e4m3 exponent (bias 7).
+//  * |v| < 2^-6: subnormal codes are multiples of 2^-9, code = rne(|v|*2^9);
+//    the product is exact and 8 lands on 0x08, the smallest normal.
+// NaN -> 0x7F; the sign is kept otherwise (negative underflow -> 0x80).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const uint32_t sign = (u >> 24) & 0x80u;
+    if (a > 0x7F800000u)
+        return 0x7Fu;
+    if (a > 0x43E80000u)                 // 464.0f
+        return sign | 0x7Eu;
+    if (a < 0x3C800000u) {               // 2^-6
+        const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
+        return sign | (uint32_t)q;
+    }
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    const uint32_t exp8 = (r >> 23) - 120u;   // (e - 127) + 7
+    return sign | (exp8 << 3) | ((r >> 20) & 7u);
+}
+
+__device__ __forceinline__ void flag_error(int *err, int bits)
+{
+    atomicOr(err, bits);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t lanes_below(int lane)
+{
+    return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+}
+
+__device__ __forceinline__ u32x4 load16(const void *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ u32x4 load16_stream(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ void store16_stream(void *p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
+// Inclusive sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int o = __shfl_up(v, d, kWave);
+        if (lane >= d)
+            v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_or(uint64_t v)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1)
+        v |= __shfl_xor(v, d, kWave);
+    return v;
+}
+
+}  // namespace epx

@@ -1,0 +1,82 @@
+// epx_internal.h -- launcher interface between the C ABI (epx_api.hip) and
+// the kernel translation units. Argument checking happens in epx_api.hip;
+// launchers assume valid shapes and return the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct epx_ctx {
+    int device;
+    int *d_err;  // device error word (EPX_DEV_* bits)
+};
+
+namespace epx {
+
+// Tokens per layout tile: 4 waves of 64 tokens, one token per thread.
+constexpr int kLayoutWaves = 4;
+constexpr int kLayoutTile = 64 * kLayoutWaves;
+
+struct LayoutArgs {
+    const int64_t *topk_idx;
+    int T, K, E, R, L, C;
+    int ntiles;
+    int32_t *tile_cnt;  // workspace [ntiles, E + R]
+    int32_t *num_tokens_per_expert, *num_tokens_per_rank;
+    uint8_t *is_token_in_rank;
+    int32_t *rank_off, *exp_off, *pos_in_rank, *slot_in_expert, *channel_prefix;
+    int32_t *totals, *totals_host_mapped;
+    int *err;
+};
+
+size_t layout_workspace_bytes(int T, int E, int R);
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
+
+struct DispatchArgs {
+    const uint16_t *x;
+    const int64_t *topk_idx;
+    const float *topk_w;
+    int h, T, K, E, R, L;
+    const int32_t *rank_off, *exp_off, *pos_in_rank, *slot_in_expert;
+    void *send_x;
+    float *send_scales;
+    int32_t *send_src;
+    int64_t *send_topk_idx;
+    float *send_topk_w;
+    int64_t send_cap;
+    void *recv_x;
+    float *recv_scales;
+    int32_t *recv_src;
+    int64_t recv_cap;
+    int32_t *pos_exp;
+    int *err;
+};
+
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, hipStream_t stream);
+
+struct LLArgs {
+    const uint16_t *x;
+    const int64_t *topk_idx;
+    int h, T, K, E, R, src_rank, cap, R_buf;
+    void *ll_x;
+    float *ll_scales;
+    int32_t *ll_src, *ll_count, *pos_ll;
+    int *err;
+};
+
+hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream);
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
+
+struct CombineArgs {
+    const uint16_t *y;
+    int64_t n_rows;
+    int h, T, K;
+    const float *topk_w;
+    const int32_t *pos;
+    uint16_t *out;
+    int *err;
+};
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+
+}  // namespace epx

@@ -1,0 +1,209 @@
+/*
+ * epx.h -- C ABI of libepx: the single-GPU hot path of DeepEP-style MoE
+ * expert-parallel dispatch / combine, written for AMD MI355X (gfx950).
+ *
+ * Sources (the three web pages the method is taken from):
+ *   [P1] "事件驱动 EP 内核的调度策略与零拷贝通信：从 DeepEP 看高性能并发架构设计"
+ *        (event-driven EP kernel scheduling and zero-copy communication)
+ *   [P2] "DeepEP 学习笔记：MoE 场景下的专家并行通信" (DeepEP study notes)
+ *   [P3] "DeepSeek DeepEP探索：低延迟分发（low latency dispatch）的架构设计与实现"
+ *        (DeepEP low-latency dispatch)
+ *
+ * One GPU owns T tokens. Destination "ranks" are logical partitions of the
+ * expert set: rank r holds experts [r*L, (r+1)*L) with L = E / R. Nothing
+ * here talks to another GPU.
+ *
+ * Conventions shared by every call
+ *   - Pointers are device memory unless a comment says "host". Every array is
+ *     dense row-major. The caller allocates and owns every buffer; no call
+ *     allocates device memory (epx_create allocates one 4-byte error word).
+ *   - bf16 data is passed as uint16 bit patterns; FP8 data as uint8 codes in
+ *     OCP E4M3FN (max 448, no infinities).
+ *   - Hidden-state buffers (x, send_x, recv_x, ll_x, expert_out, out) must be
+ *     16-byte aligned; h must be a multiple of 8 (of 128 with FP8).
+ *   - Every call only enqueues work on `stream` and returns; none waits for
+ *     the GPU, except epx_get_error. Work is ordered by the stream alone.
+ *   - Host-detectable errors are returned at once and nothing is launched.
+ *     Errors only the kernels can see (a top-k entry outside [-1, E), a row
+ *     beyond the caller's capacity, a handle row outside the expert-output
+ *     buffer) set bits in the context's device error word; read and clear
+ *     them with epx_get_error. After such an error the outputs of that call
+ *     are unspecified, but no write lands outside a buffer's stated size.
+ *   - Results are deterministic: no atomics decide an order, so two runs on
+ *     the same inputs give identical bytes.
+ */
+#ifndef EPX_H
+#define EPX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes */
+#define EPX_OK 0
+#define EPX_EINVAL (-1)       /* bad shape, parameter, null or misaligned pointer */
+#define EPX_ECAPACITY (-2)    /* T > cap (low-latency), or workspace too small */
+#define EPX_EUNSUPPORTED (-3) /* FP8 requested with h % 128 != 0 */
+#define EPX_EHIP (-4)         /* a HIP runtime call or kernel launch failed */
+#define EPX_EDEVICE (-5)      /* epx_get_error: the device error word was set */
+
+/* Bits of the device error word */
+#define EPX_DEV_BAD_ROUTE 1   /* a top-k entry outside [-1, E) */
+#define EPX_DEV_OVERFLOW 2    /* a row index reached the caller's capacity */
+#define EPX_DEV_BAD_HANDLE 4  /* a combine handle row >= n_rows */
+
+/* Limits of this implementation */
+#define EPX_MAX_TOPK 32
+#define EPX_MAX_EXPERTS 512
+#define EPX_MAX_RANKS 64
+
+typedef struct epx_ctx epx_ctx;
+
+/* Context: binds a device and owns its device error word. [P2] "Buffer 与内存
+ * 视角" / "内存生命周期": a Buffer is built once, used by every call and
+ * destroyed at the end; here it holds no communication state (there is no
+ * peer). `device` is a HIP device ordinal; the calls below must be issued
+ * with that device current. Returns EPX_EINVAL for a bad ordinal, EPX_EHIP if
+ * the error word cannot be allocated. */
+int epx_create(epx_ctx **out, int device);
+int epx_destroy(epx_ctx *ctx);
+const char *epx_strerror(int code);
+
+/* Workspace bytes epx_get_dispatch_layout needs for (T, K, E, R) (host out).
+ * [P2] "Buffer 与内存视角": the workspace is allocated up front, once. */
+int epx_workspace_size(int T, int K, int E, int R, size_t *bytes);
+
+/* Bytes of a low-latency receive buffer for max_tokens_per_rank tokens per
+ * source: E*R regions of max_tokens_per_rank rows (bf16: 2h bytes; fp8: h
+ * bytes + h/128 fp32 scales) plus one int32 source index per row and one
+ * int32 count per region, each array rounded up to 128 bytes, the total
+ * rounded up to a multiple of 128. [P3] 2.2: the size hint of the worst-case
+ * layout, rounded to the buffer alignment. Returns 0 for bad arguments. */
+size_t epx_ll_size_hint(int max_tokens_per_rank, int h, int R, int E, int fp8);
+
+/* get_dispatch_layout + receive offsets. [P2] "dispatch 前：全局布局与通知"
+ * (per-expert and per-rank token counts, is_token_in_rank, then prefix sums
+ * into channel_prefix_matrix); [P1] "事件驱动调度的本质" (count locally,
+ * prefix-sum the offsets); [P2] "DeepEP v2" (one copy per destination rank).
+ *
+ * In:  topk_idx [T,K] int64, each entry in [-1, E) (-1 = no route).
+ *      1 <= K <= 32, 1 <= E <= 512, 1 <= R <= 64, E % R == 0, T >= 0.
+ *      C >= 1 channels when channel_prefix != NULL (ignored otherwise).
+ * Out: num_tokens_per_expert [E]   entries routed to each expert
+ *      num_tokens_per_rank [R]     distinct tokens routed to each rank
+ *      is_token_in_rank [T,R]      1 if token t goes to rank r, else 0
+ *      rank_off [R+1], exp_off [E+1]   exclusive prefix sums of the counts
+ *      pos_in_rank [T,R]           tokens before t in rank r, or -1
+ *      slot_in_expert [T,K]        entries before (t,k) routed to the same
+ *                                  expert in row-major (t,k) order, or -1
+ *      channel_prefix [R,C]        optional: channel c owns tokens
+ *                                  [c*ceil(T/C), min((c+1)*ceil(T/C), T));
+ *                                  entry = tokens of rank r before its end
+ *      totals [2]                  (rows of the rank-major send buffer,
+ *                                   rows of the expert-major receive buffer)
+ *      totals_host_mapped          optional host-pinned int32[2]
+ *                                  (hipHostMalloc) that also receives totals;
+ *                                  valid once the stream has been synchronised
+ * ws:  device workspace of epx_workspace_size bytes (contents scratch). */
+int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int E,
+                            int R, int C, int32_t *num_tokens_per_expert,
+                            int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank,
+                            int32_t *rank_off, int32_t *exp_off, int32_t *pos_in_rank,
+                            int32_t *slot_in_expert, int32_t *channel_prefix,
+                            int32_t *totals, int32_t *totals_host_mapped, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* High-throughput dispatch: the rank-deduplicated pack and the local permute
+ * into expert-contiguous blocks, reading x once. [P2] "dispatch 过程" (each
+ * token is sent, in token order, to every rank is_token_in_rank marks, with
+ * its source index, top-k indices and weights; the receiver writes at the
+ * prefix offset); [P2] "DeepEP v2" (one full activation per destination
+ * rank); [P1] "高吞吐量模式：协调阶段与紧凑缓冲区" (exact-size ragged
+ * receive buffer, then a local permute into the per-expert blocks a grouped
+ * GEMM reads); [P1] "低延迟模式" and [P2] "内存布局" (optional FP8 payload
+ * with its scales).
+ *
+ * In:  x [T,h] bf16; topk_idx [T,K]; topk_w [T,K] fp32; the layout outputs
+ *      rank_off, exp_off, pos_in_rank, slot_in_expert of the same topk_idx.
+ *      fp8 = 0: rows are bf16 (2h bytes). fp8 = 1: rows are e4m3 codes
+ *      (h bytes) plus fp32 scales [rows, h/128]: per token and per 128
+ *      channels, s = max(amax, 1e-4) / 448 and q = e4m3(x / s), both IEEE
+ *      fp32 divisions, rounded to nearest even.
+ * Out: send_x [send_cap_rows, h(*2)] rank-major: row rank_off[r] +
+ *        pos_in_rank[t,r] holds token t for each rank r it goes to;
+ *      send_scales [send_cap_rows, h/128] (fp8 only, else may be NULL);
+ *      send_src [rows] source token; send_topk_idx [rows,K] int64 local
+ *        expert index (e - r*L) where expert e is on the row's rank, else -1;
+ *      send_topk_w [rows,K] the weight there, else 0;
+ *      recv_x [recv_cap_rows, ...] expert-major: row exp_off[e] +
+ *        slot_in_expert[t,k] holds token t for each entry (t,k) with expert e;
+ *      recv_scales (fp8), recv_src [rows] source token;
+ *      pos_exp [T,K] the recv row of (t,k), or -1: the handle for combine.
+ *      A row index >= its capacity is not written and sets
+ *      EPX_DEV_OVERFLOW; totals from the layout call say what is needed. */
+int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
+                 const float *topk_w, int T, int K, int E, int R, const int32_t *rank_off,
+                 const int32_t *exp_off, const int32_t *pos_in_rank,
+                 const int32_t *slot_in_expert, int fp8, void *send_x, float *send_scales,
+                 int32_t *send_src, int64_t *send_topk_idx, float *send_topk_w,
+                 int64_t send_cap_rows, void *recv_x, float *recv_scales,
+                 int32_t *recv_src, int64_t recv_cap_rows, int32_t *pos_exp,
+                 hipStream_t stream);
+
+/* Combine: reduce expert outputs back to source-token order. [P2] "combine
+ * 过程" (route back through the handle, reduce per source token); [P1]
+ * "低延迟模式" (combine stays BF16).
+ * In:  expert_out [n_rows, h] bf16 (expert-major, or the low-latency layout);
+ *      topk_w [T,K] fp32; pos [T,K] handle rows (pos_exp or pos_ll; < 0 =
+ *      skip; >= n_rows sets EPX_DEV_BAD_HANDLE and is skipped).
+ * Out: out [T,h] bf16: per column, acc = +0.0f, then for k = 0..K-1 over
+ *      valid entries acc = fmaf(topk_w[t,k], expert_out[pos[t,k]], acc);
+ *      the result is rounded to bf16, nearest even (NaN -> 0x7FC0). */
+int epx_combine(epx_ctx *ctx, const uint16_t *expert_out, int64_t n_rows, int h,
+                const float *topk_w, const int32_t *pos, int T, int K, uint16_t *out,
+                hipStream_t stream);
+
+/* Set n int32 counts to -1, the "nothing arrived" value. [P2] "Buffer 与内存
+ * 视角" (counters start at -1); [P1] "低延迟模式" (the count slot starts
+ * empty). A fill kernel, so it is safe inside a captured graph. */
+int epx_ll_reset(epx_ctx *ctx, int32_t *ll_count, int64_t n, hipStream_t stream);
+
+/* Low-latency fixed-slot dispatch in one launch, with no layout call and no
+ * host round trip. [P1] "低延迟模式：固定缓冲区与信号槽机制" (each (source
+ * rank, expert) pair owns a private region of `cap` rows at region index
+ * expert * num_ranks + src_rank; the count slot is written after the data);
+ * [P3] 4.2 (count index local_expert * num_ranks + src_rank); [P3] 2.2
+ * (receive regions sized for the worst case, every token to one expert).
+ *
+ * In:  x [T,h] bf16; topk_idx [T,K]; this GPU's source rank src_rank in
+ *      [0, R); cap >= T rows per region (else EPX_ECAPACITY, nothing
+ *      launched); R_buf = R (all destinations' buffers side by side: region
+ *      e*R + src_rank) or 1 (this source's slice only: region e);
+ *      E * R_buf * cap must fit in int32. fp8 as in epx_dispatch.
+ * Out: ll_x [E*R_buf*cap, h(*2)], ll_scales (fp8), ll_src [E*R_buf*cap]:
+ *      entry (t,k) with expert e fills row region(e)*cap + slot, where slot
+ *      counts entries before (t,k) routed to e (row-major order); other
+ *      rows are not touched.
+ *      ll_count [E*R_buf]: count[region(e)] = entries routed to e, for every
+ *      e (0 included); counts of other sources' regions are not touched, so
+ *      they keep what epx_ll_reset put there.
+ *      pos_ll [T,K]: the row of (t,k), or -1: the handle for combine. */
+int epx_ll_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
+                    int T, int K, int E, int R, int src_rank, int cap, int R_buf, int fp8,
+                    void *ll_x, float *ll_scales, int32_t *ll_src, int32_t *ll_count,
+                    int32_t *pos_ll, hipStream_t stream);
+
+/* Synchronise `stream`, return the device error word in *device_flags (host)
+ * and clear it. Returns EPX_EDEVICE if any bit was set, EPX_OK otherwise. */
+int epx_get_error(epx_ctx *ctx, int *device_flags, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPX_H */

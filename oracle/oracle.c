@@ -268,16 +268,20 @@ int orc_layout(const int64_t *topk_idx, int T, int K, int E, int R, int C,
 /* Bytes of one row's data part: bf16 = 2h, fp8 = h (scales kept apart). */
 static size_t row_bytes(int h, int fp8) { return fp8 ? (size_t)h : (size_t)h * 2; }
 
-/* Write token t's payload into row `row` of (dst, dst_scales). */
-static void put_token_row(const uint16_t *x, int h, int fp8, int t, void *dst,
-                          float *dst_scales, int64_t row)
+/* Token t's payload: its bf16 row, or (fp8) its row quantised once into the
+ * caller's scratch (q_tmp [h], s_tmp [h/128]); every destination gets a copy. */
+static void token_payload(const uint16_t *x, int h, int fp8, int t, uint8_t *q_tmp,
+                          float *s_tmp, const void **row, const float **scales)
 {
     const uint16_t *xr = x + (size_t)t * h;
-    if (fp8)
-        orc_quantize_row(xr, h, (uint8_t *)dst + (size_t)row * h,
-                         dst_scales + (size_t)row * (h / 128));
-    else
-        memcpy((uint16_t *)dst + (size_t)row * h, xr, (size_t)h * 2);
+    if (fp8) {
+        orc_quantize_row(xr, h, q_tmp, s_tmp);
+        *row = q_tmp;
+        *scales = s_tmp;
+    } else {
+        *row = xr;
+        *scales = NULL;
+    }
 }
 
 /* Copy row `src_row` of (src, src_scales) to row `dst_row` of (dst, dst_scales). */
@@ -334,13 +338,24 @@ int orc_dispatch(const uint16_t *x, int h, const int64_t *topk_idx, const float 
         return ORC_ECAPACITY;
     const int L = E / R;
 
-    /* pack: t ascending, then r ascending */
+    uint8_t *q_tmp = fp8 ? malloc((size_t)h) : NULL;
+    float *s_tmp = fp8 ? malloc(sizeof(float) * (size_t)(h / 128)) : NULL;
+    if (fp8 && (!q_tmp || !s_tmp)) {
+        free(q_tmp);
+        free(s_tmp);
+        return ORC_EINVAL;
+    }
+
+    /* pack: t ascending, then r ascending; an FP8 row is quantised once per token */
     for (int t = 0; t < T; ++t) {
+        const void *payload;
+        const float *pscales;
+        token_payload(x, h, fp8, t, q_tmp, s_tmp, &payload, &pscales);
         for (int r = 0; r < R; ++r) {
             if (!is_token_in_rank[(size_t)t * R + r])
                 continue;
             int64_t row = (int64_t)rank_off[r] + pos_in_rank[(size_t)t * R + r];
-            put_token_row(x, h, fp8, t, send_x, send_scales, row);
+            copy_row(payload, pscales, 0, send_x, send_scales, row, h, fp8);
             send_src[row] = t;
             for (int k = 0; k < K; ++k) {
                 int64_t e = topk_idx[(size_t)t * K + k];
@@ -367,6 +382,8 @@ int orc_dispatch(const uint16_t *x, int h, const int64_t *topk_idx, const float 
             pos_exp[(size_t)t * K + k] = (int32_t)row;
         }
     }
+    free(q_tmp);
+    free(s_tmp);
     return ORC_OK;
 }
 
@@ -409,10 +426,29 @@ int orc_ll_dispatch(const uint16_t *x, int h, const int64_t *topk_idx,
         if (topk_idx[i] < -1 || topk_idx[i] >= E)
             return ORC_EROUTE;
 
+    /* with distinct experts per row a region gets at most T <= cap rows; a row
+     * that repeats an expert could exceed that, which is a capacity error */
     int32_t *count = calloc((size_t)E, sizeof *count);
     if (!count)
         return ORC_EINVAL;
+    for (size_t i = 0; i < (size_t)T * K; ++i)
+        if (topk_idx[i] >= 0 && ++count[topk_idx[i]] > cap) {
+            free(count);
+            return ORC_ECAPACITY;
+        }
+    memset(count, 0, sizeof *count * (size_t)E);
+    uint8_t *q_tmp = fp8 ? malloc((size_t)h) : NULL;
+    float *s_tmp = fp8 ? malloc(sizeof(float) * (size_t)(h / 128)) : NULL;
+    if (fp8 && (!q_tmp || !s_tmp)) {
+        free(count);
+        free(q_tmp);
+        free(s_tmp);
+        return ORC_EINVAL;
+    }
     for (int t = 0; t < T; ++t) {
+        const void *payload;
+        const float *pscales;
+        token_payload(x, h, fp8, t, q_tmp, s_tmp, &payload, &pscales);
         for (int k = 0; k < K; ++k) {
             int64_t e = topk_idx[(size_t)t * K + k];
             if (e == -1) {
@@ -422,11 +458,13 @@ int orc_ll_dispatch(const uint16_t *x, int h, const int64_t *topk_idx,
             int64_t region = (R_buf == 1) ? e : e * R + src_rank;
             int64_t slot = count[e]++;
             int64_t row = region * cap + slot;
-            put_token_row(x, h, fp8, t, ll_x, ll_scales, row);
+            copy_row(payload, pscales, 0, ll_x, ll_scales, row, h, fp8);
             ll_src[row] = t;
             pos_ll[(size_t)t * K + k] = (int32_t)row;
         }
     }
+    free(q_tmp);
+    free(s_tmp);
     for (int e = 0; e < E; ++e) {
         int64_t region = (R_buf == 1) ? e : (int64_t)e * R + src_rank;
         ll_count[region] = count[e];

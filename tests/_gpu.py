@@ -1,0 +1,84 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI (via
+the torch binding) and bring results back as numpy arrays shaped like the
+oracle's."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import combine_get_dispatch_counts_amd as epx
+
+CANARY = 0xA5
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(x_u16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x_u16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 / uint8 / int / float tensor -> numpy with the same bytes."""
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def layout(topk: np.ndarray, E: int, R: int, C: int | None = None) -> dict:
+    lay = epx.get_dispatch_layout(torch.from_numpy(topk).cuda(), E, R, C)
+    out = {k: host_bits(getattr(lay, k)) for k in
+           ["num_tokens_per_expert", "num_tokens_per_rank", "is_token_in_rank", "rank_off",
+            "exp_off", "pos_in_rank", "slot_in_expert", "totals"]}
+    if C:
+        out["channel_prefix"] = host_bits(lay.channel_prefix)
+    out["_layout"] = lay
+    return out
+
+
+def dispatch(x: np.ndarray, topk: np.ndarray, w: np.ndarray, E: int, R: int, fp8: bool,
+             worst_case: bool = False, guard: int = 0) -> dict:
+    """Layout + dispatch on the GPU. worst_case: capacities T*min(K,R) and T*K
+    (the benchmark's launch configuration); guard: extra rows past the
+    capacity pre-filled with canary bytes, returned under 'guard_*'."""
+    T, h = x.shape
+    K = topk.shape[1]
+    xt, tk, wt = dev_bf16(x), torch.from_numpy(topk).cuda(), torch.from_numpy(w).cuda()
+    lay = epx.get_dispatch_layout(tk, E, R)
+    n_send, n_recv = (int(v) for v in lay.totals.cpu())
+    cap_s, cap_r = (T * min(K, R), T * K) if worst_case else (n_send, n_recv)
+    buf = epx.alloc_dispatch(T, h, K, cap_s + guard, cap_r + guard, fp8, xt.device)
+    for v in buf.values():
+        if v is not None:
+            v.view(torch.uint8).fill_(CANARY)
+    view = {k: (v[:cap_s] if k.startswith("send") else v[:cap_r] if k.startswith("recv") else v)
+            if v is not None else None for k, v in buf.items()}
+    d = epx.dispatch(xt, tk, wt, E, R, fp8=fp8, layout=lay, out=view)
+    flags = epx.get_error()
+    res = {k: host_bits(getattr(d, k)) for k in
+           ["send_src", "send_topk_idx", "send_topk_w", "recv_src", "pos_exp"]}
+    res["send_x"] = host_bits(d.send_x)
+    res["recv_x"] = host_bits(d.recv_x)
+    if fp8:
+        res["send_scales"] = host_bits(d.send_scales)
+        res["recv_scales"] = host_bits(d.recv_scales)
+    for k in list(res):
+        if k.startswith("send"):
+            res[k] = res[k][:n_send]
+        elif k.startswith("recv"):
+            res[k] = res[k][:n_recv]
+    if guard or worst_case:
+        res["guard"] = {k: host_bits(v[cap_s if k.startswith("send") else cap_r:])
+                        for k, v in buf.items() if v is not None and k != "pos_exp"}
+        res["unused"] = {k: host_bits(v[(n_send if k.startswith("send") else n_recv):
+                                          (cap_s if k.startswith("send") else cap_r)])
+                         for k, v in buf.items() if v is not None and k != "pos_exp"}
+    res["flags"] = flags
+    res["totals"] = (n_send, n_recv)
+    res["_dispatched"] = d
+    res["_w"] = wt
+    return res

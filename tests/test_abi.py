@@ -1,0 +1,80 @@
+"""The C-ABI library loads and exports every function include/epx.h declares;
+host-only helpers behave as documented. No GPU work is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "epx.h")
+
+
+def _declared() -> list[str]:
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(epx_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from combine_get_dispatch_counts_amd import _lib
+
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from combine_get_dispatch_counts_amd import _lib
+
+    names = _declared()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in epx.h but not exported"
+    assert sorted(_lib.SIGNATURES) == names, "ctypes table and header disagree"
+
+
+def test_library_is_gfx950_hip():
+    from combine_get_dispatch_counts_amd import _lib
+
+    with open(_lib.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"gfx950" in blob
+    assert b"gfx942" not in blob  # built for gfx950 only
+
+
+def test_workspace_size(lib):
+    n = ctypes.c_size_t()
+    assert lib.epx_workspace_size(4096, 8, 256, 32, ctypes.byref(n)) == 0
+    assert n.value == 16 * (256 + 32) * 4           # 16 tiles of 256 tokens
+    assert lib.epx_workspace_size(0, 8, 256, 32, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.epx_workspace_size(10, 8, 256, 30, ctypes.byref(n)) == -1   # E % R
+    assert lib.epx_workspace_size(10, 33, 256, 32, ctypes.byref(n)) == -1  # K > 32
+    assert lib.epx_workspace_size(10, 8, 1024, 32, ctypes.byref(n)) == -1  # E > 512
+    assert lib.epx_workspace_size(10, 8, 256, 128, ctypes.byref(n)) == -1  # R > 64
+
+
+def _up(n):
+    return (n + 127) // 128 * 128
+
+
+@pytest.mark.parametrize("cap,h,R,E,fp8", [(128, 7168, 32, 256, 1), (128, 7168, 32, 256, 0),
+                                          (6, 128, 4, 8, 1), (1, 8, 1, 1, 0)])
+def test_ll_size_hint(lib, cap, h, R, E, fp8):
+    rows = E * R * cap
+    data = rows * (h if fp8 else 2 * h)
+    want = _up(data) + (_up(rows * (h // 128) * 4) if fp8 else 0) + _up(rows * 4) + _up(E * R * 4)
+    assert lib.epx_ll_size_hint(cap, h, R, E, fp8) == want
+
+
+def test_ll_size_hint_rejects(lib):
+    assert lib.epx_ll_size_hint(0, 7168, 32, 256, 1) == 0
+    assert lib.epx_ll_size_hint(128, 7000, 32, 256, 1) == 0   # fp8 needs h % 128
+    assert lib.epx_ll_size_hint(128, 7168, 30, 256, 1) == 0
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.epx_strerror(code)
+    assert b"unknown" in lib.epx_strerror(7)

@@ -1,0 +1,380 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+element by element, on the same seeded inputs.
+
+Bar: layout, offsets, permutations, metadata, FP8 codes and scales
+bit-exact; combine bit-exact against the oracle's fp32 fma chain (which is
+itself within one bf16 ulp of the exact sum away from cancellation, see
+test_oracle_combine). Full-size workload cases use the benchmark's launch
+configuration (worst-case preallocated capacities, no host wait).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+from _gpu import CANARY, dev_bf16, dispatch, host_bits, layout, say
+
+pytestmark = pytest.mark.gpu
+
+LAYOUT_KEYS = ["num_tokens_per_expert", "num_tokens_per_rank", "is_token_in_rank", "rank_off",
+               "exp_off", "pos_in_rank", "slot_in_expert", "totals"]
+
+
+def _eq(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    if a.dtype.kind == "f":
+        a, b = a.view(np.uint32 if a.itemsize == 4 else np.uint64), b.view(
+            np.uint32 if b.itemsize == 4 else np.uint64)
+    bad = np.flatnonzero((a != b).ravel())
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at flat {bad[:5]}: " \
+                          f"{a.ravel()[bad[:5]]} vs {b.ravel()[bad[:5]]}"
+
+
+def _check_layout(topk, E, R, C):
+    g = layout(topk, E, R, C)
+    o = oracle.layout(topk, E, R, C)
+    for k in LAYOUT_KEYS + (["channel_prefix"] if C else []):
+        _eq(g[k], o[k], k)
+    return o
+
+
+def _edge_cases():
+    cases = []
+    for T in (0, 1, 63, 64, 65, 257):
+        cases.append(("uniform", T, 8, 256, 32, 16, 0.0))
+    for K in (1, 2, 6, 8, 32):
+        cases.append(("uniform", 300, K, 64, 8, 7, 0.0))
+    for R in (1, 4, 8, 32, 64):
+        cases.append(("uniform", 513, 4, 128, R, 33, 0.0))
+    cases.append(("dropped", 700, 8, 256, 32, 5, 0.3))
+    cases.append(("one_expert", 1000, 1, 64, 8, 10, 0.0))
+    cases.append(("max_experts", 600, 8, 512, 64, 3, 0.0))
+    cases.append(("repeats", 300, 4, 16, 4, 4, 0.0))
+    cases.append(("many_channels", 100, 2, 8, 4, 1000, 0.0))
+    return cases
+
+
+@pytest.mark.parametrize("kind,T,K,E,R,C,p_drop", _edge_cases())
+def test_layout_edge_cases(kind, T, K, E, R, C, p_drop):
+    say(f"layout {kind} T={T} K={K} E={E} R={R} C={C}")
+    if kind == "one_expert":
+        topk = np.full((T, K), 5, np.int64)
+    elif kind == "repeats":
+        topk = np.random.default_rng(T).integers(-1, E, (T, K)).astype(np.int64)
+    else:
+        topk = synth.random_routing(T, K, E, seed=T * 31 + K, p_drop=p_drop)
+    _check_layout(topk, E, R, C)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_layout_workloads(cfg):
+    inp = synth.make_inputs(cfg)
+    wl = inp["workload"]
+    say(f"layout {wl.describe()}")
+    _check_layout(inp["topk_idx"], wl.E, wl.R, 24)
+
+
+def _check_dispatch(x, topk, w, E, R, fp8, worst_case=False, guard=0):
+    g = dispatch(x, topk, w, E, R, fp8, worst_case=worst_case, guard=guard)
+    assert g["flags"] == 0, f"device flags {g['flags']:#x}"
+    o = oracle.dispatch(x, topk, w, E, R, fp8=fp8)
+    keys = ["send_x", "send_src", "send_topk_idx", "send_topk_w", "recv_x", "recv_src", "pos_exp"]
+    if fp8:
+        keys += ["send_scales", "recv_scales"]
+    for k in keys:
+        _eq(g[k], o[k], k)
+    for region in ("guard", "unused"):
+        for k, v in g.get(region, {}).items():
+            assert (v.view(np.uint8) == CANARY).all(), f"{region} rows of {k} were written"
+    return g, o
+
+
+@pytest.mark.parametrize("T,K,E,R,h,fp8,p_drop", [
+    (1, 8, 256, 32, 7168, False, 0.0), (63, 2, 8, 4, 128, False, 0.0),
+    (65, 6, 64, 8, 4096, True, 0.0), (257, 8, 256, 64, 256, True, 0.2),
+    (200, 4, 16, 1, 1024, False, 0.1), (130, 8, 128, 32, 7168, True, 0.0),
+    (96, 3, 24, 4, 136, False, 0.0), (0, 4, 16, 4, 128, True, 0.0),
+])
+def test_dispatch_edge_cases(T, K, E, R, h, fp8, p_drop):
+    say(f"dispatch T={T} K={K} E={E} R={R} h={h} fp8={fp8} drop={p_drop}")
+    rng = np.random.default_rng(T + h)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32) * 3)
+    topk = synth.random_routing(T, K, E, seed=T + 7, p_drop=p_drop)
+    w = rng.random((T, K)).astype(np.float32)
+    _check_dispatch(x, topk, w, E, R, fp8, guard=3)
+
+
+def test_dispatch_special_values():
+    """Zeros, signed zeros, tiny and huge bf16 values, an all-zero FP8 group,
+    subnormal e4m3 results and values at rounding ties."""
+    say("dispatch special values")
+    T, h = 16, 512
+    rng = np.random.default_rng(4)
+    xf = rng.standard_normal((T, h)).astype(np.float32)
+    xf[0] = 0.0
+    xf[1] = -0.0
+    xf[2, :128] = 0.0
+    xf[3, :128] = np.float32(2.0) ** rng.integers(-40, -20, 128).astype(np.float32)
+    xf[4] *= np.float32(1e30)
+    xf[5, :128] = np.linspace(-448, 448, 128, dtype=np.float32)
+    xf[6, :128] = np.float32(448.0) * np.float32(2.0) ** -np.arange(128, dtype=np.float32) / 4
+    x = synth.to_bf16_bits(xf)
+    topk = synth.random_routing(T, 4, 16, seed=5)
+    w = rng.random((T, 4)).astype(np.float32)
+    for fp8 in (False, True):
+        _check_dispatch(x, topk, w, 16, 4, fp8)
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4, 5])
+def test_dispatch_workloads_full_size(cfg):
+    inp = synth.make_inputs(cfg)
+    wl = inp["workload"]
+    say(f"dispatch {wl.describe()} (worst-case capacities, as benchmarked)")
+    _check_dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, wl.fp8 or cfg == 1,
+                    worst_case=True)
+
+
+def test_dispatch_config1_bf16_and_fp8():
+    inp = synth.make_inputs(1)
+    wl = inp["workload"]
+    for fp8 in (False, True):
+        say(f"dispatch {wl.describe()} fp8={fp8}")
+        _check_dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, fp8, guard=2)
+
+
+def test_dispatch_deterministic():
+    inp = synth.make_inputs(4, T=2048)
+    wl = inp["workload"]
+    say("dispatch twice, bitwise")
+    a = dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, False)
+    b = dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, False)
+    for k in ["send_x", "recv_x", "send_src", "recv_src", "pos_exp", "send_topk_idx"]:
+        _eq(a[k], b[k], k)
+
+
+# ------------------------------------------------------------------ combine
+
+def _gpu_combine(y: torch.Tensor, pos: np.ndarray, w: np.ndarray) -> np.ndarray:
+    import combine_get_dispatch_counts_amd as epx
+
+    out = epx.combine(y, torch.from_numpy(pos).cuda(), torch.from_numpy(w).cuda())
+    assert epx.get_error() == 0
+    return host_bits(out)
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4, 5])
+def test_combine_workloads(cfg):
+    inp = synth.make_inputs(cfg)
+    wl = inp["workload"]
+    say(f"combine {wl.describe()}")
+    o = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R)
+    n_exp = int(o["layout"]["totals"][1])
+    y = synth.expert_outputs(n_exp, wl.h, seed=77 + cfg, device="cuda")
+    g = dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, False)
+    _eq(g["pos_exp"], o["pos_exp"], "pos_exp")
+    out = _gpu_combine(y, g["pos_exp"], inp["topk_w"])          # GPU handle
+    ref = oracle.combine(host_bits(y), inp["topk_w"], o["pos_exp"])  # oracle handle
+    _eq(out, ref, "combined_x")
+
+
+def test_combine_edge_cases():
+    rng = np.random.default_rng(12)
+    for T, K, h, n in [(1, 1, 8, 1), (37, 8, 7168, 300), (64, 32, 256, 2000), (5, 3, 64, 0)]:
+        say(f"combine T={T} K={K} h={h} rows={n}")
+        y = synth.expert_outputs(max(n, 1), h, seed=T, device="cuda")[:n]
+        pos = rng.integers(-1, max(n, 1), (T, K)).astype(np.int32) if n else np.full((T, K), -1, np.int32)
+        w = rng.standard_normal((T, K)).astype(np.float32)
+        out = _gpu_combine(y.contiguous() if n else torch.empty((0, h), dtype=torch.bfloat16,
+                                                                   device="cuda"), pos, w)
+        ref = oracle.combine(host_bits(y) if n else np.zeros((0, h), np.uint16), w, pos)
+        _eq(out, ref, "combined_x")
+
+
+@pytest.mark.parametrize("cfg,fp8", [(1, False), (3, False), (5, True)])
+def test_identity_experts_closed_form(cfg, fp8):
+    """combine(dispatch(x)) with unit weights and identity experts equals
+    bf16(K_valid * x) exactly (with FP8: x replaced by bf16(dequant(q)))."""
+    inp = synth.make_inputs(cfg, T=512 if cfg != 1 else None)
+    wl = inp["workload"]
+    say(f"identity-expert closed form {wl.describe()} fp8={fp8}")
+    g = dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, fp8)
+    recv = g["_dispatched"].recv_x
+    if fp8:
+        def deq(q, s):
+            return (q.view(torch.float8_e4m3fn).float() * s.repeat_interleave(128, 1)).to(torch.bfloat16)
+
+        y = deq(recv, g["_dispatched"].recv_scales)        # the GPU's dispatched rows
+        q, sc = oracle.quantize_rows(inp["x"])             # the expected rows: the oracle's codes
+        xs = deq(torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda())
+    else:
+        y = recv
+        xs = dev_bf16(inp["x"])
+    ones = np.ones_like(inp["topk_w"])
+    out = _gpu_combine(y.contiguous(), g["pos_exp"], ones)
+    kval = torch.from_numpy((inp["topk_idx"] >= 0).sum(1).astype(np.float32)).cuda()
+    ref = host_bits((xs.float() * kval[:, None]).to(torch.bfloat16)).copy()
+    ref[(ref & 0x7FFF) == 0] = 0
+    _eq(out, ref, "unit-weight combine")
+
+
+# ------------------------------------------------------------------ low latency
+
+def _ll_gpu(x, topk, E, R, src, cap, R_buf, fp8):
+    import combine_get_dispatch_counts_amd as epx
+
+    T, h = x.shape
+    K = topk.shape[1]
+    buf = epx.alloc_ll(E, R_buf, cap, h, T, K, fp8, torch.device("cuda"))
+    buf.ll_x.view(torch.uint8).fill_(CANARY)
+    if buf.ll_scales is not None:
+        buf.ll_scales.view(torch.uint8).fill_(CANARY)
+    buf.ll_src.view(torch.uint8).fill_(CANARY)
+    epx.ll_dispatch(dev_bf16(x), torch.from_numpy(topk).cuda(), E, R, src, cap, R_buf, fp8, buf)
+    assert epx.get_error() == 0
+    return buf
+
+
+@pytest.mark.parametrize("cfg,T,src,R_buf_full,fp8,cap", [
+    (1, None, 0, True, True, 64), (1, None, 3, True, False, 64), (1, None, 2, False, True, 80),
+    (2, 24, 31, False, False, 32), (2, None, 0, False, True, 128), (2, 1, 5, False, True, 1),
+])
+def test_ll_dispatch_small(cfg, T, src, R_buf_full, fp8, cap):
+    inp = synth.make_inputs(cfg, T=T)
+    wl = inp["workload"]
+    topk = inp["topk_idx"].copy()
+    topk[np.random.default_rng(2).random(topk.shape) < 0.05] = -1
+    R_buf = wl.R if R_buf_full else 1
+    say(f"ll_dispatch {wl.describe()} T={topk.shape[0]} src={src} R_buf={R_buf} fp8={fp8} cap={cap}")
+    buf = _ll_gpu(inp["x"], topk, wl.E, wl.R, src, cap, R_buf, fp8)
+    o = oracle.ll_dispatch(inp["x"], topk, wl.E, wl.R, src, cap, R_buf, fp8=fp8)
+    _eq(host_bits(buf.pos_ll), o["pos_ll"], "pos_ll")
+    _eq(host_bits(buf.ll_count), o["ll_count"], "ll_count")
+    _eq(host_bits(buf.ll_src), o["ll_src"], "ll_src")
+    _eq(host_bits(buf.ll_x), o["ll_x"], "ll_x")
+    if fp8:
+        _eq(host_bits(buf.ll_scales), o["ll_scales"], "ll_scales")
+
+
+def test_ll_dispatch_decode_full_buffer():
+    """Decode workload at full size: T=128, E=256, R=32, cap=128, FP8, the
+    full logical buffer of all 32 destinations (1,048,576 rows, 7.75 GB).
+    The owned regions (src_rank's slice) are compared with the oracle's
+    compact layout; every other region must keep its canary and count -1."""
+    inp = synth.make_inputs(2)
+    wl = inp["workload"]
+    for src in (0, wl.R - 1):
+        say(f"ll_dispatch full buffer {wl.describe()} src={src}")
+        buf = _ll_gpu(inp["x"], inp["topk_idx"], wl.E, wl.R, src, wl.cap, wl.R, True)
+        o = oracle.ll_dispatch(inp["x"], inp["topk_idx"], wl.E, wl.R, src, wl.cap, 1, fp8=True)
+        E, R, cap, h = wl.E, wl.R, wl.cap, wl.h
+        x4 = buf.ll_x.view(E, R, cap, h)
+        s4 = buf.ll_scales.view(E, R, cap, h // 128)
+        _eq(host_bits(x4[:, src]).reshape(E * cap, h), o["ll_x"], "owned ll_x")
+        _eq(host_bits(s4[:, src]).reshape(E * cap, -1), o["ll_scales"], "owned ll_scales")
+        _eq(host_bits(buf.ll_src.view(E, R, cap)[:, src]).reshape(-1), o["ll_src"], "owned ll_src")
+        cnt = host_bits(buf.ll_count).reshape(E, R)
+        _eq(cnt[:, src], o["ll_count"], "owned counts")
+        assert (np.delete(cnt, src, axis=1) == -1).all()
+        for name, t in (("ll_x", buf.ll_x), ("ll_scales", buf.ll_scales), ("ll_src", buf.ll_src)):
+            touched = (t.view(torch.uint8).view(E, R, -1) != CANARY).any(dim=2)
+            touched[:, src] = False
+            assert not bool(touched.any()), f"a foreign region of {name} was written"
+            del touched
+        # handle rows follow the address formula of the full layout
+        slot_rows = o["pos_ll"]
+        e = inp["topk_idx"]
+        full = np.where(slot_rows >= 0, (e * R + src) * cap + (slot_rows - e * cap), -1)
+        _eq(host_bits(buf.pos_ll), full, "pos_ll")
+        del buf, x4, s4
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_ll_combine(cfg):
+    inp = synth.make_inputs(cfg)
+    wl = inp["workload"]
+    say(f"ll combine {wl.describe()}")
+    cap = max(wl.cap, wl.T)
+    buf = _ll_gpu(inp["x"], inp["topk_idx"], wl.E, wl.R, 0, cap, 1, True)
+    o = oracle.ll_dispatch(inp["x"], inp["topk_idx"], wl.E, wl.R, 0, cap, 1, fp8=True)
+    _eq(host_bits(buf.pos_ll), o["pos_ll"], "pos_ll")
+    y = synth.expert_outputs(buf.ll_x.shape[0], wl.h, seed=5 + cfg, device="cuda")
+    out = _gpu_combine(y, host_bits(buf.pos_ll), inp["topk_w"])
+    _eq(out, oracle.combine(host_bits(y), inp["topk_w"], o["pos_ll"]), "ll combined_x")
+
+
+# ------------------------------------------------------------------ errors
+
+def test_error_paths():
+    """Every error is forced from the host; each kernel still bounds-checks
+    and exits normally."""
+    import combine_get_dispatch_counts_amd as epx
+
+    inp = synth.make_inputs(1)
+    wl = inp["workload"]
+    x, tk, w = dev_bf16(inp["x"]), torch.from_numpy(inp["topk_idx"]).cuda(), \
+        torch.from_numpy(inp["topk_w"]).cuda()
+    say("errors: T > cap")
+    with pytest.raises(epx.EpxError) as ei:
+        epx.ll_dispatch(x, tk, wl.E, wl.R, 0, wl.T - 1, 1, True)
+    assert ei.value.code == -2
+    say("errors: fp8 with h % 128 != 0")
+    x136 = torch.zeros((wl.T, 136), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(epx.EpxError) as ei:
+        epx.dispatch(x136, tk, w, wl.E, wl.R, fp8=True, exact=False)
+    assert ei.value.code == -3
+    say("errors: misaligned x")
+    big = torch.zeros(wl.T * wl.h + 1, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(epx.EpxError) as ei:
+        epx.dispatch(big[1:].view(wl.T, wl.h), tk, w, wl.E, wl.R, exact=False)
+    assert ei.value.code == -1
+    say("errors: E % R != 0")
+    with pytest.raises(epx.EpxError) as ei:
+        epx.get_dispatch_layout(tk, wl.E, 3)
+    assert ei.value.code == -1
+    assert epx.get_error() == 0
+    say("errors: top-k entry out of range")
+    bad = inp["topk_idx"].copy()
+    bad[5, 1] = wl.E + 3
+    bad[9, 0] = -7
+    epx.get_dispatch_layout(torch.from_numpy(bad).cuda(), wl.E, wl.R, 4)
+    assert epx.get_error() == 1
+    say("errors: capacity one row short, guard rows stay untouched")
+    lay = epx.get_dispatch_layout(tk, wl.E, wl.R)
+    n_send, n_recv = (int(v) for v in lay.totals.cpu())
+    buf = epx.alloc_dispatch(wl.T, wl.h, wl.K, n_send + 4, n_recv + 4, False, x.device)
+    for v in buf.values():
+        if v is not None:
+            v.view(torch.uint8).fill_(CANARY)
+    view = dict(buf)
+    for k in list(view):
+        if k.startswith("send"):
+            view[k] = buf[k][:n_send - 1]
+        elif k.startswith("recv"):
+            view[k] = buf[k][:n_recv - 1]
+    epx.dispatch(x, tk, w, wl.E, wl.R, layout=lay, out=view)
+    assert epx.get_error() == 2
+    for k, v in buf.items():
+        if k == "pos_exp" or v is None:
+            continue
+        n = n_send if k.startswith("send") else n_recv
+        assert bool((v[n - 1:].view(torch.uint8) == CANARY).all()), f"{k} written past capacity"
+    say("errors: combine handle beyond the expert-output rows")
+    y = synth.expert_outputs(10, wl.h, seed=1, device="cuda")
+    pos = torch.full((wl.T, wl.K), -1, dtype=torch.int32, device="cuda")
+    pos[3, 0] = 10
+    pos[4, 1] = 2
+    out = epx.combine(y, pos, w)
+    assert epx.get_error() == 4
+    ref = oracle.combine(host_bits(y), inp["topk_w"], np.where(host_bits(pos) >= 10, -1, host_bits(pos)))
+    _eq(host_bits(out), ref, "combine skipping the bad handle row")
+    say("errors: LL row repeating an expert past the capacity")
+    rep = np.zeros((4, 2), np.int64)  # every entry to expert 0: 8 rows, cap 4
+    buf = epx.alloc_ll(wl.E, 1, 4, wl.h, 4, 2, False, x.device)
+    buf.ll_x.view(torch.uint8).fill_(CANARY)
+    epx.ll_dispatch(x[:4].contiguous(), torch.from_numpy(rep).cuda(), wl.E, wl.R, 0, 4, 1, False, buf)
+    assert epx.get_error() == 2
+    assert bool((buf.ll_x[4:].view(torch.uint8) == CANARY).all())
