@@ -83,6 +83,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", type=int, default=1, help="also time the step replayed from a HIP graph")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="MALL flush size for the labelled cold-cache figure (0: skip)")
     args = ap.parse_args()
@@ -112,10 +113,12 @@ def main():
     expert_out = synth.expert_outputs(cap_recv, h, seed=4242, device="cuda")
     out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
 
+    lay_buf = epx.alloc_layout(T, K, E, R, None, dev)
+
     def step(ev=None):
         if ev:
             ev[0].record()
-        lay = epx.get_dispatch_layout(tk, E, R, workspace=ws)
+        lay = epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay_buf)
         if ev:
             ev[1].record()
         d = epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs)
@@ -144,6 +147,32 @@ def main():
     phase = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3
              for j, name in enumerate(["layout", "dispatch", "combine"])}
     assert epx.get_error() == 0
+
+    # the same step captured once in a HIP graph and replayed (no host launch
+    # work per step); checked against the eager result first
+    graph_us = None
+    if args.graph:
+        ref_out = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out.view(torch.int16), ref_out.view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager step")
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - tg0) * 1e6 / args.steps
+        del g, ref_out
 
     # labelled cold-cache figure: flush the 256 MB MALL before each step
     cold_us = None
@@ -198,6 +227,7 @@ def main():
         "phase_us": {k: round(v, 2) for k, v in phase.items()},
         "phase_gbs": {"dispatch": round(disp_gbs, 1), "combine": round(comb_gbs, 1)},
         "cold_cache_us_per_layer": round(cold_us, 2) if cold_us else None,
+        "graph_us_per_layer": round(graph_us, 2) if graph_us else None,
         "roofline": {"bound": "hbm", "achieved": round(disp_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(disp_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel": "dispatch_kernel<bf16>",

@@ -14,6 +14,7 @@ from .api import (  # noqa: E402
     Layout,
     LowLatency,
     alloc_dispatch,
+    alloc_layout,
     alloc_ll,
     combine,
     dispatch,
@@ -26,5 +27,5 @@ from .api import (  # noqa: E402
 )
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
-           "get_error", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
+           "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
            "ll_reset", "alloc_ll", "ll_dispatch"]

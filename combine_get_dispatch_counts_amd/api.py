@@ -87,18 +87,14 @@ class Layout:
     num_ranks: int
 
 
-def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
-                        num_channels: int | None = None, workspace: torch.Tensor | None = None,
-                        totals_host: torch.Tensor | None = None) -> Layout:
-    _need(topk_idx, torch.int64, "topk_idx", 2)
-    dev = topk_idx.device
-    T, K = topk_idx.shape
-    E, R = num_experts, num_ranks
-    i32 = dict(dtype=torch.int32, device=dev)
-    lay = Layout(
+def alloc_layout(T: int, K: int, E: int, R: int, num_channels: int | None,
+                 device: torch.device) -> Layout:
+    """Output tensors for get_dispatch_layout (reusable across calls)."""
+    i32 = dict(dtype=torch.int32, device=device)
+    return Layout(
         num_tokens_per_expert=torch.empty(E, **i32),
         num_tokens_per_rank=torch.empty(R, **i32),
-        is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
+        is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=device),
         rank_off=torch.empty(R + 1, **i32),
         exp_off=torch.empty(E + 1, **i32),
         pos_in_rank=torch.empty((T, R), **i32),
@@ -106,17 +102,39 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
         channel_prefix=torch.empty((R, num_channels), **i32) if num_channels else None,
         totals=torch.empty(2, **i32),
         num_experts=E, num_ranks=R)
-    need = workspace_size(T, K, E, R)
+
+
+def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                        num_channels: int | None = None, workspace: torch.Tensor | None = None,
+                        totals_host: torch.Tensor | None = None,
+                        out: Layout | None = None) -> Layout:
+    """Counts, is_token_in_rank and receive offsets for topk_idx. ``out``
+    (from alloc_layout with the same shapes) avoids allocating; ``workspace``
+    must hold workspace_size(T, K, E, R) bytes; ``totals_host`` (pinned int32
+    [2]) also receives the totals, readable after a stream synchronisation."""
+    _need(topk_idx, torch.int64, "topk_idx", 2)
+    dev = topk_idx.device
+    T, K = topk_idx.shape
+    E, R = num_experts, num_ranks
+    lay = out if out is not None else alloc_layout(T, K, E, R, num_channels, dev)
+    if out is not None:
+        if tuple(lay.pos_in_rank.shape) != (T, R) or tuple(lay.slot_in_expert.shape) != (T, K) \
+                or lay.num_tokens_per_expert.numel() != E:
+            raise ValueError("out was allocated for different shapes")
+        if num_channels and (lay.channel_prefix is None
+                             or tuple(lay.channel_prefix.shape) != (R, num_channels)):
+            raise ValueError("out has no channel_prefix of shape (R, num_channels)")
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
     if totals_host is not None and not (totals_host.is_pinned() and totals_host.numel() >= 2
                                         and totals_host.dtype == torch.int32):
         raise ValueError("totals_host must be a pinned int32 tensor of >= 2 elements")
+    cp = lay.channel_prefix if num_channels else None
     rc = _lib.load().epx_get_dispatch_layout(
         _ctx(dev), _p(topk_idx), T, K, E, R, num_channels or 0,
         _p(lay.num_tokens_per_expert), _p(lay.num_tokens_per_rank), _p(lay.is_token_in_rank),
         _p(lay.rank_off), _p(lay.exp_off), _p(lay.pos_in_rank), _p(lay.slot_in_expert),
-        _p(lay.channel_prefix), _p(lay.totals), _p(totals_host), _p(workspace),
+        _p(cp), _p(lay.totals), _p(totals_host), _p(workspace),
         workspace.numel(), _stream(dev))
     check(rc, "epx_get_dispatch_layout")
     return lay
@@ -258,5 +276,5 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
 
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
-           "get_error", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
+           "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
            "ll_reset", "alloc_ll", "ll_dispatch"]

@@ -1,10 +1,13 @@
 // dispatch.hip -- high-throughput dispatch (pack + permute, optional FP8) and
 // the low-latency fixed-slot dispatch.
 //
-// Both kernels give one token to one block: the block reads the token's row
-// of x from HBM once (16-byte loads), optionally quantises it to FP8 in
-// registers, and writes it to every destination row with 16-byte streaming
-// stores, so each destination costs exactly one row write.
+// One wave (64 lanes) per token. The wave first issues the loads of the
+// token's row of x (16 bytes per lane per vector; quantising it to FP8 in
+// registers when asked), then works out the token's destination rows while
+// those loads are in flight, then writes the row to every destination with
+// 16-byte stores: x is read from HBM once and each destination costs exactly
+// one row write. Destination rows live in lanes and are broadcast with
+// readlane, so the kernel needs no LDS and no barrier.
 //
 // [P2] "DeepEP 学习笔记" (DeepEP study notes), "dispatch 过程": a token goes,
 // in token order, to every rank is_token_in_rank marks, together with its
@@ -12,76 +15,80 @@
 // activation per destination rank. [P1] "事件驱动 EP 内核的调度策略与零拷贝
 // 通信", "高吞吐量模式：协调阶段与紧凑缓冲区": exact-size receive buffer, then
 // a local permute into contiguous per-expert blocks. On one GPU the pack and
-// the permute read the same register copy of the row, so the permute costs
+// the permute store the same register copy of the row, so the permute costs
 // no second read. [P1] "低延迟模式：固定缓冲区与信号槽机制": fixed per-
 // (source, expert) regions, FP8 payload. [P3] "DeepSeek DeepEP探索：低延迟分发",
 // 3.2: the local path is an unrolled 16-byte vector copy with non-caching
-// loads and stores -- kept here as streaming 16-byte moves.
+// loads -- kept here as streaming 16-byte loads.
+#include <type_traits>
+
 #include "epx_device.h"
 #include "epx_internal.h"
 
 namespace epx {
 namespace {
 
-constexpr int kBlock = 128;                 // 2 waves per token
-constexpr int kMaxDst = 2 * EPX_MAX_TOPK;  // <= K rank rows + K expert rows
-constexpr int kVecBf16 = 8;                // 16-byte vectors per thread per pass
-constexpr int kSegFp8 = 4;                 // 16-channel segments per thread per pass
+// Per pass a lane holds NV items of the row: 16-byte bf16 vectors (8
+// channels each) or 16-channel FP8 segments. NV is picked per h at launch so
+// the row of the common hidden sizes fits one pass with no idle registers:
+// bf16 NV = 8 (h <= 4096), 14 (h <= 7168), 16 (larger h, several passes);
+// fp8 NV = 4, 7, 8 over the same ranges.
 
-// Copy one bf16 row (h channels) to n destination rows. Destination d < n_a
-// lives in buffer a, the rest in buffer b; rows[d] < 0 means "skip".
-__device__ __forceinline__ void scatter_bf16(const uint16_t *__restrict__ xrow, int h,
-                             const int64_t *rows, int n_a, int n, char *base_a, char *base_b)
+__device__ __forceinline__ int readlane(int v, int lane)
 {
-    const int nvec = h >> 3;
-    const size_t row_bytes = (size_t)h * 2;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
-    for (int v0 = 0; v0 < nvec; v0 += kBlock * kVecBf16) {
-        u32x4 r[kVecBf16];
-#pragma unroll
-        for (int u = 0; u < kVecBf16; ++u) {
-            const int v = v0 + u * kBlock + (int)threadIdx.x;
-            r[u] = (v < nvec) ? load16_stream(src + v) : u32x4{0u, 0u, 0u, 0u};
-        }
-        for (int d = 0; d < n; ++d) {
-            const int64_t row = rows[d];
-            if (row < 0)
-                continue;
-            char *dst = (d < n_a ? base_a : base_b) + (size_t)row * row_bytes;
-#pragma unroll
-            for (int u = 0; u < kVecBf16; ++u) {
-                const int v = v0 + u * kBlock + (int)threadIdx.x;
-                if (v < nvec)
-                    store16_stream(dst + (size_t)v * 16, r[u]);
-            }
-        }
-    }
+    return __builtin_amdgcn_readlane(v, lane);
 }
 
-// Quantise one bf16 row to e4m3 with one fp32 scale per 128 channels and copy
-// codes + scales to n destination rows (same destination rules as above).
-// A lane owns 16 consecutive channels, so a 128-channel group is 8 adjacent
-// lanes; amax is reduced over them with xor shuffles. h % 128 == 0.
-__device__ __forceinline__ void scatter_fp8(const uint16_t *__restrict__ xrow, int h, const int64_t *rows,
-                            int n_a, int n, uint8_t *q_a, float *s_a, uint8_t *q_b, float *s_b)
-{
-    const int nseg = h >> 4;
-    const int ngrp = h >> 7;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
-    for (int s0 = 0; s0 < nseg; s0 += kBlock * kSegFp8) {
-        u32x4 q[kSegFp8];
-        float sc[kSegFp8];
+
+// One pass of a bf16 row held in registers: vector v of the pass is lane +
+// 64*u for u < NV.
+template <int NV>
+struct RowBf16 {
+    static constexpr int kPerPass = NV * kWave;
+    u32x4 r[NV];
+    __device__ __forceinline__ void load(const u32x4 *src, int v0, int nvec)
+    {
 #pragma unroll
-        for (int u = 0; u < kSegFp8; ++u) {
-            const int sg = s0 + u * kBlock + (int)threadIdx.x;
+        for (int u = 0; u < NV; ++u) {
+            const int v = v0 + u * kWave + lane_id();
+            r[u] = (v < nvec) ? load16_stream(src + v) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(char *dst_row, int v0, int nvec) const
+    {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int v = v0 + u * kWave + lane_id();
+            if (v < nvec)
+                store16_stream(dst_row + (size_t)v * 16, r[u]);
+        }
+    }
+};
+
+// One pass of an FP8 row: segment sg = s0 + lane + 64*u covers channels
+// [16 sg, 16 sg + 16); a 128-channel group is 8 adjacent lanes, reduced with
+// xor shuffles. Codes: e4m3 of x / s with s = max(amax, 1e-4) / 448, both
+// IEEE fp32 divisions.
+template <int NV>
+struct RowFp8 {
+    static constexpr int kPerPass = NV * kWave;
+    u32x4 q[NV];
+    float sc[NV];
+    __device__ __forceinline__ void load_quantise(const u32x4 *src, int s0, int nseg)
+    {
+        u32x4 lo[NV], hi[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int sg = s0 + u * kWave + lane_id();
             const bool active = sg < nseg;  // uniform over each 8-lane group
-            u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-            if (active) {
-                lo = load16_stream(src + 2 * sg);
-                hi = load16_stream(src + 2 * sg + 1);
-            }
+            lo[u] = active ? load16_stream(src + 2 * sg) : u32x4{0u, 0u, 0u, 0u};
+            hi[u] = active ? load16_stream(src + 2 * sg + 1) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
             float f[16];
-            const uint32_t p[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const uint32_t p[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w,
+                                   hi[u].x, hi[u].y, hi[u].z, hi[u].w};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 f[2 * i] = bf16_lo(p[i]);
@@ -104,126 +111,156 @@ __device__ __forceinline__ void scatter_fp8(const uint16_t *__restrict__ xrow, i
             q[u] = u32x4{wd[0], wd[1], wd[2], wd[3]};
             sc[u] = s;
         }
-        for (int d = 0; d < n; ++d) {
-            const int64_t row = rows[d];
-            if (row < 0)
-                continue;
-            uint8_t *qd = (d < n_a ? q_a : q_b) + (size_t)row * h;
-            float *sd = (d < n_a ? s_a : s_b) + (size_t)row * ngrp;
+    }
+    __device__ __forceinline__ void store(uint8_t *q_row, float *s_row, int s0, int nseg) const
+    {
 #pragma unroll
-            for (int u = 0; u < kSegFp8; ++u) {
-                const int sg = s0 + u * kBlock + (int)threadIdx.x;
-                if (sg < nseg) {
-                    store16_stream(qd + (size_t)sg * 16, q[u]);
-                    if ((sg & 7) == 0)
-                        sd[sg >> 3] = sc[u];
-                }
+        for (int u = 0; u < NV; ++u) {
+            const int sg = s0 + u * kWave + lane_id();
+            if (sg < nseg) {
+                store16_stream(q_row + (size_t)sg * 16, q[u]);
+                if ((sg & 7) == 0)
+                    s_row[sg >> 3] = sc[u];
             }
         }
     }
-}
+};
 
-template <bool FP8>
-__global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a)
+// Destination rows of one token, one per lane: lane r holds the rank-major
+// row for rank r (bit r of rbits), lane k the expert-major row of entry k
+// (bit k of vbits); -1 = skip (capacity overflow, already flagged).
+struct Dests {
+    uint64_t rbits, vbits;
+    int send_row, recv_row;
+};
+
+// Write the token's row (the pass held in `row`, plus any further passes
+// loaded here) to every destination: send rows in buffer a, recv rows in b.
+template <bool FP8, typename Row>
+__device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t *xrow, int h,
+                                        void *a_x, float *a_s, void *b_x, float *b_s)
 {
-    __shared__ int64_t s_row[kMaxDst];
-    __shared__ int s_rank[EPX_MAX_TOPK];
-    __shared__ int s_nsend, s_n;
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const int64_t tk = (int64_t)t * a.K;
-
-    if (tid < kWave) {
-        const int lane = tid;
-        const int64_t e = lane < a.K ? a.topk_idx[tk + lane] : -1;
-        const bool valid = e >= 0 && e < a.E;
-        const int ei = valid ? (int)e : 0;
-        const uint64_t rbits = wave_or(valid ? (1ull << (ei / a.L)) : 0ull);
-        const int nsend = __popcll(rbits);
-        // rank-major rows: lane r owns rank r; ascending ranks
-        if (lane < a.R && ((rbits >> lane) & 1ull)) {
-            const int j = __popcll(rbits & lanes_below(lane));
-            int64_t row = (int64_t)a.rank_off[lane] + a.pos_in_rank[(int64_t)t * a.R + lane];
-            if (row < 0 || row >= a.send_cap) {
-                flag_error(a.err, EPX_DEV_OVERFLOW);
-                row = -1;
-            }
-            s_row[j] = row;
-            s_rank[j] = lane;
-        }
-        // expert-major rows: valid entries in k order
-        const uint64_t vbits = __ballot(valid);
-        if (lane < a.K) {
-            int32_t pe = -1;
-            if (valid) {
-                const int j = nsend + __popcll(vbits & lanes_below(lane));
-                int64_t row = (int64_t)a.exp_off[ei] + a.slot_in_expert[tk + lane];
-                if (row < 0 || row >= a.recv_cap) {
-                    flag_error(a.err, EPX_DEV_OVERFLOW);
-                    row = -1;
-                } else {
-                    pe = (int32_t)row;
-                }
-                s_row[j] = row;
-            }
-            a.pos_exp[tk + lane] = pe;
-        }
-        if (lane == 0) {
-            s_nsend = nsend;
-            s_n = nsend + __popcll(vbits);
-        }
-    }
-    __syncthreads();
-    const int nsend = s_nsend, n = s_n;
-
-    // per-row metadata: source token, and the top-k list seen from the row's rank
-    for (int i = tid; i < nsend * a.K; i += kBlock) {
-        const int j = i / a.K, k = i - j * a.K;
-        const int64_t row = s_row[j];
-        if (row < 0)
-            continue;
-        const int r = s_rank[j];
-        const int64_t e = a.topk_idx[tk + k];
-        const bool on_r = e >= 0 && e < a.E && (int)e / a.L == r;
-        a.send_topk_idx[row * a.K + k] = on_r ? e - (int64_t)r * a.L : -1;
-        a.send_topk_w[row * a.K + k] = on_r ? a.topk_w[tk + k] : 0.0f;
-    }
-    if (tid < n) {
-        const int64_t row = s_row[tid];
-        if (row >= 0) {
-            if (tid < nsend)
-                a.send_src[row] = t;
+    const int nvec = h >> 3, nseg = h >> 4, ngrp = h >> 7;
+    const int per_pass = Row::kPerPass;
+    const int nitems = FP8 ? nseg : nvec;
+    const size_t row_bytes = FP8 ? (size_t)h : (size_t)h * 2;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
+    for (int i0 = 0; i0 < nitems; i0 += per_pass) {
+        if (i0 > 0) {
+            if constexpr (FP8)
+                row.load_quantise(src, i0, nseg);
             else
-                a.recv_src[row] = t;
+                row.load(src, i0, nvec);
+        }
+        for (uint64_t m = d.rbits; m; m &= m - 1) {
+            const int r = readlane(d.send_row, __builtin_ctzll(m));
+            if (r < 0)
+                continue;
+            if constexpr (FP8)
+                row.store(static_cast<uint8_t *>(a_x) + (size_t)r * row_bytes,
+                          a_s + (size_t)r * ngrp, i0, nseg);
+            else
+                row.store(static_cast<char *>(a_x) + (size_t)r * row_bytes, i0, nvec);
+        }
+        for (uint64_t m = d.vbits; m; m &= m - 1) {
+            const int r = readlane(d.recv_row, __builtin_ctzll(m));
+            if (r < 0)
+                continue;
+            if constexpr (FP8)
+                row.store(static_cast<uint8_t *>(b_x) + (size_t)r * row_bytes,
+                          b_s + (size_t)r * ngrp, i0, nseg);
+            else
+                row.store(static_cast<char *>(b_x) + (size_t)r * row_bytes, i0, nvec);
         }
     }
-
-    const uint16_t *xrow = a.x + (size_t)t * a.h;
-    if (FP8)
-        scatter_fp8(xrow, a.h, s_row, nsend, n, static_cast<uint8_t *>(a.send_x), a.send_scales,
-                    static_cast<uint8_t *>(a.recv_x), a.recv_scales);
-    else
-        scatter_bf16(xrow, a.h, s_row, nsend, n, static_cast<char *>(a.send_x),
-                     static_cast<char *>(a.recv_x));
 }
 
-// Low-latency dispatch, one launch. Block t handles token t; every block
+template <bool FP8, int NV>
+__global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
+{
+    const int t = blockIdx.x, lane = threadIdx.x;
+    const int64_t tk = (int64_t)t * a.K;
+    const uint16_t *xrow = a.x + (size_t)t * a.h;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
+
+    // first pass of the row: issued before anything else
+    typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
+    if constexpr (FP8)
+        row.load_quantise(src, 0, a.h >> 4);
+    else
+        row.load(src, 0, a.h >> 3);
+
+    // destinations
+    const int64_t e = lane < a.K ? a.topk_idx[tk + lane] : -1;
+    const bool valid = e >= 0 && e < a.E;
+    const int ei = valid ? (int)e : 0;
+    Dests d;
+    d.rbits = uniform64(wave_or(valid ? (1ull << (ei / a.L)) : 0ull));
+    d.vbits = uniform64(__ballot(valid));
+    d.send_row = -1;
+    d.recv_row = -1;
+    if (lane < a.R && ((d.rbits >> lane) & 1ull)) {
+        const int64_t r = (int64_t)a.rank_off[lane] + a.pos_in_rank[(int64_t)t * a.R + lane];
+        if (r >= 0 && r < a.send_cap)
+            d.send_row = (int)r;
+        else
+            flag_error(a.err, EPX_DEV_OVERFLOW);
+    }
+    if (lane < a.K) {
+        if (valid) {
+            const int64_t r = (int64_t)a.exp_off[ei] + a.slot_in_expert[tk + lane];
+            if (r >= 0 && r < a.recv_cap)
+                d.recv_row = (int)r;
+            else
+                flag_error(a.err, EPX_DEV_OVERFLOW);
+        }
+        a.pos_exp[tk + lane] = d.recv_row;
+        if (d.recv_row >= 0)
+            a.recv_src[d.recv_row] = t;
+    }
+    // per send row: source token and the top-k list seen from that rank
+    if (d.send_row >= 0) {
+        const int64_t row = d.send_row;
+        a.send_src[row] = t;
+        for (int k = 0; k < a.K; ++k) {
+            const int64_t ek = a.topk_idx[tk + k];
+            const bool on_r = ek >= 0 && ek < a.E && (int)ek / a.L == lane;
+            a.send_topk_idx[row * a.K + k] = on_r ? ek - (int64_t)lane * a.L : -1;
+            a.send_topk_w[row * a.K + k] = on_r ? a.topk_w[tk + k] : 0.0f;
+        }
+    }
+
+    scatter<FP8>(row, d, xrow, a.h, a.send_x, a.send_scales, a.recv_x, a.recv_scales);
+}
+
+// Low-latency dispatch, one launch. Block t (one wave) handles token t. It
 // first histograms all T*K entries in LDS (decode batches are small): the
 // full histogram gives the count slots, the part before token t gives t's
 // slots. LDS atomics only add, so the result does not depend on their order.
-template <bool FP8>
-__global__ __launch_bounds__(kBlock) void ll_dispatch_kernel(LLArgs a)
+template <bool FP8, int NV>
+__global__ __launch_bounds__(kWave) void ll_dispatch_kernel(LLArgs a)
 {
     extern __shared__ int hist[];  // [E] all entries, [E] entries before token t
-    __shared__ int64_t s_row[EPX_MAX_TOPK];
-    __shared__ int s_n;
-    const int t = blockIdx.x, tid = threadIdx.x;
+    const int t = blockIdx.x, lane = threadIdx.x;
     int *hist_all = hist, *hist_before = hist + a.E;
-    for (int i = tid; i < 2 * a.E; i += kBlock)
+    const bool have_token = t < a.T;
+    const int64_t tk = (int64_t)t * a.K;
+    const uint16_t *xrow = a.x + (size_t)t * a.h;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
+
+    typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
+    if (have_token) {
+        if constexpr (FP8)
+            row.load_quantise(src, 0, a.h >> 4);
+        else
+            row.load(src, 0, a.h >> 3);
+    }
+
+    for (int i = lane; i < 2 * a.E; i += kWave)
         hist[i] = 0;
     __syncthreads();
     const int64_t n_ent = (int64_t)a.T * a.K;
-    const int64_t tk = (int64_t)t * a.K;
-    for (int64_t i = tid; i < n_ent; i += kBlock) {
+    for (int64_t i = lane; i < n_ent; i += kWave) {
         const int64_t e = a.topk_idx[i];
         if (e == -1)
             continue;
@@ -239,51 +276,37 @@ __global__ __launch_bounds__(kBlock) void ll_dispatch_kernel(LLArgs a)
     __syncthreads();
 
     // count slots: every expert's count, written by a spread of blocks
-    for (int e = blockIdx.x * kBlock + tid; e < a.E; e += gridDim.x * kBlock) {
+    for (int e = blockIdx.x * kWave + lane; e < a.E; e += gridDim.x * kWave) {
         const int64_t region = a.R_buf == 1 ? e : (int64_t)e * a.R + a.src_rank;
         a.ll_count[region] = hist_all[e];
     }
-    if (t >= a.T)
+    if (!have_token)
         return;
 
-    if (tid < kWave) {
-        const int lane = tid;
-        const int64_t e = lane < a.K ? a.topk_idx[tk + lane] : -1;
-        const bool valid = e >= 0 && e < a.E;
-        int rep = 0;  // earlier entries of this row with the same expert
-        if (valid)
+    const int64_t e = lane < a.K ? a.topk_idx[tk + lane] : -1;
+    const bool valid = e >= 0 && e < a.E;
+    Dests d;
+    d.rbits = 0;
+    d.vbits = uniform64(__ballot(valid));
+    d.send_row = -1;
+    d.recv_row = -1;
+    if (lane < a.K) {
+        if (valid) {
+            int rep = 0;  // earlier entries of this row with the same expert
             for (int k2 = 0; k2 < lane; ++k2)
                 rep += (a.topk_idx[tk + k2] == e);
-        const uint64_t vbits = __ballot(valid);
-        if (lane < a.K) {
-            int32_t p = -1;
-            if (valid) {
-                const int j = __popcll(vbits & lanes_below(lane));
-                const int slot = hist_before[e] + rep;
-                int64_t row = -1;
-                if (slot < a.cap) {
-                    const int64_t region = a.R_buf == 1 ? e : e * a.R + a.src_rank;
-                    row = region * a.cap + slot;
-                    a.ll_src[row] = t;
-                    p = (int32_t)row;
-                } else {
-                    flag_error(a.err, EPX_DEV_OVERFLOW);
-                }
-                s_row[j] = row;
+            const int slot = hist_before[e] + rep;
+            if (slot < a.cap) {
+                const int64_t region = a.R_buf == 1 ? e : e * a.R + a.src_rank;
+                d.recv_row = (int)(region * a.cap + slot);
+                a.ll_src[d.recv_row] = t;
+            } else {
+                flag_error(a.err, EPX_DEV_OVERFLOW);
             }
-            a.pos_ll[tk + lane] = p;
         }
-        if (lane == 0)
-            s_n = __popcll(vbits);
+        a.pos_ll[tk + lane] = d.recv_row;
     }
-    __syncthreads();
-
-    const uint16_t *xrow = a.x + (size_t)t * a.h;
-    if (FP8)
-        scatter_fp8(xrow, a.h, s_row, 0, s_n, nullptr, nullptr, static_cast<uint8_t *>(a.ll_x),
-                    a.ll_scales);
-    else
-        scatter_bf16(xrow, a.h, s_row, 0, s_n, nullptr, static_cast<char *>(a.ll_x));
+    scatter<FP8>(row, d, xrow, a.h, nullptr, nullptr, a.ll_x, a.ll_scales);
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
@@ -295,25 +318,55 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
 
 }  // namespace
 
+// Items per lane per pass for hidden size h (see the comment on NV above).
+static int pick_nv(int h, bool fp8)
+{
+    if (h <= 4096)
+        return fp8 ? 4 : 8;
+    if (h <= 7168)
+        return fp8 ? 7 : 14;
+    return fp8 ? 8 : 16;
+}
+
+template <bool FP8, int NV>
+static void launch_dispatch_nv(const DispatchArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((dispatch_kernel<FP8, NV>), dim3(a.T), dim3(kWave), 0, stream, a);
+}
+
 hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, hipStream_t stream)
 {
     if (a.T == 0)
         return hipSuccess;
-    if (fp8)
-        hipLaunchKernelGGL(dispatch_kernel<true>, dim3(a.T), dim3(kBlock), 0, stream, a);
-    else
-        hipLaunchKernelGGL(dispatch_kernel<false>, dim3(a.T), dim3(kBlock), 0, stream, a);
+    switch (pick_nv(a.h, fp8) + (fp8 ? 100 : 0)) {
+    case 8: launch_dispatch_nv<false, 8>(a, stream); break;
+    case 14: launch_dispatch_nv<false, 14>(a, stream); break;
+    case 16: launch_dispatch_nv<false, 16>(a, stream); break;
+    case 104: launch_dispatch_nv<true, 4>(a, stream); break;
+    case 107: launch_dispatch_nv<true, 7>(a, stream); break;
+    default: launch_dispatch_nv<true, 8>(a, stream); break;
+    }
     return hipGetLastError();
+}
+
+template <bool FP8, int NV>
+static void launch_ll_nv(const LLArgs &a, hipStream_t stream)
+{
+    const dim3 grid(a.T > 0 ? a.T : 1);
+    const size_t lds = sizeof(int) * 2 * (size_t)a.E;
+    hipLaunchKernelGGL((ll_dispatch_kernel<FP8, NV>), grid, dim3(kWave), lds, stream, a);
 }
 
 hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream)
 {
-    const dim3 grid(a.T > 0 ? a.T : 1);
-    const size_t lds = sizeof(int) * 2 * (size_t)a.E;
-    if (fp8)
-        hipLaunchKernelGGL(ll_dispatch_kernel<true>, grid, dim3(kBlock), lds, stream, a);
-    else
-        hipLaunchKernelGGL(ll_dispatch_kernel<false>, grid, dim3(kBlock), lds, stream, a);
+    switch (pick_nv(a.h, fp8) + (fp8 ? 100 : 0)) {
+    case 8: launch_ll_nv<false, 8>(a, stream); break;
+    case 14: launch_ll_nv<false, 14>(a, stream); break;
+    case 16: launch_ll_nv<false, 16>(a, stream); break;
+    case 104: launch_ll_nv<true, 4>(a, stream); break;
+    case 107: launch_ll_nv<true, 7>(a, stream); break;
+    default: launch_ll_nv<true, 8>(a, stream); break;
+    }
     return hipGetLastError();
 }
 

@@ -155,6 +155,9 @@ int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K,
         return EPX_EINVAL;
     if (T > 0 && (!topk_idx || !is_token_in_rank || !pos_in_rank || !slot_in_expert))
         return EPX_EINVAL;
+    if (T > 0 && (!aligned16(is_token_in_rank) || !aligned16(pos_in_rank) ||
+                  !aligned16(slot_in_expert)))
+        return EPX_EINVAL;
     const size_t need = epx::layout_workspace_bytes(T, E, R);
     if (ws_bytes < need)
         return EPX_ECAPACITY;

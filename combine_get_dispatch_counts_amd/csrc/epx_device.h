@@ -97,6 +97,16 @@ __device__ __forceinline__ int wave_inclusive_sum(int v)
     return v;
 }
 
+// A 64-bit value every lane holds alike, moved to scalar registers. The
+// builtin returns a signed int: each half goes through uint32_t so the low
+// half is zero-extended, never sign-extended into the high half.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
 __device__ __forceinline__ uint64_t wave_or(uint64_t v)
 {
 #pragma unroll

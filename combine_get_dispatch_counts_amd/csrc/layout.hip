@@ -64,11 +64,63 @@ __device__ TileLds carve(char *base, int E, int R)
     return s;
 }
 
+// Flat index walker over a [rows, cols] block of a row-major array: thread
+// tid starts at element tid and advances by blockDim, tracking (row, col)
+// with one division up front instead of one per element.
+struct Walk {
+    int row, col, drow, dcol, cols;
+    __device__ Walk(int tid, int step, int ncols)
+    {
+        cols = ncols;
+        row = tid / ncols;
+        col = tid - row * ncols;
+        drow = step / ncols;
+        dcol = step - drow * ncols;
+    }
+    __device__ void next()
+    {
+        row += drow;
+        col += dcol;
+        if (col >= cols) {
+            col -= cols;
+            ++row;
+        }
+    }
+};
+
 // Build the bitmaps and per-wave expert counts of one tile. Every thread of
-// the block must call this (it holds barriers).
-__device__ void build_tile(const LayoutArgs &a, int tile_base, const TileLds &s, bool report)
+// the block must call this (it holds barriers). The token's K entries are
+// loaded first, so their latency overlaps the LDS clear; they are returned
+// in ek (expert id, -1 = no route, -2 = out of range).
+__device__ void build_tile(const LayoutArgs &a, int tile_base, const TileLds &s, bool report,
+                           int (&ek)[EPX_MAX_TOPK])
 {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int t = tile_base + tid;
+    // Loads go out 8 at a time from clamped (always valid) addresses and are
+    // masked afterwards, so they are in flight together rather than one
+    // branch and one wait each. A tile exists only when T >= 1.
+    const int64_t *row = a.topk_idx + (int64_t)min(t, a.T - 1) * a.K;
+#pragma unroll
+    for (int k0 = 0; k0 < EPX_MAX_TOPK; k0 += 8) {
+        if (k0 < a.K) {
+            int64_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = row[min(k0 + j, a.K - 1)];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t e = v[j];
+                ek[k0 + j] = (k0 + j >= a.K || t >= a.T) ? -1
+                             : (e >= 0 && e < a.E)      ? (int)e
+                             : (e == -1 ? -1 : -2);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                ek[k0 + j] = -1;
+        }
+    }
     for (int i = tid; i < W * a.E; i += blockDim.x) {
         s.emask[i] = 0;
         s.ecnt[i] = 0;
@@ -79,28 +131,23 @@ __device__ void build_tile(const LayoutArgs &a, int tile_base, const TileLds &s,
         s.dupwave[tid] = 0;
     __syncthreads();
 
-    const int t = tile_base + tid;
     const uint64_t bit = 1ull << lane;
     uint64_t rbits = 0;
-    int dup = 0;
-    if (t < a.T) {
-        const int64_t *row = a.topk_idx + (int64_t)t * a.K;
-        for (int k = 0; k < a.K; ++k) {
-            const int64_t e = row[k];
-            if (e == -1)
-                continue;
-            if (e < 0 || e >= a.E) {
-                if (report)
-                    flag_error(a.err, EPX_DEV_BAD_ROUTE);
-                continue;
-            }
-            const uint64_t old =
-                atomicOr(reinterpret_cast<unsigned long long *>(&s.emask[w * a.E + e]), bit);
-            dup |= (old & bit) != 0;
-            atomicAdd(&s.ecnt[w * a.E + e], 1);
-            rbits |= 1ull << (int)(e / a.L);
-        }
+    int dup = 0, bad = 0;
+#pragma unroll
+    for (int k = 0; k < EPX_MAX_TOPK; ++k) {
+        const int e = ek[k];
+        bad |= (e == -2);
+        if (e < 0)
+            continue;
+        const uint64_t old =
+            atomicOr(reinterpret_cast<unsigned long long *>(&s.emask[w * a.E + e]), bit);
+        dup |= (old & bit) != 0;
+        atomicAdd(&s.ecnt[w * a.E + e], 1);
+        rbits |= 1ull << (e / a.L);
     }
+    if (report && bad)
+        flag_error(a.err, EPX_DEV_BAD_ROUTE);
     s.tok_rbits[tid] = rbits;
     for (uint64_t m = rbits; m; m &= m - 1) {
         const int r = __builtin_ctzll(m);
@@ -145,19 +192,36 @@ __device__ void wave_exclusive_scan(const int *in, int n, int *out)
         out[n] = incl;
 }
 
+// Row of R bytes (0/1) for one token; 16-byte stores when R allows it.
+__device__ void write_rank_row(uint8_t *dst, uint64_t rbits, int R)
+{
+    if ((R & 15) == 0) {
+        for (int r0 = 0; r0 < R; r0 += 16) {
+            uint32_t wd[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t nib = (uint32_t)(rbits >> (r0 + 4 * j)) & 0xFu;
+                wd[j] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+            }
+            *reinterpret_cast<u32x4 *>(dst + r0) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+        }
+    } else {
+        for (int r = 0; r < R; ++r)
+            dst[r] = (uint8_t)((rbits >> r) & 1ull);
+    }
+}
+
 __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(LayoutArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const TileLds s = carve(lds, a.E, a.R);
     const int tile_base = blockIdx.x * kLayoutTile;
-    build_tile(a, tile_base, s, true);
+    int ek[EPX_MAX_TOPK];
+    build_tile(a, tile_base, s, true, ek);
 
-    const int ntok = min(kLayoutTile, a.T - tile_base);
-    uint8_t *itr = a.is_token_in_rank + (int64_t)tile_base * a.R;
-    for (int i = threadIdx.x; i < ntok * a.R; i += blockDim.x) {
-        const int tt = i / a.R, r = i - tt * a.R;
-        itr[i] = (uint8_t)((s.tok_rbits[tt] >> r) & 1ull);
-    }
+    const int t = tile_base + (int)threadIdx.x;
+    if (t < a.T)
+        write_rank_row(a.is_token_in_rank + (int64_t)t * a.R, s.tok_rbits[threadIdx.x], a.R);
     int32_t *cnt = a.tile_cnt + (int64_t)blockIdx.x * (a.E + a.R);
     for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
         int c = 0;
@@ -180,16 +244,25 @@ __global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs
     const int b = blockIdx.x, tid = threadIdx.x;
     const int tile_base = b * kLayoutTile;
     const int ER = a.E + a.R;
+    int ek[EPX_MAX_TOPK];
     if (a.ntiles > 0)
-        build_tile(a, tile_base, s, false);
+        build_tile(a, tile_base, s, false, ek);
 
-    // counts before this tile and over all tiles, per expert then per rank
+    // counts before this tile and over all tiles, per expert then per rank;
+    // 16 independent loads in flight per thread
     for (int i = tid; i < ER; i += blockDim.x) {
         int p = 0, q = 0;
-        for (int j = 0; j < a.ntiles; ++j) {
-            const int v = a.tile_cnt[(int64_t)j * ER + i];
-            p += (j < b) ? v : 0;
-            q += v;
+        for (int j0 = 0; j0 < a.ntiles; j0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)  // clamped rows, masked below
+                v[u] = a.tile_cnt[(int64_t)min(j0 + u, a.ntiles - 1) * ER + i];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int c = (j0 + u < a.ntiles) ? v[u] : 0;
+                p += (j0 + u < b) ? c : 0;
+                q += c;
+            }
         }
         s.pre[i] = p;
         s.tot[i] = q;
@@ -226,39 +299,70 @@ __global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs
         return;
 
     const int ntok = min(kLayoutTile, a.T - tile_base);
-    // pos_in_rank rows of the tile are contiguous: write them flat
-    int32_t *pir = a.pos_in_rank + (int64_t)tile_base * a.R;
-    for (int i = tid; i < ntok * a.R; i += blockDim.x) {
-        const int tt = i / a.R, r = i - tt * a.R;
-        int v = -1;
-        if ((s.tok_rbits[tt] >> r) & 1ull) {
-            const int w = tt >> 6, l = tt & 63;
-            v = s.pre[a.E + r] + __popcll(s.rmask[w * a.R + r] & lanes_below(l));
-            for (int w2 = 0; w2 < w; ++w2)
-                v += __popcll(s.rmask[w2 * a.R + r]);
+    const int tt = tid, t = tile_base + tid;
+    if (t < a.T) {
+        const int w = tt >> 6;
+        const uint64_t below = lanes_below(tt & 63);
+        const uint64_t rbits = s.tok_rbits[tt];
+        // pos_in_rank row: tokens before t in each rank it goes to, else -1
+        int32_t *pir = a.pos_in_rank + (int64_t)t * a.R;
+        for (int r0 = 0; r0 < a.R; r0 += 4) {
+            int v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = r0 + j;
+                v[j] = -1;
+                if (r < a.R && ((rbits >> r) & 1ull)) {
+                    int p = s.pre[a.E + r] + __popcll(s.rmask[w * a.R + r] & below);
+                    for (int w2 = 0; w2 < w; ++w2)
+                        p += __popcll(s.rmask[w2 * a.R + r]);
+                    v[j] = p;
+                }
+            }
+            if ((a.R & 3) == 0) {
+                *reinterpret_cast<u32x4 *>(pir + r0) =
+                    u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (r0 + j < a.R)
+                        pir[r0 + j] = v[j];
+            }
         }
-        pir[i] = v;
-    }
-    int32_t *sie = a.slot_in_expert + (int64_t)tile_base * a.K;
-    const int64_t *tk = a.topk_idx + (int64_t)tile_base * a.K;
-    for (int i = tid; i < ntok * a.K; i += blockDim.x) {
-        const int tt = i / a.K, k = i - tt * a.K;
-        const int64_t e = tk[i];
-        int v = -1;
-        if (e >= 0 && e < a.E) {
-            const int w = tt >> 6;
-            v = s.pre[e] + wave_rank(a, s, tile_base, tt, k, e);
-            for (int w2 = 0; w2 < w; ++w2)
-                v += s.ecnt[w2 * a.E + e];
+        // slot_in_expert row: entries before (t,k) routed to the same expert
+        int32_t *sie = a.slot_in_expert + (int64_t)t * a.K;
+        int v[EPX_MAX_TOPK];
+#pragma unroll
+        for (int k = 0; k < EPX_MAX_TOPK; ++k) {
+            v[k] = -1;
+            const int e = ek[k];
+            if (k < a.K && e >= 0) {
+                int p = s.pre[e] + wave_rank(a, s, tile_base, tt, k, e);
+                for (int w2 = 0; w2 < w; ++w2)
+                    p += s.ecnt[w2 * a.E + e];
+                v[k] = p;
+            }
         }
-        sie[i] = v;
+        if ((a.K & 3) == 0) {
+#pragma unroll
+            for (int k0 = 0; k0 < EPX_MAX_TOPK; k0 += 4)
+                if (k0 < a.K)
+                    *reinterpret_cast<u32x4 *>(sie + k0) = u32x4{
+                        (uint32_t)v[k0], (uint32_t)v[k0 + 1], (uint32_t)v[k0 + 2], (uint32_t)v[k0 + 3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPX_MAX_TOPK; ++k)
+                if (k < a.K)
+                    sie[k] = v[k];
+        }
     }
     // channel c ends at min((c+1)*ceil(T/C), T); the tile holding token end-1
     // writes the channel's column
     if (a.channel_prefix) {
         const int64_t span = ((int64_t)a.T + a.C - 1) / a.C;
-        for (int i = tid; i < a.R * a.C; i += blockDim.x) {
-            const int r = i / a.C, c = i - r * a.C;
+        Walk it(tid, blockDim.x, a.C);
+        for (int i = tid; i < a.R * a.C; i += blockDim.x, it.next()) {
+            const int r = it.row, c = it.col;
             const int64_t end = min((int64_t)(c + 1) * span, (int64_t)a.T);
             if (end <= tile_base || end > tile_base + ntok)
                 continue;

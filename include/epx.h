@@ -19,8 +19,9 @@
  *     allocates device memory (epx_create allocates one 4-byte error word).
  *   - bf16 data is passed as uint16 bit patterns; FP8 data as uint8 codes in
  *     OCP E4M3FN (max 448, no infinities).
- *   - Hidden-state buffers (x, send_x, recv_x, ll_x, expert_out, out) must be
- *     16-byte aligned; h must be a multiple of 8 (of 128 with FP8).
+ *   - Hidden-state buffers (x, send_x, recv_x, ll_x, expert_out, out) and the
+ *     per-token layout tables (is_token_in_rank, pos_in_rank, slot_in_expert)
+ *     must be 16-byte aligned; h must be a multiple of 8 (of 128 with FP8).
  *   - Every call only enqueues work on `stream` and returns; none waits for
  *     the GPU, except epx_get_error. Work is ordered by the stream alone.
  *   - Host-detectable errors are returned at once and nothing is launched.

@@ -351,6 +351,8 @@ def test_error_paths():
             v.view(torch.uint8).fill_(CANARY)
     view = dict(buf)
     for k in list(view):
+        if view[k] is None:
+            continue
         if k.startswith("send"):
             view[k] = buf[k][:n_send - 1]
         elif k.startswith("recv"):
