@@ -10,16 +10,18 @@
 //   count    one block per tile of 256 tokens (4 waves, one token per lane).
 //            Each wave ORs its lanes into LDS bitmaps: emask[w][e] has bit l
 //            set when token l of wave w routes an entry to expert e, rmask
-//            likewise per rank (OR deduplicates ranks for free). Tile counts
-//            go to the workspace [tile, E + R]; is_token_in_rank is written.
-//   finalize one block per tile again. Each block sums the counts of the
-//            tiles before it (a few KB from L2), scans the totals into
-//            exp_off / rank_off in LDS, rebuilds its bitmaps and writes the
-//            final positions: rank(t) = tile prefix + earlier waves' counts +
-//            popcount(mask & lanes below t). Block 0 writes the counts,
-//            offsets and totals.
-// A wave in which some token lists one expert twice falls back to counting
-// earlier entries directly, so ranks stay "entries before (t,k)" exactly.
+//            likewise per rank (the OR deduplicates ranks for free). A
+//            token's rank inside the tile is then the earlier waves' count
+//            plus popcount(mask & lanes below it). The block writes
+//            is_token_in_rank and these tile-local ranks straight into
+//            pos_in_rank / slot_in_expert / channel_prefix, and the tile's
+//            counts into the workspace [tile, E + R].
+//   finalize one block per tile again: sums the counts of the tiles before
+//            it (a few KB from L2), scans all tiles' totals into exp_off /
+//            rank_off in LDS and adds the tile's prefix to the tile-local
+//            ranks. Block 0 writes the counts, offsets and totals.
+// A wave in which some token lists one expert twice counts earlier entries
+// directly instead, so a slot stays "entries before (t,k)" exactly.
 #include "epx_device.h"
 #include "epx_internal.h"
 
@@ -28,45 +30,41 @@ namespace {
 
 constexpr int W = kLayoutWaves;
 
-struct TileLds {
-    uint64_t *emask;      // [W][E]
-    uint64_t *rmask;      // [W][R]
-    uint64_t *tok_rbits;  // [tile] rank bits per token
-    int *ecnt;            // [W][E] entries per expert in the wave
-    int *dupwave;         // [W] 1 if the wave has a row with a repeated expert
-    int *pre;             // [E+R] counts in earlier tiles (finalize only)
-    int *tot;             // [E+R] counts over all tiles (finalize only)
-    int *off;             // [E+1 + R+1] exclusive offsets (finalize only)
+struct CountLds {
+    uint64_t *emask;  // [W][E]
+    uint64_t *rmask;  // [W][R]
+    int *ecnt;        // [W][E] entries of wave w routed to e
+    int *wpre_e;      // [W][E] entries of the tile's earlier waves routed to e
+    int *wpre_r;      // [W][R] tokens of the tile's earlier waves going to r
+    int *dupwave;     // [W] 1 if the wave has a row with a repeated expert
 };
 
-__host__ __device__ inline size_t tile_lds_bytes(int E, int R)
+__host__ __device__ inline size_t count_lds_bytes(int E, int R)
 {
-    return sizeof(uint64_t) * ((size_t)W * E + (size_t)W * R + kLayoutTile) +
-           sizeof(int) * ((size_t)W * E + W);
+    return sizeof(uint64_t) * ((size_t)W * E + (size_t)W * R) +
+           sizeof(int) * (2 * (size_t)W * E + (size_t)W * R + W);
+}
+
+__device__ CountLds carve_count(char *base, int E, int R)
+{
+    CountLds s;
+    s.emask = reinterpret_cast<uint64_t *>(base);
+    s.rmask = s.emask + (size_t)W * E;
+    s.ecnt = reinterpret_cast<int *>(s.rmask + (size_t)W * R);
+    s.wpre_e = s.ecnt + (size_t)W * E;
+    s.wpre_r = s.wpre_e + (size_t)W * E;
+    s.dupwave = s.wpre_r + (size_t)W * R;
+    return s;
 }
 
 __host__ __device__ inline size_t finalize_lds_bytes(int E, int R)
 {
-    return tile_lds_bytes(E, R) + sizeof(int) * (2 * (size_t)(E + R) + (E + R + 2));
+    return sizeof(int) * (2 * (size_t)(E + R) + (E + R + 2));  // pre, tot, off
 }
 
-__device__ TileLds carve(char *base, int E, int R)
-{
-    TileLds s;
-    s.emask = reinterpret_cast<uint64_t *>(base);
-    s.rmask = s.emask + (size_t)W * E;
-    s.tok_rbits = s.rmask + (size_t)W * R;
-    s.ecnt = reinterpret_cast<int *>(s.tok_rbits + kLayoutTile);
-    s.dupwave = s.ecnt + (size_t)W * E;
-    s.pre = s.dupwave + W;
-    s.tot = s.pre + (E + R);
-    s.off = s.tot + (E + R);
-    return s;
-}
-
-// Flat index walker over a [rows, cols] block of a row-major array: thread
-// tid starts at element tid and advances by blockDim, tracking (row, col)
-// with one division up front instead of one per element.
+// Flat index walker over a [rows, cols] row-major block: thread tid starts
+// at element tid and steps by blockDim, tracking (row, col) with one
+// division up front instead of one per element.
 struct Walk {
     int row, col, drow, dcol, cols;
     __device__ Walk(int tid, int step, int ncols)
@@ -88,21 +86,15 @@ struct Walk {
     }
 };
 
-// Build the bitmaps and per-wave expert counts of one tile. Every thread of
-// the block must call this (it holds barriers). The token's K entries are
-// loaded first, so their latency overlaps the LDS clear; they are returned
-// in ek (expert id, -1 = no route, -2 = out of range).
-__device__ void build_tile(const LayoutArgs &a, int tile_base, const TileLds &s, bool report,
-                           int (&ek)[EPX_MAX_TOPK])
+// Load a token's K expert ids into ek (-1 = no route or k >= K, -2 = out of
+// range). Loads go out 8 at a time from clamped, always-valid addresses and
+// are masked afterwards, so they are in flight together. Needs T >= 1.
+template <int KMAX>
+__device__ __forceinline__ void load_row_experts(const LayoutArgs &a, int t, int (&ek)[KMAX])
 {
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int t = tile_base + tid;
-    // Loads go out 8 at a time from clamped (always valid) addresses and are
-    // masked afterwards, so they are in flight together rather than one
-    // branch and one wait each. A tile exists only when T >= 1.
     const int64_t *row = a.topk_idx + (int64_t)min(t, a.T - 1) * a.K;
 #pragma unroll
-    for (int k0 = 0; k0 < EPX_MAX_TOPK; k0 += 8) {
+    for (int k0 = 0; k0 < KMAX; k0 += 8) {
         if (k0 < a.K) {
             int64_t v[8];
 #pragma unroll
@@ -121,75 +113,30 @@ __device__ void build_tile(const LayoutArgs &a, int tile_base, const TileLds &s,
                 ek[k0 + j] = -1;
         }
     }
-    for (int i = tid; i < W * a.E; i += blockDim.x) {
-        s.emask[i] = 0;
-        s.ecnt[i] = 0;
-    }
-    for (int i = tid; i < W * a.R; i += blockDim.x)
-        s.rmask[i] = 0;
-    if (tid < W)
-        s.dupwave[tid] = 0;
-    __syncthreads();
-
-    const uint64_t bit = 1ull << lane;
-    uint64_t rbits = 0;
-    int dup = 0, bad = 0;
-#pragma unroll
-    for (int k = 0; k < EPX_MAX_TOPK; ++k) {
-        const int e = ek[k];
-        bad |= (e == -2);
-        if (e < 0)
-            continue;
-        const uint64_t old =
-            atomicOr(reinterpret_cast<unsigned long long *>(&s.emask[w * a.E + e]), bit);
-        dup |= (old & bit) != 0;
-        atomicAdd(&s.ecnt[w * a.E + e], 1);
-        rbits |= 1ull << (e / a.L);
-    }
-    if (report && bad)
-        flag_error(a.err, EPX_DEV_BAD_ROUTE);
-    s.tok_rbits[tid] = rbits;
-    for (uint64_t m = rbits; m; m &= m - 1) {
-        const int r = __builtin_ctzll(m);
-        atomicOr(reinterpret_cast<unsigned long long *>(&s.rmask[w * a.R + r]), bit);
-    }
-    if (__any(dup) && lane == 0)
-        s.dupwave[w] = 1;
-    __syncthreads();
 }
 
-// Entries before (tile token tt, slot k) inside tt's wave that route to e.
-__device__ int wave_rank(const LayoutArgs &a, const TileLds &s, int tile_base, int tt, int k,
-                         int64_t e)
+// Entries before (tile token tt, slot k) inside tt's wave that route to e,
+// counted one by one: the path for a wave in which some row repeats an
+// expert (kept out of line so the common path stays small).
+__device__ __noinline__ int wave_rank_slow(const LayoutArgs &a, int tile_base, int tt, int k,
+                                           int e)
 {
-    const int w = tt >> 6, l = tt & 63;
-    if (!s.dupwave[w])
-        return __popcll(s.emask[w * a.E + e] & lanes_below(l));
-    const int64_t *base = a.topk_idx + (int64_t)(tile_base + (w << 6)) * a.K;
-    const int upto = l * a.K + k;
+    const int64_t *base = a.topk_idx + (int64_t)(tile_base + (tt & ~63)) * a.K;
+    const int upto = (tt & 63) * a.K + k;
     int n = 0;
     for (int i = 0; i < upto; ++i)
         n += (base[i] == e);
     return n;
 }
 
-// Exclusive scan of in[0..n) into out[0..n] by one wave.
-__device__ void wave_exclusive_scan(const int *in, int n, int *out)
+// Entries before (tile token tt, slot k) inside tt's wave that route to e.
+__device__ __forceinline__ int wave_rank(const LayoutArgs &a, const CountLds &s, int tile_base,
+                                         int tt, int k, int e)
 {
-    const int lane = lane_id();
-    const int per = (n + kWave - 1) / kWave;
-    const int lo = min(n, lane * per), hi = min(n, lo + per);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i)
-        sum += in[i];
-    const int incl = wave_inclusive_sum(sum);
-    int run = incl - sum;
-    for (int i = lo; i < hi; ++i) {
-        out[i] = run;
-        run += in[i];
-    }
-    if (lane == kWave - 1)
-        out[n] = incl;
+    const int w = tt >> 6;
+    if (!s.dupwave[w])
+        return __popcll(s.emask[w * a.E + e] & lanes_below(tt & 63));
+    return wave_rank_slow(a, tile_base, tt, k, e);
 }
 
 // Row of R bytes (0/1) for one token; 16-byte stores when R allows it.
@@ -211,51 +158,189 @@ __device__ void write_rank_row(uint8_t *dst, uint64_t rbits, int R)
     }
 }
 
+// Exclusive scan of in[0..n) into out[0..n] by one wave.
+__device__ void wave_exclusive_scan(const int *in, int n, int *out)
+{
+    const int lane = lane_id();
+    const int per = (n + kWave - 1) / kWave;
+    const int lo = min(n, lane * per), hi = min(n, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i)
+        sum += in[i];
+    const int incl = wave_inclusive_sum(sum);
+    int run = incl - sum;
+    for (int i = lo; i < hi; ++i) {
+        out[i] = run;
+        run += in[i];
+    }
+    if (lane == kWave - 1)
+        out[n] = incl;
+}
+
+// Channel c covers tokens [c*ceil(T/C), min((c+1)*ceil(T/C), T)); the tile
+// holding its last token owns column c of channel_prefix.
+__device__ __forceinline__ int64_t channel_end(const LayoutArgs &a, int c)
+{
+    const int64_t span = ((int64_t)a.T + a.C - 1) / a.C;
+    return min((int64_t)(c + 1) * span, (int64_t)a.T);
+}
+
+template <int KMAX>
 __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(LayoutArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const TileLds s = carve(lds, a.E, a.R);
+    const CountLds s = carve_count(lds, a.E, a.R);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int tile_base = blockIdx.x * kLayoutTile;
-    int ek[EPX_MAX_TOPK];
-    build_tile(a, tile_base, s, true, ek);
+    const int ntok = min(kLayoutTile, a.T - tile_base);
+    const int t = tile_base + tid;
 
-    const int t = tile_base + (int)threadIdx.x;
-    if (t < a.T)
-        write_rank_row(a.is_token_in_rank + (int64_t)t * a.R, s.tok_rbits[threadIdx.x], a.R);
-    int32_t *cnt = a.tile_cnt + (int64_t)blockIdx.x * (a.E + a.R);
-    for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
-        int c = 0;
-        for (int w = 0; w < W; ++w)
-            c += s.ecnt[w * a.E + e];
-        cnt[e] = c;
+    int ek[KMAX];
+    load_row_experts<KMAX>(a, t, ek);
+    for (int i = tid; i < W * a.E; i += blockDim.x) {
+        s.emask[i] = 0;
+        s.ecnt[i] = 0;
     }
-    for (int r = threadIdx.x; r < a.R; r += blockDim.x) {
-        int c = 0;
-        for (int w = 0; w < W; ++w)
-            c += __popcll(s.rmask[w * a.R + r]);
-        cnt[a.E + r] = c;
+    for (int i = tid; i < W * a.R; i += blockDim.x)
+        s.rmask[i] = 0;
+    if (tid < W)
+        s.dupwave[tid] = 0;
+    __syncthreads();
+
+    const uint64_t bit = 1ull << lane;
+    uint64_t rbits = 0;
+    int dup = 0, bad = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int e = ek[k];
+        bad |= (e == -2);
+        if (e < 0)
+            continue;
+        const uint64_t old =
+            atomicOr(reinterpret_cast<unsigned long long *>(&s.emask[w * a.E + e]), bit);
+        dup |= (old & bit) != 0;
+        atomicAdd(&s.ecnt[w * a.E + e], 1);
+        rbits |= 1ull << (e / a.L);
+    }
+    if (bad)
+        flag_error(a.err, EPX_DEV_BAD_ROUTE);
+    for (uint64_t m = rbits; m; m &= m - 1) {
+        const int r = __builtin_ctzll(m);
+        atomicOr(reinterpret_cast<unsigned long long *>(&s.rmask[w * a.R + r]), bit);
+    }
+    if (__any(dup) && lane == 0)
+        s.dupwave[w] = 1;
+    __syncthreads();
+
+    // wave prefixes inside the tile, and the tile's counts
+    int32_t *cnt = a.tile_cnt + (int64_t)blockIdx.x * (a.E + a.R);
+    for (int e = tid; e < a.E; e += blockDim.x) {
+        int run = 0;
+        for (int w2 = 0; w2 < W; ++w2) {
+            s.wpre_e[w2 * a.E + e] = run;
+            run += s.ecnt[w2 * a.E + e];
+        }
+        cnt[e] = run;
+    }
+    for (int r = tid; r < a.R; r += blockDim.x) {
+        int run = 0;
+        for (int w2 = 0; w2 < W; ++w2) {
+            s.wpre_r[w2 * a.R + r] = run;
+            run += __popcll(s.rmask[w2 * a.R + r]);
+        }
+        cnt[a.E + r] = run;
+    }
+    __syncthreads();
+
+    if (t < a.T) {
+        const uint64_t below = lanes_below(lane);
+        write_rank_row(a.is_token_in_rank + (int64_t)t * a.R, rbits, a.R);
+        // tile-local rank of t in each rank it goes to, else -1: the row is
+        // cleared first, then only the (at most K) ranks t goes to are set
+        int32_t *pir = a.pos_in_rank + (int64_t)t * a.R;
+        if ((a.R & 3) == 0) {
+            for (int r0 = 0; r0 < a.R; r0 += 4)
+                *reinterpret_cast<u32x4 *>(pir + r0) = u32x4{~0u, ~0u, ~0u, ~0u};
+        } else {
+            for (int r = 0; r < a.R; ++r)
+                pir[r] = -1;
+        }
+        uint64_t m = rbits;
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+            if (m) {
+                const int r = __builtin_ctzll(m);
+                m &= m - 1;
+                pir[r] = s.wpre_r[w * a.R + r] + __popcll(s.rmask[w * a.R + r] & below);
+            }
+        }
+        // tile-local slot of each entry, else -1
+        int32_t *sie = a.slot_in_expert + (int64_t)t * a.K;
+        int v[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int e = ek[k];
+            v[k] = e >= 0 ? s.wpre_e[w * a.E + e] + wave_rank(a, s, tile_base, tid, k, e) : -1;
+        }
+        if ((a.K & 3) == 0) {
+#pragma unroll
+            for (int k0 = 0; k0 < KMAX; k0 += 4)
+                if (k0 < a.K)
+                    *reinterpret_cast<u32x4 *>(sie + k0) = u32x4{
+                        (uint32_t)v[k0], (uint32_t)v[k0 + 1], (uint32_t)v[k0 + 2], (uint32_t)v[k0 + 3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (k < a.K)
+                    sie[k] = v[k];
+        }
+    }
+
+    // tile-local part of the channel columns this tile owns
+    if (a.channel_prefix) {
+        Walk it(tid, blockDim.x, a.C);
+        for (int i = tid; i < a.R * a.C; i += blockDim.x, it.next()) {
+            const int r = it.row;
+            const int64_t end = channel_end(a, it.col);
+            if (end <= tile_base || end > tile_base + ntok)
+                continue;
+            const int n = (int)(end - tile_base);
+            int v = 0;
+            for (int w2 = 0; w2 < W; ++w2) {
+                const int lo = w2 * kWave;
+                if (n <= lo)
+                    break;
+                const uint64_t m = (n >= lo + kWave) ? ~0ull : lanes_below(n - lo);
+                v += __popcll(s.rmask[w2 * a.R + r] & m);
+            }
+            a.channel_prefix[i] = v;
+        }
     }
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    const TileLds s = carve(lds, a.E, a.R);
+    extern __shared__ __attribute__((aligned(16))) int fin[];
     const int b = blockIdx.x, tid = threadIdx.x;
-    const int tile_base = b * kLayoutTile;
     const int ER = a.E + a.R;
-    int ek[EPX_MAX_TOPK];
-    if (a.ntiles > 0)
-        build_tile(a, tile_base, s, false, ek);
+    int *pre = fin, *tot = fin + ER, *off = fin + 2 * ER;
+    const int tile_base = b * kLayoutTile;
+    const int t = tile_base + tid;
 
-    // counts before this tile and over all tiles, per expert then per rank;
-    // 16 independent loads in flight per thread
+    // this token's experts (for the slot fix-up) go out first
+    int ek[KMAX];
+    if (a.ntiles > 0)
+        load_row_experts<KMAX>(a, t, ek);
+
+    // counts in earlier tiles and over all tiles, per expert then per rank;
+    // 16 loads in flight per thread, from clamped rows masked afterwards
     for (int i = tid; i < ER; i += blockDim.x) {
         int p = 0, q = 0;
         for (int j0 = 0; j0 < a.ntiles; j0 += 16) {
             int v[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)  // clamped rows, masked below
+            for (int u = 0; u < 16; ++u)
                 v[u] = a.tile_cnt[(int64_t)min(j0 + u, a.ntiles - 1) * ER + i];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
@@ -264,31 +349,31 @@ __global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs
                 q += c;
             }
         }
-        s.pre[i] = p;
-        s.tot[i] = q;
+        pre[i] = p;
+        tot[i] = q;
     }
     __syncthreads();
     if (tid < kWave)
-        wave_exclusive_scan(s.tot, a.E, s.off);
+        wave_exclusive_scan(tot, a.E, off);
     else if (tid < 2 * kWave)
-        wave_exclusive_scan(s.tot + a.E, a.R, s.off + a.E + 1);
+        wave_exclusive_scan(tot + a.E, a.R, off + a.E + 1);
     __syncthreads();
 
     if (b == 0) {
         for (int e = tid; e < a.E; e += blockDim.x)
-            a.num_tokens_per_expert[e] = s.tot[e];
+            a.num_tokens_per_expert[e] = tot[e];
         for (int r = tid; r < a.R; r += blockDim.x)
-            a.num_tokens_per_rank[r] = s.tot[a.E + r];
+            a.num_tokens_per_rank[r] = tot[a.E + r];
         for (int i = tid; i <= a.E; i += blockDim.x)
-            a.exp_off[i] = s.off[i];
+            a.exp_off[i] = off[i];
         for (int i = tid; i <= a.R; i += blockDim.x)
-            a.rank_off[i] = s.off[a.E + 1 + i];
+            a.rank_off[i] = off[a.E + 1 + i];
         if (tid == 0) {
-            a.totals[0] = s.off[a.E + 1 + a.R];
-            a.totals[1] = s.off[a.E];
+            a.totals[0] = off[a.E + 1 + a.R];
+            a.totals[1] = off[a.E];
             if (a.totals_host_mapped) {
-                a.totals_host_mapped[0] = s.off[a.E + 1 + a.R];
-                a.totals_host_mapped[1] = s.off[a.E];
+                a.totals_host_mapped[0] = off[a.E + 1 + a.R];
+                a.totals_host_mapped[1] = off[a.E];
             }
         }
         if (a.ntiles == 0 && a.channel_prefix)
@@ -298,84 +383,44 @@ __global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs
     if (a.ntiles == 0)
         return;
 
+    // add the tile prefix to the tile-local ranks: only the (at most K)
+    // ranks and the K entries of the token change
     const int ntok = min(kLayoutTile, a.T - tile_base);
-    const int tt = tid, t = tile_base + tid;
     if (t < a.T) {
-        const int w = tt >> 6;
-        const uint64_t below = lanes_below(tt & 63);
-        const uint64_t rbits = s.tok_rbits[tt];
-        // pos_in_rank row: tokens before t in each rank it goes to, else -1
+        uint64_t rbits = 0;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (ek[k] >= 0)
+                rbits |= 1ull << (ek[k] / a.L);
         int32_t *pir = a.pos_in_rank + (int64_t)t * a.R;
-        for (int r0 = 0; r0 < a.R; r0 += 4) {
-            int v[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = r0 + j;
-                v[j] = -1;
-                if (r < a.R && ((rbits >> r) & 1ull)) {
-                    int p = s.pre[a.E + r] + __popcll(s.rmask[w * a.R + r] & below);
-                    for (int w2 = 0; w2 < w; ++w2)
-                        p += __popcll(s.rmask[w2 * a.R + r]);
-                    v[j] = p;
-                }
-            }
-            if ((a.R & 3) == 0) {
-                *reinterpret_cast<u32x4 *>(pir + r0) =
-                    u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (r0 + j < a.R)
-                        pir[r0 + j] = v[j];
-            }
-        }
-        // slot_in_expert row: entries before (t,k) routed to the same expert
         int32_t *sie = a.slot_in_expert + (int64_t)t * a.K;
-        int v[EPX_MAX_TOPK];
+        int rr[KMAX], vr[KMAX], vs[KMAX];
+        uint64_t m = rbits;
 #pragma unroll
-        for (int k = 0; k < EPX_MAX_TOPK; ++k) {
-            v[k] = -1;
-            const int e = ek[k];
-            if (k < a.K && e >= 0) {
-                int p = s.pre[e] + wave_rank(a, s, tile_base, tt, k, e);
-                for (int w2 = 0; w2 < w; ++w2)
-                    p += s.ecnt[w2 * a.E + e];
-                v[k] = p;
+        for (int i = 0; i < KMAX; ++i) {
+            rr[i] = -1;
+            if (m) {
+                rr[i] = __builtin_ctzll(m);
+                m &= m - 1;
+                vr[i] = pir[rr[i]];
             }
+            if (i < a.K && ek[i] >= 0)
+                vs[i] = sie[i];
         }
-        if ((a.K & 3) == 0) {
 #pragma unroll
-            for (int k0 = 0; k0 < EPX_MAX_TOPK; k0 += 4)
-                if (k0 < a.K)
-                    *reinterpret_cast<u32x4 *>(sie + k0) = u32x4{
-                        (uint32_t)v[k0], (uint32_t)v[k0 + 1], (uint32_t)v[k0 + 2], (uint32_t)v[k0 + 3]};
-        } else {
-#pragma unroll
-            for (int k = 0; k < EPX_MAX_TOPK; ++k)
-                if (k < a.K)
-                    sie[k] = v[k];
+        for (int i = 0; i < KMAX; ++i) {
+            if (rr[i] >= 0)
+                pir[rr[i]] = vr[i] + pre[a.E + rr[i]];
+            if (i < a.K && ek[i] >= 0)
+                sie[i] = vs[i] + pre[ek[i]];
         }
     }
-    // channel c ends at min((c+1)*ceil(T/C), T); the tile holding token end-1
-    // writes the channel's column
     if (a.channel_prefix) {
-        const int64_t span = ((int64_t)a.T + a.C - 1) / a.C;
         Walk it(tid, blockDim.x, a.C);
         for (int i = tid; i < a.R * a.C; i += blockDim.x, it.next()) {
-            const int r = it.row, c = it.col;
-            const int64_t end = min((int64_t)(c + 1) * span, (int64_t)a.T);
-            if (end <= tile_base || end > tile_base + ntok)
-                continue;
-            const int n = (int)(end - tile_base);
-            int v = s.pre[a.E + r];
-            for (int w = 0; w < W; ++w) {
-                const int lo = w * kWave;
-                if (n <= lo)
-                    break;
-                const uint64_t m = (n >= lo + kWave) ? ~0ull : lanes_below(n - lo);
-                v += __popcll(s.rmask[w * a.R + r] & m);
-            }
-            a.channel_prefix[i] = v;
+            const int64_t end = channel_end(a, it.col);
+            if (end > tile_base && end <= tile_base + ntok)
+                a.channel_prefix[i] += pre[a.E + it.row];
         }
     }
 }
@@ -388,13 +433,24 @@ size_t layout_workspace_bytes(int T, int E, int R)
     return ntiles * (size_t)(E + R) * sizeof(int32_t);
 }
 
-hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream)
+template <int KMAX>
+static void launch_layout_k(const LayoutArgs &a, hipStream_t stream)
 {
     if (a.ntiles > 0)
-        hipLaunchKernelGGL(layout_count_kernel, dim3(a.ntiles), dim3(kLayoutTile),
-                           tile_lds_bytes(a.E, a.R), stream, a);
-    hipLaunchKernelGGL(layout_finalize_kernel, dim3(a.ntiles > 0 ? a.ntiles : 1),
+        hipLaunchKernelGGL((layout_count_kernel<KMAX>), dim3(a.ntiles), dim3(kLayoutTile),
+                           count_lds_bytes(a.E, a.R), stream, a);
+    hipLaunchKernelGGL((layout_finalize_kernel<KMAX>), dim3(a.ntiles > 0 ? a.ntiles : 1),
                        dim3(kLayoutTile), finalize_lds_bytes(a.E, a.R), stream, a);
+}
+
+// The per-token top-k loops are unrolled to KMAX; the common K <= 8 gets a
+// small kernel (instruction fetch matters for these short, few-block kernels).
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream)
+{
+    if (a.K <= 8)
+        launch_layout_k<8>(a, stream);
+    else
+        launch_layout_k<EPX_MAX_TOPK>(a, stream);
     return hipGetLastError();
 }
 
