@@ -60,7 +60,7 @@ struct RowBf16 {
         for (int u = 0; u < NV; ++u) {
             const int v = v0 + u * kWave + lane_id();
             if (v < nvec)
-                store16_stream(dst_row + (size_t)v * 16, r[u]);
+                store16_wt(dst_row + (size_t)v * 16, r[u]);
         }
     }
 };
@@ -118,7 +118,7 @@ struct RowFp8 {
         for (int u = 0; u < NV; ++u) {
             const int sg = s0 + u * kWave + lane_id();
             if (sg < nseg) {
-                store16_stream(q_row + (size_t)sg * 16, q[u]);
+                store16_wt(q_row + (size_t)sg * 16, q[u]);
                 if ((sg & 7) == 0)
                     s_row[sg >> 3] = sc[u];
             }

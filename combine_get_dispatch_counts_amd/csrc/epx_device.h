@@ -84,6 +84,17 @@ __device__ __forceinline__ void store16_stream(void *p, u32x4 v)
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 
+// 16-byte vector store with the sc1 cache-policy bit (device-coherent
+// write-through), which measured ~4% faster than the nontemporal policy for
+// the scattered whole-row writes of dispatch (the combine's interleaved
+// reads and writes prefer nontemporal). A vector-memory store: nothing in
+// the kernel reads the data back, and the kernel's end makes it visible to
+// later work.
+__device__ __forceinline__ void store16_wt(void *p, u32x4 v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+
 // Inclusive sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_inclusive_sum(int v)
 {

@@ -328,10 +328,28 @@ __global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs
     const int tile_base = b * kLayoutTile;
     const int t = tile_base + tid;
 
-    // this token's experts (for the slot fix-up) go out first
+    // this token's experts and its tile-local rows go out first: nothing
+    // below the scan has to wait for memory except these loads
     int ek[KMAX];
     if (a.ntiles > 0)
         load_row_experts<KMAX>(a, t, ek);
+    const bool vec_rows = (a.R & 3) == 0;
+    const int tl = min(t, a.T - 1);  // clamped: loads stay inside the arrays
+    int32_t *pir = a.pos_in_rank + (int64_t)tl * a.R;
+    int32_t *sie = a.slot_in_expert + (int64_t)tl * a.K;
+    u32x4 prow[EPX_MAX_RANKS / 4];
+    int srow[KMAX];
+    if (a.ntiles > 0) {
+        if (vec_rows) {
+#pragma unroll
+            for (int j = 0; j < EPX_MAX_RANKS / 4; ++j)
+                if (4 * j < a.R)
+                    prow[j] = *reinterpret_cast<const u32x4 *>(pir + 4 * j);
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            srow[k] = (k < a.K) ? sie[k] : -1;
+    }
 
     // counts in earlier tiles and over all tiles, per expert then per rank;
     // 16 loads in flight per thread, from clamped rows masked afterwards
@@ -383,36 +401,46 @@ __global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs
     if (a.ntiles == 0)
         return;
 
-    // add the tile prefix to the tile-local ranks: only the (at most K)
-    // ranks and the K entries of the token change
+    // add the tile prefix to the tile-local ranks (already in registers)
     const int ntok = min(kLayoutTile, a.T - tile_base);
     if (t < a.T) {
-        uint64_t rbits = 0;
+        if (vec_rows) {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (ek[k] >= 0)
-                rbits |= 1ull << (ek[k] / a.L);
-        int32_t *pir = a.pos_in_rank + (int64_t)t * a.R;
-        int32_t *sie = a.slot_in_expert + (int64_t)t * a.K;
-        int rr[KMAX], vr[KMAX], vs[KMAX];
-        uint64_t m = rbits;
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-            rr[i] = -1;
-            if (m) {
-                rr[i] = __builtin_ctzll(m);
-                m &= m - 1;
-                vr[i] = pir[rr[i]];
+            for (int j = 0; j < EPX_MAX_RANKS / 4; ++j) {
+                const int r = 4 * j;
+                if (r < a.R) {
+                    u32x4 o = prow[j];
+                    o.x = (int)o.x >= 0 ? o.x + pre[a.E + r] : o.x;
+                    o.y = (int)o.y >= 0 ? o.y + pre[a.E + r + 1] : o.y;
+                    o.z = (int)o.z >= 0 ? o.z + pre[a.E + r + 2] : o.z;
+                    o.w = (int)o.w >= 0 ? o.w + pre[a.E + r + 3] : o.w;
+                    *reinterpret_cast<u32x4 *>(pir + r) = o;
+                }
             }
-            if (i < a.K && ek[i] >= 0)
-                vs[i] = sie[i];
+        } else {
+            for (int r = 0; r < a.R; ++r) {
+                const int v = pir[r];
+                if (v >= 0)
+                    pir[r] = v + pre[a.E + r];
+            }
         }
+        if ((a.K & 3) == 0) {
 #pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-            if (rr[i] >= 0)
-                pir[rr[i]] = vr[i] + pre[a.E + rr[i]];
-            if (i < a.K && ek[i] >= 0)
-                sie[i] = vs[i] + pre[ek[i]];
+            for (int k0 = 0; k0 < KMAX; k0 += 4) {
+                if (k0 < a.K) {
+                    int o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        o[j] = ek[k0 + j] >= 0 ? srow[k0 + j] + pre[ek[k0 + j]] : srow[k0 + j];
+                    *reinterpret_cast<u32x4 *>(sie + k0) =
+                        u32x4{(uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (k < a.K && ek[k] >= 0)
+                    sie[k] = srow[k] + pre[ek[k]];
         }
     }
     if (a.channel_prefix) {
