@@ -108,6 +108,130 @@ def cpu_baseline(inp, wl, target_s=12.0, max_reps=5):
     return med, n_rank, n_exp, len(times)
 
 
+def _loop_us(fn, n):
+    """Average microseconds per call of fn launched n times back to back on
+    the current stream (one event pair around all of them)."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+def other_workloads(n=20):
+    """The FP8 and low-latency rows on their own workloads: per-kernel time,
+    compulsory GB/s and fraction of the 8 TB/s HBM peak. Not the headline
+    figure (that is the prefill step above); reported beside it."""
+    import numpy as np
+    import torch
+
+    import combine_get_dispatch_counts_amd as epx
+    import synth
+
+    dev = torch.device("cuda", 0)
+    out = {}
+
+    def rec(us, nbytes):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us": round(us, 2), "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "bytes": int(nbytes)}
+
+    # large FP8 prefill: T=16384, h=7168, E=256, R=64, topk=8
+    inp = synth.make_inputs(5)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    tk = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    ws = torch.empty(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    lay = epx.alloc_layout(T, K, E, R, None, dev)
+    bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, True, dev)
+    epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay)
+    n_rank, n_exp = (int(v) for v in lay.totals.cpu())
+    y = synth.expert_outputs(T * K, h, seed=17, device="cuda")
+    comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    row8 = h + 4 * (h // 128)
+    lay_us = _loop_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay), n)
+    d_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs), n)
+    d = epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs)
+    c_us = _loop_us(lambda: epx.combine(y, d.pos_exp, w, out=comb), n)
+    assert epx.get_error() == 0
+    d_bytes = (T * 2 * h + 12 * T * K + (n_rank + n_exp) * row8 + 4 * (n_rank + n_exp)
+               + 12 * n_rank * K + 8 * T * K)
+    c_bytes = n_exp * 2 * h + 8 * T * K + T * 2 * h
+    out["fp8_prefill"] = {
+        "workload": f"T={T} h={h} E={E} R={R} topk={K}, FP8 e4m3 dispatch, bf16 combine",
+        "n_rank_rows": n_rank, "n_expert_rows": n_exp, "layout_us": round(lay_us, 2),
+        "dispatch_fp8": rec(d_us, d_bytes), "combine": rec(c_us, c_bytes),
+        "step_us": round(lay_us + d_us + c_us, 2)}
+    del x, tk, w, ws, lay, bufs, y, comb, d
+    torch.cuda.empty_cache()
+
+    # decode, low-latency: T=128, h=7168, E=256, R=32, topk=8, cap=128, FP8
+    inp = synth.make_inputs(2)
+    wl = inp["workload"]
+    T, h, E, R, K, cap = wl.T, wl.h, wl.E, wl.R, wl.K, wl.cap
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    tk = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    row8 = h + 4 * (h // 128)
+    for R_buf in (1, R):
+        buf = epx.alloc_ll(E, R_buf, cap, h, T, K, True, dev)
+        ll_us = _loop_us(lambda: epx.ll_dispatch(x, tk, E, R, 0, cap, R_buf, True, buf), n)
+        n_rows = T * K
+        ll_bytes = T * 2 * h + 8 * T * K + n_rows * (row8 + 4) + 4 * T * K + 4 * E
+        entry = {"ll_dispatch_fp8": rec(ll_us, ll_bytes)}
+        if R_buf == 1:
+            y = synth.expert_outputs(E * cap, h, seed=19, device="cuda")
+            comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+            c_us = _loop_us(lambda: epx.combine(y, buf.pos_ll, w, out=comb), n)
+            entry["combine"] = rec(c_us, n_rows * 2 * h + 8 * T * K + T * 2 * h)
+            entry["step_us"] = round(ll_us + c_us, 2)
+            del y, comb
+        assert epx.get_error() == 0
+        out[f"decode_ll_rbuf{R_buf}"] = dict(
+            workload=f"T={T} h={h} E={E} R={R} topk={K} cap={cap}, "
+                     + ("this source's slice" if R_buf == 1 else "all destinations' regions")
+                     + f" ({E * R_buf * cap} rows)", **entry)
+        del buf
+        torch.cuda.empty_cache()
+
+    # skewed routing, bf16: T=8192, h=4096, E=64, R=8, topk=6
+    inp = synth.make_inputs(4)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    tk = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    ws = torch.empty(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    lay = epx.alloc_layout(T, K, E, R, None, dev)
+    bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, False, dev)
+    epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay)
+    n_rank, n_exp = (int(v) for v in lay.totals.cpu())
+    y = synth.expert_outputs(T * K, h, seed=23, device="cuda")
+    comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    lay_us = _loop_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay), n)
+    d_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs), n)
+    d = epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs)
+    c_us = _loop_us(lambda: epx.combine(y, d.pos_exp, w, out=comb), n)
+    assert epx.get_error() == 0
+    by = step_bytes(T, h, K, R, n_rank, n_exp)
+    out["skew"] = {
+        "workload": f"T={T} h={h} E={E} R={R} topk={K}, Zipf-biased experts, bf16",
+        "n_rank_rows": n_rank, "n_expert_rows": n_exp,
+        "max_tokens_per_expert": int(lay.num_tokens_per_expert.max()),
+        "layout_us": round(lay_us, 2), "dispatch": rec(d_us, by["dispatch"]),
+        "combine": rec(c_us, by["combine"]), "step_us": round(lay_us + d_us + c_us, 2),
+        "step_gbs": round(survey_bmin(T, h, K, R, n_rank, n_exp) / ((lay_us + d_us + c_us) * 1e-6) / 1e9, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=1, help="also time the step replayed from a HIP graph")
+    ap.add_argument("--other", type=int, default=1,
+                    help="also time the FP8, low-latency and skewed workloads (reported beside the headline)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device copy of this many MB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--flush-mb", type=int, default=512,
@@ -249,6 +375,12 @@ def main():
     comb_gbs = by["combine"] / (phase["combine"] * 1e-6) / 1e9
     b_flow = bmin + n_rank * 2 * h
 
+    others = None
+    if args.other:
+        del bufs, expert_out, out, x
+        torch.cuda.empty_cache()
+        others = other_workloads()
+
     cpu = None
     if not args.no_cpu_baseline:
         med, nr, ne, reps = cpu_baseline(inp, wl)
@@ -288,6 +420,7 @@ def main():
                      "traffic": measured_traffic(), "kernel": "dispatch_kernel<bf16>",
                      "bytes_per_launch": by["dispatch"]},
         "cpu_baseline": cpu,
+        "other_workloads": others,
     }
     print(json.dumps(rec), flush=True)
 

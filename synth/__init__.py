@@ -26,7 +26,7 @@ expert permutation (4) or the outlier channels (5)):
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 import numpy as np
 
@@ -107,7 +107,8 @@ def make_inputs(cfg: int | Workload, T: int | None = None, seed: int | None = No
         cols = rng.choice(wl.h, size=n_out, replace=False)
         xf[:, cols] *= np.float32(50.0)
     topk_idx, topk_w = topk_softmax(logits, wl.K)
-    return dict(x=to_bf16_bits(xf), topk_idx=topk_idx, topk_w=topk_w, workload=wl)
+    return dict(x=to_bf16_bits(xf), topk_idx=topk_idx, topk_w=topk_w,
+                workload=replace(wl, T=T))
 
 
 def expert_outputs(n_rows: int, h: int, seed: int, device: str = "cpu"):

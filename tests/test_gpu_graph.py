@@ -1,0 +1,126 @@
+"""The hot path captured in a HIP graph: every replay, with unrelated eager
+work and outputs scribbled over between replays, must reproduce the eager
+results bit for bit (the layout and low-latency paths clear counts with fill
+kernels, never with memset nodes)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu import CANARY, dev_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _snapshot(tensors):
+    return [t.clone() for t in tensors if t is not None]
+
+
+def _scribble(tensors):
+    for t in tensors:
+        if t is not None:
+            t.view(torch.uint8).fill_(CANARY)
+
+
+def _same(a, b, what):
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"{what}: output {i} differs"
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_high_throughput_step_in_graph(fp8):
+    import combine_get_dispatch_counts_amd as epx
+
+    inp = synth.make_inputs(4, T=1024)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    say(f"graph HT step T={T} h={h} E={E} R={R} K={K} fp8={fp8}")
+    dev = torch.device("cuda")
+    x, tk, w = dev_bf16(inp["x"]), torch.from_numpy(inp["topk_idx"]).cuda(), \
+        torch.from_numpy(inp["topk_w"]).cuda()
+    ws = torch.zeros(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    lay = epx.alloc_layout(T, K, E, R, 16, dev)
+    bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, fp8, dev)
+    y = synth.expert_outputs(T * K, h, seed=3, device="cuda")
+    out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        epx.get_dispatch_layout(tk, E, R, 16, workspace=ws, out=lay)
+        d = epx.dispatch(x, tk, w, E, R, fp8=fp8, layout=lay, out=bufs)
+        epx.combine(y, d.pos_exp, w, out=out)
+
+    watched = [lay.num_tokens_per_expert, lay.num_tokens_per_rank, lay.is_token_in_rank,
+               lay.rank_off, lay.exp_off, lay.pos_in_rank, lay.slot_in_expert,
+               lay.channel_prefix, lay.totals, *bufs.values(), out]
+    _scribble(watched)  # rows past the totals are never written: keep them canary
+    step()
+    torch.cuda.synchronize()
+    ref = _snapshot(watched)
+    g = _capture(step)
+    other_x = dev_bf16(synth.make_inputs(4, T=1024, seed=77)["x"])
+    other_bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, fp8, dev)
+    for replay in range(3):
+        _scribble(watched)
+        # unrelated eager work between replays
+        epx.dispatch(other_x, tk, w, E, R, fp8=fp8, layout=epx.get_dispatch_layout(tk, E, R),
+                     out=other_bufs)
+        torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert epx.get_error() == 0
+        _same(_snapshot(watched), ref, f"replay {replay}")
+
+
+def test_low_latency_step_in_graph():
+    import combine_get_dispatch_counts_amd as epx
+
+    inp = synth.make_inputs(2, T=64)
+    wl = inp["workload"]
+    T, h, E, R, K, cap = wl.T, wl.h, wl.E, wl.R, wl.K, 64
+    say(f"graph LL step T={T} h={h} E={E} R={R} K={K} cap={cap}")
+    dev = torch.device("cuda")
+    x, tk, w = dev_bf16(inp["x"]), torch.from_numpy(inp["topk_idx"]).cuda(), \
+        torch.from_numpy(inp["topk_w"]).cuda()
+    buf = epx.alloc_ll(E, 1, cap, h, T, K, True, dev)
+    y = synth.expert_outputs(E * cap, h, seed=5, device="cuda")
+    out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    _scribble([buf.ll_x, buf.ll_scales, buf.ll_src])
+
+    def step():
+        epx.ll_reset(buf.ll_count)
+        epx.ll_dispatch(x, tk, E, R, 3, cap, 1, True, buf)
+        epx.combine(y, buf.pos_ll, w, out=out)
+
+    watched = [buf.ll_x, buf.ll_scales, buf.ll_src, buf.ll_count, buf.pos_ll, out]
+    step()
+    torch.cuda.synchronize()
+    ref = _snapshot(watched)
+    g = _capture(step)
+    for replay in range(3):
+        # counts set to a wrong value and pos scribbled; rows keep the canary
+        # they had before the first call, since the same rows are rewritten
+        buf.ll_count.fill_(7)
+        buf.pos_ll.fill_(-3)
+        out.zero_()
+        torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert epx.get_error() == 0
+        _same(_snapshot(watched), ref, f"replay {replay}")
+    assert np.all(buf.ll_count.cpu().numpy() >= 0)
