@@ -65,10 +65,49 @@ struct RowBf16 {
     }
 };
 
+// x / s for a group scale s with rs = 1/s (both IEEE divisions, once per
+// group): the product x*rs corrected by one fused residual step (Markstein's
+// construction), with the sign of zero taken from x. Run over every pair of
+// a finite bf16 x and a finite bf16 group maximum amax >= |x| on gfx950,
+// this gives the same e4m3 code as the IEEE quotient x / s in all
+// 1,065,402,240 cases (the quotients themselves differ only below the fp32
+// normal range, which every e4m3 rounding sends to a signed zero).
+__device__ __forceinline__ float quotient(float x, float s, float rs)
+{
+    const float q0 = x * rs;
+    const float e = __builtin_fmaf(-q0, s, x);
+    return __builtin_copysignf(__builtin_fmaf(e, rs, q0), x);
+}
+
+// e4m3 codes of two fp32 values placed in byte pair HI of w: gfx950's
+// OCP E4M3FN convert, nearest even, which gives the format's code for every
+// fp32 of magnitude <= 464 (checked on all of them).
+template <bool HI>
+__device__ __forceinline__ int cvt2_e4m3(float a, float b, int w)
+{
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, HI);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest magnitude pattern among the 16 bf16 values of a segment: an
+// unsigned max over the patterns with the sign cleared, which orders like
+// the magnitudes; an Inf or NaN pattern (>= 0x7F80) beats every finite one.
+__device__ __forceinline__ uint32_t seg_abs_max_bits(const uint32_t (&p)[8])
+{
+    u16x2 m = __builtin_bit_cast(u16x2, p[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, p[i] & 0x7FFF7FFFu));
+    return m.x > m.y ? m.x : m.y;
+}
+
 // One pass of an FP8 row: segment sg = s0 + lane + 64*u covers channels
 // [16 sg, 16 sg + 16); a 128-channel group is 8 adjacent lanes, reduced with
-// xor shuffles. Codes: e4m3 of x / s with s = max(amax, 1e-4) / 448, both
-// IEEE fp32 divisions.
+// xor shuffles. Codes: e4m3 of x / s with s = max(amax, 1e-4) / 448 (IEEE),
+// |x / s| <= 448 up to one rounding. A group holding an Inf or NaN takes a
+// separate branch (uniform over the wave, almost never taken) that divides
+// outright: amax over the non-NaN values, NaN quotients coded 0x7F.
 template <int NV>
 struct RowFp8 {
     static constexpr int kPerPass = NV * kWave;
@@ -86,28 +125,56 @@ struct RowFp8 {
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            float f[16];
             const uint32_t p[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w,
                                    hi[u].x, hi[u].y, hi[u].z, hi[u].w};
+            float f[16];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 f[2 * i] = bf16_lo(p[i]);
                 f[2 * i + 1] = bf16_hi(p[i]);
             }
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                amax = fmaxf(amax, fabsf(f[i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-            amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-            amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
-            const float s = fmaxf(amax, 1e-4f) / 448.0f;
+            uint32_t abits = seg_abs_max_bits(p);
+            abits = max(abits, (uint32_t)__shfl_xor((int)abits, 1, kWave));
+            abits = max(abits, (uint32_t)__shfl_xor((int)abits, 2, kWave));
+            abits = max(abits, (uint32_t)__shfl_xor((int)abits, 4, kWave));
             uint32_t wd[4];
+            float s;
+            if (__builtin_expect(__ballot(abits >= 0x7F80u) == 0, 1)) {
+                s = fmaxf(__uint_as_float(abits << 16), 1e-4f) / 448.0f;
+                const float rs = 1.0f / s;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                wd[j] = f32_to_e4m3(f[4 * j] / s) | (f32_to_e4m3(f[4 * j + 1] / s) << 8) |
-                        (f32_to_e4m3(f[4 * j + 2] / s) << 16) |
-                        (f32_to_e4m3(f[4 * j + 3] / s) << 24);
+                for (int j = 0; j < 4; ++j) {
+                    const int w = cvt2_e4m3<false>(quotient(f[4 * j], s, rs),
+                                                   quotient(f[4 * j + 1], s, rs), 0);
+                    wd[j] = (uint32_t)cvt2_e4m3<true>(quotient(f[4 * j + 2], s, rs),
+                                                      quotient(f[4 * j + 3], s, rs), w);
+                }
+            } else {
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float a = fabsf(f[i]);
+                    amax = (a > amax) ? a : amax;  // a NaN never wins
+                }
+#pragma unroll
+                for (int d = 1; d < 8; d <<= 1) {
+                    const float o = __shfl_xor(amax, d, kWave);
+                    amax = (o > amax) ? o : amax;
+                }
+                s = fmaxf(amax, 1e-4f) / 448.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const float v = f[4 * j + b] / s;
+                        const uint32_t c = (v != v) ? 0x7Fu
+                                                    : ((uint32_t)cvt2_e4m3<false>(v, 0.0f, 0) & 0xFFu);
+                        word |= c << (8 * b);
+                    }
+                    wd[j] = word;
+                }
+            }
             q[u] = u32x4{wd[0], wd[1], wd[2], wd[3]};
             sc[u] = s;
         }

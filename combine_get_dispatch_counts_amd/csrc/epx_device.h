@@ -1,8 +1,8 @@
 // epx_device.h -- device-side helpers shared by the libepx kernels (gfx950).
 //
-// Number formats are written from their definitions:
-//   bf16: the top half of an fp32 pattern, rounded to nearest even;
-//   e4m3: OCP E4M3FN, 1/4/3 bits, bias 7, no infinities, max 448.
+// bf16 is the top half of an fp32 pattern; f32_to_bf16 rounds to nearest
+// even, written from that definition. (FP8 codes come from gfx950's OCP
+// E4M3FN convert instruction, see dispatch.hip.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,33 +28,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float v)
     if ((u & 0x7FFFFFFFu) > 0x7F800000u)
         return 0x7FC0u;
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// fp32 -> OCP E4M3FN code, nearest even, saturating to 448.
-//  * |v| > 464 (the midpoint between 448 and the NaN pattern's 480): 0x7E|sign.
-//  * |v| >= 2^-6: a normal e4m3 keeps 3 of fp32's 23 mantissa bits, so round
-//    the magnitude pattern at bit 20 (add 0x7FFFF plus the lowest kept bit);
-//    a carry out of the mantissa bumps the exponent by itself. The fp32
-//    exponent (bias 127) becomes the e4m3 exponent (bias 7).
-//  * |v| < 2^-6: subnormal codes are multiples of 2^-9, code = rne(|v|*2^9);
-//    the product is exact and 8 lands on 0x08, the smallest normal.
-// NaN -> 0x7F; the sign is kept otherwise (negative underflow -> 0x80).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
-{
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t a = u & 0x7FFFFFFFu;
-    const uint32_t sign = (u >> 24) & 0x80u;
-    if (a > 0x7F800000u)
-        return 0x7Fu;
-    if (a > 0x43E80000u)                 // 464.0f
-        return sign | 0x7Eu;
-    if (a < 0x3C800000u) {               // 2^-6
-        const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
-        return sign | (uint32_t)q;
-    }
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    const uint32_t exp8 = (r >> 23) - 120u;   // (e - 127) + 7
-    return sign | (exp8 << 3) | ((r >> 20) & 7u);
 }
 
 __device__ __forceinline__ void flag_error(int *err, int bits)

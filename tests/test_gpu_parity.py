@@ -128,6 +128,62 @@ def test_dispatch_special_values():
         _check_dispatch(x, topk, w, 16, 4, fp8)
 
 
+def test_dispatch_fp8_nonfinite_groups():
+    """FP8 groups holding +-Inf or NaN (quiet, signalling, either sign) take
+    the exact-division branch; so do the finite groups of the same tokens
+    (the branch is taken per token), while other tokens keep the fast one."""
+    say("dispatch fp8 non-finite groups")
+    T, h = 12, 1024
+    rng = np.random.default_rng(12)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    x[0, 5] = 0x7F80
+    x[0, 3 * 128 + 1] = 0xFF80
+    x[0, 3 * 128 + 2] = 0x7FC0
+    x[1, 128 + 7] = 0x7FC0
+    x[1, 128 + 9] = 0xFF81
+    x[2, 256:384] = 0x7FC1
+    x[3, :] = 0x7F80
+    x[4, 640 + 3] = 0xFF80
+    x[4, 640 + 4] = 0x7F80
+    x[5, 1023] = 0xFFC0
+    topk = synth.random_routing(T, 3, 8, seed=13)
+    w = rng.random((T, 3)).astype(np.float32)
+    _check_dispatch(x, topk, w, 8, 4, True)
+
+
+def _patterns_below(rng, top: np.ndarray, n: int) -> np.ndarray:
+    """n bf16 patterns per entry of `top`, uniform over the magnitude patterns
+    0..top, random sign."""
+    mag = (rng.random((top.size, n)) * (top[:, None].astype(np.float64) + 1)).astype(np.uint32)
+    sign = rng.integers(0, 2, (top.size, n)).astype(np.uint32) << 15
+    return (mag | sign).astype(np.uint16)
+
+
+@pytest.mark.parametrize("arrangement", ["sorted", "shuffled", "group_max_planted"])
+def test_dispatch_fp8_every_bf16_pattern(arrangement):
+    """Every one of the 65536 bf16 patterns (NaNs and infinities included)
+    through the FP8 dispatch, against the oracle's IEEE division and
+    format-definition encoder; the planted arrangement sweeps group maxima
+    over the whole finite range, each with values spread below it."""
+    say(f"dispatch fp8 every bf16 pattern, {arrangement}")
+    rng = np.random.default_rng(65536)
+    h = 4096
+    if arrangement == "sorted":
+        x = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    elif arrangement == "shuffled":
+        x = rng.permutation(65536).astype(np.uint16)
+    else:
+        top = rng.integers(0, 0x7F80, 2048).astype(np.uint32)
+        groups = _patterns_below(rng, top, 128)
+        groups[np.arange(top.size), rng.integers(0, 128, top.size)] = top
+        x = groups.ravel()
+    x = x.reshape(-1, h)
+    T = x.shape[0]
+    topk = synth.random_routing(T, 4, 16, seed=T)
+    w = rng.random((T, 4)).astype(np.float32)
+    _check_dispatch(x, topk, w, 16, 4, True)
+
+
 @pytest.mark.parametrize("cfg", [1, 3, 4, 5])
 def test_dispatch_workloads_full_size(cfg):
     inp = synth.make_inputs(cfg)

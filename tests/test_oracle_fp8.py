@@ -100,6 +100,37 @@ def test_zero_group_uses_floor(orc):
     assert s[0, 1] == np.float32(2.0) / np.float32(448.0)
 
 
+def test_nonfinite_groups(orc):
+    """Groups holding Inf or NaN follow IEEE fp32 arithmetic through the same
+    formula: the maximum is taken over the values that compare (a NaN never
+    wins), an Inf maximum gives an Inf scale and signed-zero codes for the
+    finite values, and every NaN quotient is coded 0x7F."""
+    rng = np.random.default_rng(9)
+    xf = rng.standard_normal(512).astype(np.float32)
+    xb = synth.to_bf16_bits(xf)[None, :].copy()
+    xb[0, 5] = 0x7F80                      # group 0: +Inf
+    xb[0, 128 + 7] = 0x7FC0                # group 1: a quiet NaN ...
+    xb[0, 128 + 9] = 0xFF81                # ... and a negative signalling NaN
+    xb[0, 256 + 1] = 0xFF80                # group 2: -Inf and +Inf
+    xb[0, 256 + 2] = 0x7F80
+    xb[0, 384:] = 0x7FC1                   # group 3: all NaN
+    q, s = orc.quantize_rows(xb)
+    assert np.isinf(s[0, 0]) and np.isinf(s[0, 2])
+    finite0 = np.delete(np.arange(128), 5)
+    signs0 = (xb[0, finite0] >> 15).astype(np.uint8) * 0x80
+    np.testing.assert_array_equal(q[0, finite0], signs0)
+    assert q[0, 5] == 0x7F
+    g1 = (xb[0, 128:256].astype(np.uint32) << 16).view(np.float32)
+    nan1 = np.isnan(g1)
+    assert s[0, 1] == np.float32(np.abs(g1[~nan1]).max()) / np.float32(448.0)
+    assert (q[0, 128:256][nan1] == 0x7F).all()
+    v = (g1[~nan1] / s[0, 1]).astype(np.float32)
+    np.testing.assert_array_equal(q[0, 128:256][~nan1], _torch_e4m3(v))
+    assert q[0, 257] == 0x7F and q[0, 258] == 0x7F
+    assert s[0, 3] == np.float32(1e-4) / np.float32(448.0)
+    assert (q[0, 384:] == 0x7F).all()
+
+
 def _numpy_quantize(xb: np.ndarray):
     """The quantiser written with numpy's IEEE fp32 arithmetic and torch's cast."""
     T, h = xb.shape
