@@ -23,9 +23,10 @@ from .api import (  # noqa: E402
     ll_dispatch,
     ll_reset,
     ll_size_hint,
+    scale_stride,
     workspace_size,
 )
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
-           "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
+           "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
            "ll_reset", "alloc_ll", "ll_dispatch"]

@@ -26,6 +26,7 @@ SIGNATURES = {
     "epx_strerror": (ctypes.c_char_p, [_I]),
     "epx_workspace_size": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "epx_ll_size_hint": (_SZ, [_I, _I, _I, _I, _I]),
+    "epx_scale_stride": (_I, [_I]),
     "epx_get_dispatch_layout": (_I, [_P, _P, _I, _I, _I, _I, _I] + [_P] * 11 + [_SZ, _P]),
     "epx_dispatch": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I] + [_P] * 4 + [_I]
                      + [_P] * 5 + [_I64] + [_P] * 3 + [_I64, _P, _P]),

@@ -140,8 +140,21 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
     return lay
 
 
+def scale_stride(h: int) -> int:
+    """fp32 entries per FP8 scale row: h/128 rounded up to whole 128-byte
+    lines; the entries past h/128 are written as +0.0."""
+    n = _lib.load().epx_scale_stride(h)
+    if n <= 0:  # the code epx_dispatch gives for such an h with fp8
+        bad_h = h < 8 or h % 8 != 0
+        raise EpxError(_lib.EPX_EINVAL if bad_h else _lib.EPX_EUNSUPPORTED,
+                       f"FP8 rows need h % 128 == 0 (h = {h})")
+    return n
+
+
 @dataclass
 class Dispatched:
+    """Dispatch outputs. FP8 scales are [rows, scale_stride(h)]: the group
+    scales of row i are ``send_scales[i, :h // 128]``."""
     send_x: torch.Tensor          # [rows, h] bf16, or uint8 codes with fp8
     send_scales: torch.Tensor | None
     send_src: torch.Tensor        # [rows] int32
@@ -161,12 +174,12 @@ def alloc_dispatch(T: int, h: int, K: int, send_rows: int, recv_rows: int, fp8: 
     f32 = dict(dtype=torch.float32, device=device)
     return dict(
         send_x=torch.empty((send_rows, h), dtype=dt, device=device),
-        send_scales=torch.empty((send_rows, h // 128), **f32) if fp8 else None,
+        send_scales=torch.empty((send_rows, scale_stride(h)), **f32) if fp8 else None,
         send_src=torch.empty(send_rows, dtype=torch.int32, device=device),
         send_topk_idx=torch.empty((send_rows, K), dtype=torch.int64, device=device),
         send_topk_w=torch.empty((send_rows, K), **f32),
         recv_x=torch.empty((recv_rows, h), dtype=dt, device=device),
-        recv_scales=torch.empty((recv_rows, h // 128), **f32) if fp8 else None,
+        recv_scales=torch.empty((recv_rows, scale_stride(h)), **f32) if fp8 else None,
         recv_src=torch.empty(recv_rows, dtype=torch.int32, device=device),
         pos_exp=torch.empty((T, K), dtype=torch.int32, device=device))
 
@@ -235,7 +248,7 @@ def ll_reset(ll_count: torch.Tensor) -> None:
 @dataclass
 class LowLatency:
     ll_x: torch.Tensor              # [E*R_buf*cap, h] bf16 or uint8
-    ll_scales: torch.Tensor | None  # [E*R_buf*cap, h/128] fp32
+    ll_scales: torch.Tensor | None  # [E*R_buf*cap, scale_stride(h)] fp32
     ll_src: torch.Tensor            # [E*R_buf*cap] int32
     ll_count: torch.Tensor          # [E*R_buf] int32
     pos_ll: torch.Tensor            # [T,K] int32 -- the handle for combine
@@ -246,7 +259,8 @@ def alloc_ll(E: int, R_buf: int, cap: int, h: int, T: int, K: int, fp8: bool,
     rows = E * R_buf * cap
     buf = LowLatency(
         ll_x=torch.empty((rows, h), dtype=torch.uint8 if fp8 else torch.bfloat16, device=device),
-        ll_scales=torch.empty((rows, h // 128), dtype=torch.float32, device=device) if fp8 else None,
+        ll_scales=torch.empty((rows, scale_stride(h)), dtype=torch.float32,
+                              device=device) if fp8 else None,
         ll_src=torch.empty(rows, dtype=torch.int32, device=device),
         ll_count=torch.empty(E * R_buf, dtype=torch.int32, device=device),
         pos_ll=torch.empty((T, K), dtype=torch.int32, device=device))
@@ -276,5 +290,6 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
 
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
+           "scale_stride",
            "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
            "ll_reset", "alloc_ll", "ll_dispatch"]

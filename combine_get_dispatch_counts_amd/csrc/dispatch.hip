@@ -108,13 +108,19 @@ __device__ __forceinline__ uint32_t seg_abs_max_bits(const uint32_t (&p)[8])
 // |x / s| <= 448 up to one rounding. A group holding an Inf or NaN takes a
 // separate branch (uniform over the wave, almost never taken) that divides
 // outright: amax over the non-NaN values, NaN quotients coded 0x7F.
+// Scale rows are scale_stride(h) floats apart, a whole number of 128-byte
+// lines, and written in full (zeros past the last group): a scattered row
+// that ends inside a line leaves that line to be merged in memory with a
+// neighbour written at another time, which costs far more than the pad.
 template <int NV>
 struct RowFp8 {
     static constexpr int kPerPass = NV * kWave;
     u32x4 q[NV];
-    float sc[NV];
+    u32x4 sv;   // scales of groups s0/8 + 4*lane .. +3 of the pass, +0 past the last group
+    int n_sv;   // lanes holding a slice of the (padded) scale row in this pass
     __device__ __forceinline__ void load_quantise(const u32x4 *src, int s0, int nseg)
     {
+        float sc[NV];
         u32x4 lo[NV], hi[NV];
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -178,18 +184,35 @@ struct RowFp8 {
             q[u] = u32x4{wd[0], wd[1], wd[2], wd[3]};
             sc[u] = s;
         }
+        // Group gl = 4L + j of the pass sits in pass item u = L/2, on the
+        // lanes 8*(gl % 8) .. +7; collect four per lane for one store.
+        const int L = lane_id(), g0 = s0 >> 3, ngrp = nseg >> 3;
+        float g4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = __shfl(sc[u], 8 * (4 * (L & 1) + j), kWave);
+                if ((L >> 1) == u && g0 + 4 * L + j < ngrp)
+                    g4[j] = v;
+            }
+        }
+        sv = u32x4{__float_as_uint(g4[0]), __float_as_uint(g4[1]), __float_as_uint(g4[2]),
+                   __float_as_uint(g4[3])};
+        n_sv = min(16, (scale_stride(nseg << 4) - g0) >> 2);
     }
+    // Codes of the pass to one destination row, plus that row's slice of
+    // the scale row (one 16-byte store by the first lanes).
     __device__ __forceinline__ void store(uint8_t *q_row, float *s_row, int s0, int nseg) const
     {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int sg = s0 + u * kWave + lane_id();
-            if (sg < nseg) {
+            if (sg < nseg)
                 store16_wt(q_row + (size_t)sg * 16, q[u]);
-                if ((sg & 7) == 0)
-                    s_row[sg >> 3] = sc[u];
-            }
         }
+        if (lane_id() < n_sv)
+            store16_wt(s_row + (s0 >> 3) + 4 * lane_id(), sv);
     }
 };
 
@@ -207,7 +230,7 @@ template <bool FP8, typename Row>
 __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t *xrow, int h,
                                         void *a_x, float *a_s, void *b_x, float *b_s)
 {
-    const int nvec = h >> 3, nseg = h >> 4, ngrp = h >> 7;
+    const int nvec = h >> 3, nseg = h >> 4, ld_s = scale_stride(h);
     const int per_pass = Row::kPerPass;
     const int nitems = FP8 ? nseg : nvec;
     const size_t row_bytes = FP8 ? (size_t)h : (size_t)h * 2;
@@ -225,7 +248,7 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
                 continue;
             if constexpr (FP8)
                 row.store(static_cast<uint8_t *>(a_x) + (size_t)r * row_bytes,
-                          a_s + (size_t)r * ngrp, i0, nseg);
+                          a_s + (size_t)r * ld_s, i0, nseg);
             else
                 row.store(static_cast<char *>(a_x) + (size_t)r * row_bytes, i0, nvec);
         }
@@ -235,7 +258,7 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
                 continue;
             if constexpr (FP8)
                 row.store(static_cast<uint8_t *>(b_x) + (size_t)r * row_bytes,
-                          b_s + (size_t)r * ngrp, i0, nseg);
+                          b_s + (size_t)r * ld_s, i0, nseg);
             else
                 row.store(static_cast<char *>(b_x) + (size_t)r * row_bytes, i0, nvec);
         }

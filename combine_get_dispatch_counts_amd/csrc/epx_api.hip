@@ -120,6 +120,13 @@ int epx_workspace_size(int T, int K, int E, int R, size_t *bytes)
     return EPX_OK;
 }
 
+int epx_scale_stride(int h)
+{
+    if (check_hidden(h, 1) != EPX_OK)
+        return 0;
+    return epx::scale_stride(h);
+}
+
 size_t epx_ll_size_hint(int max_tokens_per_rank, int h, int R, int E, int fp8)
 {
     if (max_tokens_per_rank < 1 || check_hidden(h, fp8) != EPX_OK || R < 1 || E < 1 ||
@@ -130,7 +137,7 @@ size_t epx_ll_size_hint(int max_tokens_per_rank, int h, int R, int E, int fp8)
     const size_t rows = (size_t)E * R * max_tokens_per_rank;
     size_t total = up(rows * (fp8 ? (size_t)h : (size_t)h * 2));
     if (fp8)
-        total += up(rows * (size_t)(h / 128) * sizeof(float));
+        total += up(rows * (size_t)epx::scale_stride(h) * sizeof(float));
     total += up(rows * sizeof(int32_t));                 // source index per row
     total += up((size_t)E * R * sizeof(int32_t));        // count per region
     return up(total);
@@ -205,7 +212,8 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
             !slot_in_expert || !pos_exp || !send_x || !send_src || !send_topk_idx ||
             !send_topk_w || !recv_x || !recv_src)
             return EPX_EINVAL;
-        if (fp8 && (!send_scales || !recv_scales))
+        if (fp8 && (!send_scales || !recv_scales || !aligned16(send_scales) ||
+                    !aligned16(recv_scales)))
             return EPX_EINVAL;
         if (!aligned16(x) || !aligned16(send_x) || !aligned16(recv_x))
             return EPX_EINVAL;
@@ -276,7 +284,7 @@ int epx_ll_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_
         return EPX_ECAPACITY;
     if (!ll_count || (T > 0 && (!x || !topk_idx || !ll_x || !ll_src || !pos_ll)))
         return EPX_EINVAL;
-    if (T > 0 && fp8 && !ll_scales)
+    if (T > 0 && fp8 && (!ll_scales || !aligned16(ll_scales)))
         return EPX_EINVAL;
     if (T > 0 && (!aligned16(x) || !aligned16(ll_x)))
         return EPX_EINVAL;

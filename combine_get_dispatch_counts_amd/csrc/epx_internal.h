@@ -13,6 +13,14 @@ struct epx_ctx {
 
 namespace epx {
 
+// fp32 entries per row of an FP8 scale array for hidden size h: the h/128
+// group scales rounded up to a multiple of 32, so every row is a whole
+// number of 128-byte lines (entries past h/128 hold +0).
+__host__ __device__ constexpr int scale_stride(int h)
+{
+    return ((h >> 7) + 31) & ~31;
+}
+
 // Tokens per layout tile: 4 waves of 64 tokens, one token per thread.
 constexpr int kLayoutWaves = 4;
 constexpr int kLayoutTile = 64 * kLayoutWaves;

@@ -79,9 +79,17 @@ const char *epx_strerror(int code);
  * [P2] "Buffer 与内存视角": the workspace is allocated up front, once. */
 int epx_workspace_size(int T, int K, int E, int R, size_t *bytes);
 
+/* fp32 entries per row of every FP8 scale array (send_scales, recv_scales,
+ * ll_scales) for hidden size h: the h/128 group scales rounded up to a
+ * multiple of 32, so each row fills whole 128-byte lines; the kernels write
+ * the padding entries as +0.0f. Row i's scales start at i * stride. Returns
+ * 0 if h is not a positive multiple of 128. (Rows that end inside a line
+ * would leave each line shared by two rows written at different times.) */
+int epx_scale_stride(int h);
+
 /* Bytes of a low-latency receive buffer for max_tokens_per_rank tokens per
  * source: E*R regions of max_tokens_per_rank rows (bf16: 2h bytes; fp8: h
- * bytes + h/128 fp32 scales) plus one int32 source index per row and one
+ * bytes + epx_scale_stride(h) fp32 scales) plus one int32 source index per row and one
  * int32 count per region, each array rounded up to 128 bytes, the total
  * rounded up to a multiple of 128. [P3] 2.2: the size hint of the worst-case
  * layout, rounded to the buffer alignment. Returns 0 for bad arguments. */
@@ -132,18 +140,22 @@ int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K,
  * In:  x [T,h] bf16; topk_idx [T,K]; topk_w [T,K] fp32; the layout outputs
  *      rank_off, exp_off, pos_in_rank, slot_in_expert of the same topk_idx.
  *      fp8 = 0: rows are bf16 (2h bytes). fp8 = 1: rows are e4m3 codes
- *      (h bytes) plus fp32 scales [rows, h/128]: per token and per 128
- *      channels, s = max(amax, 1e-4) / 448 and q = e4m3(x / s), both IEEE
- *      fp32 divisions, rounded to nearest even.
+ *      (h bytes) plus fp32 scales [rows, epx_scale_stride(h)], of which the
+ *      first h/128 are used: per token and per 128 channels, s = max(amax,
+ *      1e-4) / 448 and q = e4m3(x / s), both IEEE fp32 divisions, rounded to
+ *      nearest even (OCP E4M3FN, saturating to 448). amax is the largest
+ *      magnitude that compares (a NaN never wins); a NaN quotient (x NaN,
+ *      or +-Inf over an Inf scale) is coded 0x7F.
  * Out: send_x [send_cap_rows, h(*2)] rank-major: row rank_off[r] +
  *        pos_in_rank[t,r] holds token t for each rank r it goes to;
- *      send_scales [send_cap_rows, h/128] (fp8 only, else may be NULL);
+ *      send_scales [send_cap_rows, epx_scale_stride(h)] (fp8 only, else
+ *        may be NULL; 16-byte aligned);
  *      send_src [rows] source token; send_topk_idx [rows,K] int64 local
  *        expert index (e - r*L) where expert e is on the row's rank, else -1;
  *      send_topk_w [rows,K] the weight there, else 0;
  *      recv_x [recv_cap_rows, ...] expert-major: row exp_off[e] +
  *        slot_in_expert[t,k] holds token t for each entry (t,k) with expert e;
- *      recv_scales (fp8), recv_src [rows] source token;
+ *      recv_scales (fp8, as send_scales), recv_src [rows] source token;
  *      pos_exp [T,K] the recv row of (t,k), or -1: the handle for combine.
  *      A row index >= its capacity is not written and sets
  *      EPX_DEV_OVERFLOW; totals from the layout call say what is needed. */
@@ -186,7 +198,8 @@ int epx_ll_reset(epx_ctx *ctx, int32_t *ll_count, int64_t n, hipStream_t stream)
  *      launched); R_buf = R (all destinations' buffers side by side: region
  *      e*R + src_rank) or 1 (this source's slice only: region e);
  *      E * R_buf * cap must fit in int32. fp8 as in epx_dispatch.
- * Out: ll_x [E*R_buf*cap, h(*2)], ll_scales (fp8), ll_src [E*R_buf*cap]:
+ * Out: ll_x [E*R_buf*cap, h(*2)], ll_scales (fp8: [E*R_buf*cap,
+ *      epx_scale_stride(h)], 16-byte aligned), ll_src [E*R_buf*cap]:
  *      entry (t,k) with expert e fills row region(e)*cap + slot, where slot
  *      counts entries before (t,k) routed to e (row-major order); other
  *      rows are not touched.

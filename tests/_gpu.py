@@ -64,9 +64,15 @@ def dispatch(x: np.ndarray, topk: np.ndarray, w: np.ndarray, E: int, R: int, fp8
     res["send_x"] = host_bits(d.send_x)
     res["recv_x"] = host_bits(d.recv_x)
     if fp8:
-        res["send_scales"] = host_bits(d.send_scales)
-        res["recv_scales"] = host_bits(d.recv_scales)
+        ngrp = h // 128
+        for k in ("send_scales", "recv_scales"):
+            full = host_bits(getattr(d, k))
+            n = n_send if k.startswith("send") else n_recv
+            res[k + "_pad"] = full[:n, ngrp:]
+            res[k] = full[:, :ngrp]
     for k in list(res):
+        if k.endswith("_pad"):
+            continue
         if k.startswith("send"):
             res[k] = res[k][:n_send]
         elif k.startswith("recv"):

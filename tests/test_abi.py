@@ -64,8 +64,22 @@ def _up(n):
 def test_ll_size_hint(lib, cap, h, R, E, fp8):
     rows = E * R * cap
     data = rows * (h if fp8 else 2 * h)
-    want = _up(data) + (_up(rows * (h // 128) * 4) if fp8 else 0) + _up(rows * 4) + _up(E * R * 4)
+    stride = -(-(h // 128) // 32) * 32
+    want = _up(data) + (_up(rows * stride * 4) if fp8 else 0) + _up(rows * 4) + _up(E * R * 4)
     assert lib.epx_ll_size_hint(cap, h, R, E, fp8) == want
+
+
+@pytest.mark.parametrize("h,stride", [(128, 32), (4096, 32), (4224, 64), (7168, 64),
+                                      (8192, 64), (9216, 96), (16384, 128)])
+def test_scale_stride(lib, h, stride):
+    """Scale rows: h/128 entries rounded up to whole 128-byte lines."""
+    assert lib.epx_scale_stride(h) == stride
+    assert stride >= h // 128 and (stride * 4) % 128 == 0 and stride - h // 128 < 32
+
+
+def test_scale_stride_rejects(lib):
+    for h in (0, -128, 100, 7000):
+        assert lib.epx_scale_stride(h) == 0
 
 
 def test_ll_size_hint_rejects(lib):
@@ -78,3 +92,15 @@ def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.epx_strerror(code)
     assert b"unknown" in lib.epx_strerror(7)
+
+
+def test_binding_scale_stride():
+    import combine_get_dispatch_counts_amd as epx
+
+    assert epx.scale_stride(7168) == 64
+    with pytest.raises(epx.EpxError) as ei:
+        epx.scale_stride(136)
+    assert ei.value.code == -3
+    with pytest.raises(epx.EpxError) as ei:
+        epx.scale_stride(4)
+    assert ei.value.code == -1

@@ -84,6 +84,8 @@ def _check_dispatch(x, topk, w, E, R, fp8, worst_case=False, guard=0):
     keys = ["send_x", "send_src", "send_topk_idx", "send_topk_w", "recv_x", "recv_src", "pos_exp"]
     if fp8:
         keys += ["send_scales", "recv_scales"]
+        for k in ("send_scales_pad", "recv_scales_pad"):
+            assert (g[k].view(np.uint32) == 0).all(), f"{k}: scale row padding is not +0"
     for k in keys:
         _eq(g[k], o[k], k)
     for region in ("guard", "unused"):
@@ -262,7 +264,7 @@ def test_identity_experts_closed_form(cfg, fp8):
         def deq(q, s):
             return (q.view(torch.float8_e4m3fn).float() * s.repeat_interleave(128, 1)).to(torch.bfloat16)
 
-        y = deq(recv, g["_dispatched"].recv_scales)        # the GPU's dispatched rows
+        y = deq(recv, g["_dispatched"].recv_scales[:, :wl.h // 128])  # the GPU's rows
         q, sc = oracle.quantize_rows(inp["x"])             # the expected rows: the oracle's codes
         xs = deq(torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda())
     else:
@@ -277,6 +279,19 @@ def test_identity_experts_closed_form(cfg, fp8):
 
 
 # ------------------------------------------------------------------ low latency
+
+def _check_ll_scales(got: np.ndarray, want: np.ndarray, want_src: np.ndarray, what: str):
+    """Scale rows [rows, stride] against the oracle's [rows, h/128]: the
+    used columns bit-exact, the padding +0 on written rows and untouched
+    (canary) on the others."""
+    ngrp = want.shape[1]
+    _eq(got[:, :ngrp], want, what)
+    pad = got[:, ngrp:].view(np.uint32)
+    written = want_src >= 0
+    assert (pad[written] == 0).all(), f"{what}: padding of written rows is not +0"
+    assert (pad[~written] == np.uint32(0x01010101 * CANARY)).all(), \
+        f"{what}: padding of untouched rows was written"
+
 
 def _ll_gpu(x, topk, E, R, src, cap, R_buf, fp8):
     import combine_get_dispatch_counts_amd as epx
@@ -311,7 +326,7 @@ def test_ll_dispatch_small(cfg, T, src, R_buf_full, fp8, cap):
     _eq(host_bits(buf.ll_src), o["ll_src"], "ll_src")
     _eq(host_bits(buf.ll_x), o["ll_x"], "ll_x")
     if fp8:
-        _eq(host_bits(buf.ll_scales), o["ll_scales"], "ll_scales")
+        _check_ll_scales(host_bits(buf.ll_scales), o["ll_scales"], o["ll_src"], "ll_scales")
 
 
 def test_ll_dispatch_decode_full_buffer():
@@ -327,9 +342,10 @@ def test_ll_dispatch_decode_full_buffer():
         o = oracle.ll_dispatch(inp["x"], inp["topk_idx"], wl.E, wl.R, src, wl.cap, 1, fp8=True)
         E, R, cap, h = wl.E, wl.R, wl.cap, wl.h
         x4 = buf.ll_x.view(E, R, cap, h)
-        s4 = buf.ll_scales.view(E, R, cap, h // 128)
+        s4 = buf.ll_scales.view(E, R, cap, -1)
         _eq(host_bits(x4[:, src]).reshape(E * cap, h), o["ll_x"], "owned ll_x")
-        _eq(host_bits(s4[:, src]).reshape(E * cap, -1), o["ll_scales"], "owned ll_scales")
+        _check_ll_scales(host_bits(s4[:, src]).reshape(E * cap, -1), o["ll_scales"], o["ll_src"],
+                         "owned ll_scales")
         _eq(host_bits(buf.ll_src.view(E, R, cap)[:, src]).reshape(-1), o["ll_src"], "owned ll_src")
         cnt = host_bits(buf.ll_count).reshape(E, R)
         _eq(cnt[:, src], o["ll_count"], "owned counts")
