@@ -149,7 +149,7 @@ def other_workloads(n=20):
     x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
     tk = torch.from_numpy(inp["topk_idx"]).to(dev)
     w = torch.from_numpy(inp["topk_w"]).to(dev)
-    ws = torch.empty(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
     lay = epx.alloc_layout(T, K, E, R, None, dev)
     bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, True, dev)
     epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay)
@@ -209,7 +209,7 @@ def other_workloads(n=20):
     x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
     tk = torch.from_numpy(inp["topk_idx"]).to(dev)
     w = torch.from_numpy(inp["topk_w"]).to(dev)
-    ws = torch.empty(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
     lay = epx.alloc_layout(T, K, E, R, None, dev)
     bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, False, dev)
     epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay)
@@ -268,7 +268,7 @@ def main():
     w = torch.from_numpy(inp["topk_w"]).to(dev)
     cap_send, cap_recv = T * min(K, R), T * K
     bufs = epx.alloc_dispatch(T, h, K, cap_send, cap_recv, False, dev)
-    ws = torch.empty(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
     expert_out = synth.expert_outputs(cap_recv, h, seed=4242, device="cuda")
     out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
 

@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libepx.so")
 
 EPX_OK, EPX_EINVAL, EPX_ECAPACITY, EPX_EUNSUPPORTED, EPX_EHIP, EPX_EDEVICE = 0, -1, -2, -3, -4, -5
-DEV_BAD_ROUTE, DEV_OVERFLOW, DEV_BAD_HANDLE = 1, 2, 4
+DEV_BAD_ROUTE, DEV_OVERFLOW, DEV_BAD_HANDLE, DEV_WORKSPACE = 1, 2, 4, 8
 MAX_TOPK, MAX_EXPERTS, MAX_RANKS = 32, 512, 64
 
 _P = ctypes.c_void_p

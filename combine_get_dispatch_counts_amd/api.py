@@ -52,6 +52,21 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = Non
         raise ValueError(f"{name} must have {ndim} dims")
 
 
+_workspaces: dict[tuple[int, int], torch.Tensor] = {}
+
+
+def _layout_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-filled layout workspace of >= nbytes for this device and
+    stream, kept for later calls (the layout call leaves it reusable)."""
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (idx, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
 def workspace_size(T: int, K: int, E: int, R: int) -> int:
     n = ctypes.c_size_t()
     check(_lib.load().epx_workspace_size(T, K, E, R, ctypes.byref(n)), "epx_workspace_size")
@@ -110,7 +125,9 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
                         out: Layout | None = None) -> Layout:
     """Counts, is_token_in_rank and receive offsets for topk_idx. ``out``
     (from alloc_layout with the same shapes) avoids allocating; ``workspace``
-    must hold workspace_size(T, K, E, R) bytes; ``totals_host`` (pinned int32
+    must hold workspace_size(T, K, E, R) bytes and be zero-filled before its
+    first use (each call leaves it ready for the next; without one, a cached
+    workspace per device and stream is used); ``totals_host`` (pinned int32
     [2]) also receives the totals, readable after a stream synchronisation."""
     _need(topk_idx, torch.int64, "topk_idx", 2)
     dev = topk_idx.device
@@ -125,7 +142,7 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
                              or tuple(lay.channel_prefix.shape) != (R, num_channels)):
             raise ValueError("out has no channel_prefix of shape (R, num_channels)")
     if workspace is None:
-        workspace = torch.empty(max(workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+        workspace = _layout_workspace(dev, workspace_size(T, K, E, R))
     if totals_host is not None and not (totals_host.is_pinned() and totals_host.numel() >= 2
                                         and totals_host.dtype == torch.int32):
         raise ValueError("totals_host must be a pinned int32 tensor of >= 2 elements")

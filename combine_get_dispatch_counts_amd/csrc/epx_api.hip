@@ -175,7 +175,9 @@ int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K,
     a.T = T; a.K = K; a.E = E; a.R = R; a.L = E / R;
     a.C = channel_prefix ? C : 0;
     a.ntiles = (T + epx::kLayoutTile - 1) / epx::kLayoutTile;
-    a.tile_cnt = static_cast<int32_t *>(ws);
+    a.hdr = static_cast<epx::LayoutHdr *>(ws);
+    a.pub = need ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(epx::LayoutHdr))
+                 : nullptr;
     a.num_tokens_per_expert = num_tokens_per_expert;
     a.num_tokens_per_rank = num_tokens_per_rank;
     a.is_token_in_rank = is_token_in_rank;

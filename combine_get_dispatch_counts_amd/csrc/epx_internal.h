@@ -24,12 +24,22 @@ __host__ __device__ constexpr int scale_stride(int h)
 // Tokens per layout tile: 4 waves of 64 tokens, one token per thread.
 constexpr int kLayoutWaves = 4;
 constexpr int kLayoutTile = 64 * kLayoutWaves;
+constexpr int kLayoutThreads = 2 * kLayoutTile;  // two threads per token of a tile
+
+// Head of the layout workspace (the rest: published words [ntiles, E + R]).
+// Zero before the first call; every call leaves it ready for the next.
+struct LayoutHdr {
+    unsigned long long calls;  // calls completed << 32 | blocks of this call arrived;
+                               // the call's tag (in published words) is calls >> 32, + 1
+    int pad[30];
+};
 
 struct LayoutArgs {
     const int64_t *topk_idx;
     int T, K, E, R, L, C;
     int ntiles;
-    int32_t *tile_cnt;  // workspace [ntiles, E + R]
+    LayoutHdr *hdr;
+    uint64_t *pub;  // [ntiles, E + R]
     int32_t *num_tokens_per_expert, *num_tokens_per_rank;
     uint8_t *is_token_in_rank;
     int32_t *rank_off, *exp_off, *pos_in_rank, *slot_in_expert, *channel_prefix;

@@ -6,20 +6,28 @@
 // 通信", "事件驱动调度的本质": count locally, prefix-sum the offsets.
 // [P2] "DeepEP v2": a token counts once per destination rank.
 //
-// Two launches, no global atomics, deterministic:
-//   count    one block per tile of 256 tokens (4 waves, one token per lane).
-//            Each wave ORs its lanes into LDS bitmaps: emask[w][e] has bit l
-//            set when token l of wave w routes an entry to expert e, rmask
-//            likewise per rank (the OR deduplicates ranks for free). A
-//            token's rank inside the tile is then the earlier waves' count
-//            plus popcount(mask & lanes below it). The block writes
-//            is_token_in_rank and these tile-local ranks straight into
-//            pos_in_rank / slot_in_expert / channel_prefix, and the tile's
-//            counts into the workspace [tile, E + R].
-//   finalize one block per tile again: sums the counts of the tiles before
-//            it (a few KB from L2), scans all tiles' totals into exp_off /
-//            rank_off in LDS and adds the tile's prefix to the tile-local
-//            ranks. Block 0 writes the counts, offsets and totals.
+// One launch, deterministic results:
+//   Block b handles tile b of 256 tokens (4 waves, one token per lane).
+//   Workgroups are dispatched in index order, so a tile waits only for
+//   tiles that are running or done; with a few hundred tiles they are all
+//   resident at once anyway. Each wave ORs its lanes into LDS bitmaps:
+//   emask[w][e] has bit l set when token l of wave w routes an entry to
+//   expert e, rmask likewise per rank (the OR deduplicates ranks for free).
+//   A token's rank inside the tile is the earlier waves' count plus
+//   popcount(mask & lanes below it).
+//   The tile then publishes its per-expert and per-rank counts and looks
+//   back over the earlier tiles' published words for its prefix (a
+//   decoupled look-back: a word carries the call's tag, an "inclusive" bit
+//   and the value, so one 64-bit load reads all three). With the prefix the
+//   block writes is_token_in_rank, pos_in_rank, slot_in_expert and its
+//   channel_prefix columns once, in final form. One more block looks back
+//   from past the last tile: that prefix is the totals, from which it
+//   writes the counts, offsets and totals while the tiles write rows.
+//   A 64-bit counter in the workspace (call number << 32 | blocks arrived)
+//   gives every block the call's tag in one atomic, issued beside the topk
+//   loads; the last block to arrive moves it on to the next call. Waits are
+//   bounded: a tile that waits too long flags EPX_DEV_WORKSPACE and goes
+//   on, so the kernel always ends.
 // A wave in which some token lists one expert twice counts earlier entries
 // directly instead, so a slot stays "entries before (t,k)" exactly.
 #include "epx_device.h"
@@ -31,6 +39,7 @@ namespace {
 constexpr int W = kLayoutWaves;
 
 struct CountLds {
+    uint64_t *rb;     // [kLayoutTile] rank bits of each token of the tile
     uint64_t *emask;  // [W][E]
     uint64_t *rmask;  // [W][R]
     int *ecnt;        // [W][E] entries of wave w routed to e
@@ -41,14 +50,15 @@ struct CountLds {
 
 __host__ __device__ inline size_t count_lds_bytes(int E, int R)
 {
-    return sizeof(uint64_t) * ((size_t)W * E + (size_t)W * R) +
+    return sizeof(uint64_t) * (kLayoutTile + (size_t)W * E + (size_t)W * R) +
            sizeof(int) * (2 * (size_t)W * E + (size_t)W * R + W);
 }
 
 __device__ CountLds carve_count(char *base, int E, int R)
 {
     CountLds s;
-    s.emask = reinterpret_cast<uint64_t *>(base);
+    s.rb = reinterpret_cast<uint64_t *>(base);
+    s.emask = s.rb + kLayoutTile;
     s.rmask = s.emask + (size_t)W * E;
     s.ecnt = reinterpret_cast<int *>(s.rmask + (size_t)W * R);
     s.wpre_e = s.ecnt + (size_t)W * E;
@@ -57,9 +67,83 @@ __device__ CountLds carve_count(char *base, int E, int R)
     return s;
 }
 
-__host__ __device__ inline size_t finalize_lds_bytes(int E, int R)
+// After the count scratch: the tile's counts, its prefix and (last tile)
+// the offsets, each E + R (+ 2) ints.
+__host__ __device__ inline size_t layout_lds_bytes(int E, int R)
 {
-    return sizeof(int) * (2 * (size_t)(E + R) + (E + R + 2));  // pre, tot, off
+    return count_lds_bytes(E, R) + sizeof(int) * (3 * (size_t)(E + R) + 2);
+}
+
+// Published words: (tag << 32) | inclusive bit 31 | value (< 2^31). A word
+// from an earlier call carries an older tag and reads as "not yet".
+constexpr uint64_t kInclusive = 0x80000000ull;
+constexpr int kSpinLimit = 1 << 18;
+
+__device__ __forceinline__ void pub_store(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t pub_load(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One round of the look-back: the words of tiles j, j-1, .., j-B+1 of
+// column c, loaded together (a tile index below 0 loads the reader's own
+// row instead, so surplus loads do not pile onto the lines every tile
+// reads), then summed from j down until a word is unpublished or carries an
+// inclusive prefix. Returns how many words were consumed; *done is set when
+// an inclusive prefix ended the walk.
+template <int B>
+__device__ __forceinline__ int look_back_round(const uint64_t *pub, int ER, int self, int j, int c,
+                                               uint32_t tag, uint32_t &acc, bool &done)
+{
+    uint64_t w[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+        w[u] = pub_load(pub + (int64_t)(j - u >= 0 ? j - u : self) * ER + c);
+    int u = 0;
+    for (; u < B && j - u >= 0; ++u) {
+        if ((uint32_t)(w[u] >> 32) != tag)
+            break;
+        acc += (uint32_t)w[u] & 0x7FFFFFFFu;
+        if (w[u] & kInclusive) {
+            done = true;
+            return u + 1;
+        }
+    }
+    return u;
+}
+
+// Sum over tiles before `tile` of column c: walk back from tile - 1, adding
+// aggregates until a tile's inclusive prefix ends the walk (a decoupled
+// look-back). `self` is a row of the workspace that surplus loads may read
+// (the reader's own tile row). Returns false if a word stayed unpublished
+// too long.
+__device__ bool look_back(const uint64_t *pub, int ER, int tile, int self, int c, uint32_t tag,
+                          int *out)
+{
+    uint32_t acc = 0;
+    int j = tile - 1, polls = 0;
+    while (j >= 0) {
+        bool done = false;
+        const int batch = j < 4 ? 4 : 16;
+        const int u = j < 4 ? look_back_round<4>(pub, ER, self, j, c, tag, acc, done)
+                            : look_back_round<16>(pub, ER, self, j, c, tag, acc, done);
+        if (done)
+            break;
+        j -= u;
+        if (j >= 0 && u < batch) {  // stopped at an unpublished word: poll again
+            if (++polls > kSpinLimit) {
+                *out = (int)acc;
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    *out = (int)acc;
+    return true;
 }
 
 // Flat index walker over a [rows, cols] row-major block: thread tid starts
@@ -139,23 +223,23 @@ __device__ __forceinline__ int wave_rank(const LayoutArgs &a, const CountLds &s,
     return wave_rank_slow(a, tile_base, tt, k, e);
 }
 
-// Row of R bytes (0/1) for one token; 16-byte stores when R allows it.
+// Bytes (0/1) for the low 16 bits of `bits`, one byte per bit.
+__device__ __forceinline__ u32x4 rank_bytes16(uint64_t bits)
+{
+    uint32_t wd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t nib = (uint32_t)(bits >> (4 * j)) & 0xFu;
+        wd[j] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+    }
+    return u32x4{wd[0], wd[1], wd[2], wd[3]};
+}
+
+// Row of R bytes (0/1) for one token, byte by byte (R not a multiple of 16).
 __device__ void write_rank_row(uint8_t *dst, uint64_t rbits, int R)
 {
-    if ((R & 15) == 0) {
-        for (int r0 = 0; r0 < R; r0 += 16) {
-            uint32_t wd[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t nib = (uint32_t)(rbits >> (r0 + 4 * j)) & 0xFu;
-                wd[j] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
-            }
-            *reinterpret_cast<u32x4 *>(dst + r0) = u32x4{wd[0], wd[1], wd[2], wd[3]};
-        }
-    } else {
-        for (int r = 0; r < R; ++r)
-            dst[r] = (uint8_t)((rbits >> r) & 1ull);
-    }
+    for (int r = 0; r < R; ++r)
+        dst[r] = (uint8_t)((rbits >> r) & 1ull);
 }
 
 // Exclusive scan of in[0..n) into out[0..n] by one wave.
@@ -185,18 +269,97 @@ __device__ __forceinline__ int64_t channel_end(const LayoutArgs &a, int c)
     return min((int64_t)(c + 1) * span, (int64_t)a.T);
 }
 
+// Counts, offsets and totals from the totals in tot[0..E+R), using off as
+// scratch; one block.
+__device__ void write_totals(const LayoutArgs &a, const int *tot, int *off)
+{
+    const int tid = threadIdx.x;
+    if (tid < kWave)
+        wave_exclusive_scan(tot, a.E, off);
+    else if (tid < 2 * kWave)
+        wave_exclusive_scan(tot + a.E, a.R, off + a.E + 1);
+    __syncthreads();
+    for (int e = tid; e < a.E; e += blockDim.x)
+        a.num_tokens_per_expert[e] = tot[e];
+    for (int r = tid; r < a.R; r += blockDim.x)
+        a.num_tokens_per_rank[r] = tot[a.E + r];
+    for (int i = tid; i <= a.E; i += blockDim.x)
+        a.exp_off[i] = off[i];
+    for (int i = tid; i <= a.R; i += blockDim.x)
+        a.rank_off[i] = off[a.E + 1 + i];
+    if (tid == 0) {
+        a.totals[0] = off[a.E + 1 + a.R];
+        a.totals[1] = off[a.E];
+        if (a.totals_host_mapped) {
+            a.totals_host_mapped[0] = off[a.E + 1 + a.R];
+            a.totals_host_mapped[1] = off[a.E];
+        }
+    }
+}
+
 template <int KMAX>
-__global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(LayoutArgs a)
+__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const CountLds s = carve_count(lds, a.E, a.R);
+    const int ER = a.E + a.R;
+    int *agg = reinterpret_cast<int *>(lds + count_lds_bytes(a.E, a.R));
+    int *pre = agg + ER, *off = pre + ER;
+    __shared__ int s_ok;
+    __shared__ uint32_t s_tag;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int tile_base = blockIdx.x * kLayoutTile;
-    const int ntok = min(kLayoutTile, a.T - tile_base);
-    const int t = tile_base + tid;
 
+    if (a.ntiles == 0) {  // T = 0: zero counts and offsets, no tiles
+        for (int i = tid; i < ER; i += blockDim.x)
+            agg[i] = 0;
+        __syncthreads();
+        write_totals(a, agg, off);
+        if (a.channel_prefix)
+            for (int i = tid; i < a.R * a.C; i += blockDim.x)
+                a.channel_prefix[i] = 0;
+        return;
+    }
+
+    // Threads tid and tid + 256 both hold token tid of the tile: the first
+    // counts it, both share its slot writes; all share the look-back and the
+    // row writes (more waves than tokens per SIMD, to hide latency).
+    const int tile = blockIdx.x;
+    const int tile_base = tile * kLayoutTile;
+    const int ntok = min(kLayoutTile, a.T - tile_base);
+    const int tt0 = tid & (kLayoutTile - 1);
+    const bool counter = tid < kLayoutTile;
+    const int t = tile_base + tt0;
     int ek[KMAX];
-    load_row_experts<KMAX>(a, t, ek);
+    if (tile < a.ntiles)
+        load_row_experts<KMAX>(a, t, ek);
+    if (tid == 0) {
+        const unsigned long long v = atomicAdd(&a.hdr->calls, 1ull);
+        const uint32_t arrived = (uint32_t)v;
+        s_ok = arrived < gridDim.x;
+        s_tag = (uint32_t)(v >> 32) + 1u;
+        if (arrived == gridDim.x - 1)  // all blocks are in: open the next call
+            atomicAdd(&a.hdr->calls, (1ull << 32) - (unsigned long long)gridDim.x);
+    }
+
+    // The block after the last tile: the totals are the inclusive prefix
+    // past the last tile, found by the same look-back a tile does.
+    if (tile == a.ntiles) {
+        __syncthreads();
+        if (!s_ok) {
+            if (tid == 0)
+                flag_error(a.err, EPX_DEV_WORKSPACE);
+            return;
+        }
+        for (int c = tid; c < ER; c += blockDim.x) {
+            int p = 0;
+            if (!look_back(a.pub, ER, a.ntiles, a.ntiles - 1, c, s_tag, &p))
+                flag_error(a.err, EPX_DEV_WORKSPACE);
+            agg[c] = p;
+        }
+        __syncthreads();
+        write_totals(a, agg, off);
+        return;
+    }
     for (int i = tid; i < W * a.E; i += blockDim.x) {
         s.emask[i] = 0;
         s.ecnt[i] = 0;
@@ -212,7 +375,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(LayoutArgs a)
     int dup = 0, bad = 0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        const int e = ek[k];
+        const int e = counter ? ek[k] : -1;
         bad |= (e == -2);
         if (e < 0)
             continue;
@@ -222,25 +385,36 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(LayoutArgs a)
         atomicAdd(&s.ecnt[w * a.E + e], 1);
         rbits |= 1ull << (e / a.L);
     }
+    if (counter)
+        s.rb[tid] = rbits;
     if (bad)
         flag_error(a.err, EPX_DEV_BAD_ROUTE);
     for (uint64_t m = rbits; m; m &= m - 1) {
         const int r = __builtin_ctzll(m);
         atomicOr(reinterpret_cast<unsigned long long *>(&s.rmask[w * a.R + r]), bit);
     }
-    if (__any(dup) && lane == 0)
+    if (counter && __any(dup) && lane == 0)
         s.dupwave[w] = 1;
     __syncthreads();
+    const uint32_t tag = s_tag;
+    if (!s_ok) {  // the counter was not left by a previous call: give up
+        if (tid == 0)
+            flag_error(a.err, EPX_DEV_WORKSPACE);
+        return;
+    }
 
-    // wave prefixes inside the tile, and the tile's counts
-    int32_t *cnt = a.tile_cnt + (int64_t)blockIdx.x * (a.E + a.R);
+    // wave prefixes inside the tile and the tile's counts, published at
+    // once (tile 0's counts are already its inclusive prefix)
+    uint64_t *pub_row = a.pub + (int64_t)tile * ER;
+    const uint64_t hi = ((uint64_t)tag << 32) | (tile == 0 ? kInclusive : 0);
     for (int e = tid; e < a.E; e += blockDim.x) {
         int run = 0;
         for (int w2 = 0; w2 < W; ++w2) {
             s.wpre_e[w2 * a.E + e] = run;
             run += s.ecnt[w2 * a.E + e];
         }
-        cnt[e] = run;
+        agg[e] = run;
+        pub_store(pub_row + e, hi | (uint32_t)run);
     }
     for (int r = tid; r < a.R; r += blockDim.x) {
         int run = 0;
@@ -248,55 +422,120 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(LayoutArgs a)
             s.wpre_r[w2 * a.R + r] = run;
             run += __popcll(s.rmask[w2 * a.R + r]);
         }
-        cnt[a.E + r] = run;
+        agg[a.E + r] = run;
+        pub_store(pub_row + a.E + r, hi | (uint32_t)run);
+    }
+    // this tile's prefix, then its inclusive prefix for the tiles after it
+    for (int c = tid; c < ER; c += blockDim.x) {
+        int p = 0;
+        if (!look_back(a.pub, ER, tile, tile, c, tag, &p))
+            flag_error(a.err, EPX_DEV_WORKSPACE);
+        pre[c] = p;
+        if (tile > 0)
+            pub_store(pub_row + c, ((uint64_t)tag << 32) | kInclusive | (uint32_t)(p + agg[c]));
     }
     __syncthreads();
 
-    if (t < a.T) {
-        const uint64_t below = lanes_below(lane);
-        write_rank_row(a.is_token_in_rank + (int64_t)t * a.R, rbits, a.R);
-        // tile-local rank of t in each rank it goes to, else -1: the row is
-        // cleared first, then only the (at most K) ranks t goes to are set
-        int32_t *pir = a.pos_in_rank + (int64_t)t * a.R;
-        if ((a.R & 3) == 0) {
-            for (int r0 = 0; r0 < a.R; r0 += 4)
-                *reinterpret_cast<u32x4 *>(pir + r0) = u32x4{~0u, ~0u, ~0u, ~0u};
-        } else {
-            for (int r = 0; r < a.R; ++r)
-                pir[r] = -1;
+    // is_token_in_rank and pos_in_rank rows of the tile are contiguous:
+    // write them as one block, 16 bytes per thread per step
+    if ((a.R & 15) == 0) {
+        uint8_t *dst = a.is_token_in_rank + (int64_t)tile_base * a.R;
+        const int nq = a.R >> 4;
+        for (int q = tid; q < ntok * nq; q += blockDim.x) {
+            const int tt = q / nq, r0 = (q - tt * nq) * 16;
+            *reinterpret_cast<u32x4 *>(dst + (int64_t)q * 16) = rank_bytes16(s.rb[tt] >> r0);
         }
-        uint64_t m = rbits;
+    } else if (counter && t < a.T) {
+        write_rank_row(a.is_token_in_rank + (int64_t)t * a.R, rbits, a.R);
+    }
+    if (a.R >= 4 && (a.R & (a.R - 1)) == 0) {
+        // R/4 chunks per row, a power of two dividing the thread count, so a
+        // thread's ranks r0..r0+3 stay fixed: their prefixes and masks for
+        // each wave of tokens are read from LDS once
+        int32_t *dst = a.pos_in_rank + (int64_t)tile_base * a.R;
+        const int nq = a.R >> 2, qs = __builtin_ctz(nq);
+        const int r0 = (tid & (nq - 1)) * 4;
 #pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-            if (m) {
-                const int r = __builtin_ctzll(m);
-                m &= m - 1;
-                pir[r] = s.wpre_r[w * a.R + r] + __popcll(s.rmask[w * a.R + r] & below);
+        for (int ww = 0; ww < W; ++ww) {
+            int base[4];
+            uint64_t rm[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                base[j] = pre[a.E + r0 + j] + s.wpre_r[ww * a.R + r0 + j];
+                rm[j] = s.rmask[ww * a.R + r0 + j];
+            }
+            const int qend = min((ww + 1) * kWave, ntok) * nq;
+            for (int q = ww * kWave * nq + tid; q < qend; q += blockDim.x) {
+                const int tt = q >> qs;
+                const uint64_t rbt = s.rb[tt] >> r0, below = lanes_below(tt & 63);
+                int v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = ((rbt >> j) & 1ull) ? base[j] + __popcll(rm[j] & below) : -1;
+                *reinterpret_cast<u32x4 *>(dst + (int64_t)q * 4) =
+                    u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
             }
         }
-        // tile-local slot of each entry, else -1
+    } else if ((a.R & 3) == 0) {
+        int32_t *dst = a.pos_in_rank + (int64_t)tile_base * a.R;
+        const int nq = a.R >> 2;
+        for (int q = tid; q < ntok * nq; q += blockDim.x) {
+            const int tt = q / nq, r0 = (q - tt * nq) * 4;
+            const uint64_t rbt = s.rb[tt];
+            const int ww = tt >> 6;
+            const uint64_t below = lanes_below(tt & 63);
+            int v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = r0 + j;
+                v[j] = ((rbt >> r) & 1ull) ? pre[a.E + r] + s.wpre_r[ww * a.R + r] +
+                                                 __popcll(s.rmask[ww * a.R + r] & below)
+                                           : -1;
+            }
+            *reinterpret_cast<u32x4 *>(dst + (int64_t)q * 4) =
+                u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+        }
+    } else if (counter && t < a.T) {
+        const uint64_t below = lanes_below(lane);
+        int32_t *pir = a.pos_in_rank + (int64_t)t * a.R;
+        for (int r = 0; r < a.R; ++r)
+            pir[r] = ((rbits >> r) & 1ull) ? pre[a.E + r] + s.wpre_r[w * a.R + r] +
+                                                 __popcll(s.rmask[w * a.R + r] & below)
+                                           : -1;
+    }
+
+    if (t < a.T) {
+        // slot of each entry among the entries of its expert, else -1; the
+        // two threads of a token take half the entries each when K % 8 == 0
+        const int wt = tt0 >> 6;
+        const bool halves = (a.K & 7) == 0;
+        const int k_lo = halves ? (tid >> 8) * (a.K >> 1) : 0;
+        const int k_hi = halves ? k_lo + (a.K >> 1) : (counter ? a.K : 0);
         int32_t *sie = a.slot_in_expert + (int64_t)t * a.K;
         int v[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             const int e = ek[k];
-            v[k] = e >= 0 ? s.wpre_e[w * a.E + e] + wave_rank(a, s, tile_base, tid, k, e) : -1;
+            v[k] = (e >= 0 && k >= k_lo && k < k_hi)
+                       ? pre[e] + s.wpre_e[wt * a.E + e] + wave_rank(a, s, tile_base, tt0, k, e)
+                       : -1;
         }
         if ((a.K & 3) == 0) {
 #pragma unroll
             for (int k0 = 0; k0 < KMAX; k0 += 4)
-                if (k0 < a.K)
-                    *reinterpret_cast<u32x4 *>(sie + k0) = u32x4{
-                        (uint32_t)v[k0], (uint32_t)v[k0 + 1], (uint32_t)v[k0 + 2], (uint32_t)v[k0 + 3]};
+                if (k0 >= k_lo && k0 < k_hi)
+                    *reinterpret_cast<u32x4 *>(sie + k0) =
+                        u32x4{(uint32_t)v[k0], (uint32_t)v[k0 + 1], (uint32_t)v[k0 + 2],
+                              (uint32_t)v[k0 + 3]};
         } else {
 #pragma unroll
             for (int k = 0; k < KMAX; ++k)
-                if (k < a.K)
+                if (k >= k_lo && k < k_hi)
                     sie[k] = v[k];
         }
     }
 
-    // tile-local part of the channel columns this tile owns
+    // the channel columns whose last token lies in this tile
     if (a.channel_prefix) {
         Walk it(tid, blockDim.x, a.C);
         for (int i = tid; i < a.R * a.C; i += blockDim.x, it.next()) {
@@ -305,7 +544,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(LayoutArgs a)
             if (end <= tile_base || end > tile_base + ntok)
                 continue;
             const int n = (int)(end - tile_base);
-            int v = 0;
+            int v = pre[a.E + r];
             for (int w2 = 0; w2 < W; ++w2) {
                 const int lo = w2 * kWave;
                 if (n <= lo)
@@ -316,141 +555,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(LayoutArgs a)
             a.channel_prefix[i] = v;
         }
     }
-}
 
-template <int KMAX>
-__global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs a)
-{
-    extern __shared__ __attribute__((aligned(16))) int fin[];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int ER = a.E + a.R;
-    int *pre = fin, *tot = fin + ER, *off = fin + 2 * ER;
-    const int tile_base = b * kLayoutTile;
-    const int t = tile_base + tid;
-
-    // this token's experts and its tile-local rows go out first: nothing
-    // below the scan has to wait for memory except these loads
-    int ek[KMAX];
-    if (a.ntiles > 0)
-        load_row_experts<KMAX>(a, t, ek);
-    const bool vec_rows = (a.R & 3) == 0;
-    const int tl = min(t, a.T - 1);  // clamped: loads stay inside the arrays
-    int32_t *pir = a.pos_in_rank + (int64_t)tl * a.R;
-    int32_t *sie = a.slot_in_expert + (int64_t)tl * a.K;
-    u32x4 prow[EPX_MAX_RANKS / 4];
-    int srow[KMAX];
-    if (a.ntiles > 0) {
-        if (vec_rows) {
-#pragma unroll
-            for (int j = 0; j < EPX_MAX_RANKS / 4; ++j)
-                if (4 * j < a.R)
-                    prow[j] = *reinterpret_cast<const u32x4 *>(pir + 4 * j);
-        }
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            srow[k] = (k < a.K) ? sie[k] : -1;
-    }
-
-    // counts in earlier tiles and over all tiles, per expert then per rank;
-    // 16 loads in flight per thread, from clamped rows masked afterwards
-    for (int i = tid; i < ER; i += blockDim.x) {
-        int p = 0, q = 0;
-        for (int j0 = 0; j0 < a.ntiles; j0 += 16) {
-            int v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v[u] = a.tile_cnt[(int64_t)min(j0 + u, a.ntiles - 1) * ER + i];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int c = (j0 + u < a.ntiles) ? v[u] : 0;
-                p += (j0 + u < b) ? c : 0;
-                q += c;
-            }
-        }
-        pre[i] = p;
-        tot[i] = q;
-    }
-    __syncthreads();
-    if (tid < kWave)
-        wave_exclusive_scan(tot, a.E, off);
-    else if (tid < 2 * kWave)
-        wave_exclusive_scan(tot + a.E, a.R, off + a.E + 1);
-    __syncthreads();
-
-    if (b == 0) {
-        for (int e = tid; e < a.E; e += blockDim.x)
-            a.num_tokens_per_expert[e] = tot[e];
-        for (int r = tid; r < a.R; r += blockDim.x)
-            a.num_tokens_per_rank[r] = tot[a.E + r];
-        for (int i = tid; i <= a.E; i += blockDim.x)
-            a.exp_off[i] = off[i];
-        for (int i = tid; i <= a.R; i += blockDim.x)
-            a.rank_off[i] = off[a.E + 1 + i];
-        if (tid == 0) {
-            a.totals[0] = off[a.E + 1 + a.R];
-            a.totals[1] = off[a.E];
-            if (a.totals_host_mapped) {
-                a.totals_host_mapped[0] = off[a.E + 1 + a.R];
-                a.totals_host_mapped[1] = off[a.E];
-            }
-        }
-        if (a.ntiles == 0 && a.channel_prefix)
-            for (int i = tid; i < a.R * a.C; i += blockDim.x)
-                a.channel_prefix[i] = 0;
-    }
-    if (a.ntiles == 0)
-        return;
-
-    // add the tile prefix to the tile-local ranks (already in registers)
-    const int ntok = min(kLayoutTile, a.T - tile_base);
-    if (t < a.T) {
-        if (vec_rows) {
-#pragma unroll
-            for (int j = 0; j < EPX_MAX_RANKS / 4; ++j) {
-                const int r = 4 * j;
-                if (r < a.R) {
-                    u32x4 o = prow[j];
-                    o.x = (int)o.x >= 0 ? o.x + pre[a.E + r] : o.x;
-                    o.y = (int)o.y >= 0 ? o.y + pre[a.E + r + 1] : o.y;
-                    o.z = (int)o.z >= 0 ? o.z + pre[a.E + r + 2] : o.z;
-                    o.w = (int)o.w >= 0 ? o.w + pre[a.E + r + 3] : o.w;
-                    *reinterpret_cast<u32x4 *>(pir + r) = o;
-                }
-            }
-        } else {
-            for (int r = 0; r < a.R; ++r) {
-                const int v = pir[r];
-                if (v >= 0)
-                    pir[r] = v + pre[a.E + r];
-            }
-        }
-        if ((a.K & 3) == 0) {
-#pragma unroll
-            for (int k0 = 0; k0 < KMAX; k0 += 4) {
-                if (k0 < a.K) {
-                    int o[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        o[j] = ek[k0 + j] >= 0 ? srow[k0 + j] + pre[ek[k0 + j]] : srow[k0 + j];
-                    *reinterpret_cast<u32x4 *>(sie + k0) =
-                        u32x4{(uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]};
-                }
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (k < a.K && ek[k] >= 0)
-                    sie[k] = srow[k] + pre[ek[k]];
-        }
-    }
-    if (a.channel_prefix) {
-        Walk it(tid, blockDim.x, a.C);
-        for (int i = tid; i < a.R * a.C; i += blockDim.x, it.next()) {
-            const int64_t end = channel_end(a, it.col);
-            if (end > tile_base && end <= tile_base + ntok)
-                a.channel_prefix[i] += pre[a.E + it.row];
-        }
-    }
 }
 
 }  // namespace
@@ -458,21 +563,21 @@ __global__ __launch_bounds__(kLayoutTile) void layout_finalize_kernel(LayoutArgs
 size_t layout_workspace_bytes(int T, int E, int R)
 {
     const size_t ntiles = ((size_t)T + kLayoutTile - 1) / kLayoutTile;
-    return ntiles * (size_t)(E + R) * sizeof(int32_t);
+    if (ntiles == 0)
+        return 0;
+    return sizeof(LayoutHdr) + ntiles * (size_t)(E + R) * sizeof(uint64_t);
 }
 
 template <int KMAX>
 static void launch_layout_k(const LayoutArgs &a, hipStream_t stream)
 {
-    if (a.ntiles > 0)
-        hipLaunchKernelGGL((layout_count_kernel<KMAX>), dim3(a.ntiles), dim3(kLayoutTile),
-                           count_lds_bytes(a.E, a.R), stream, a);
-    hipLaunchKernelGGL((layout_finalize_kernel<KMAX>), dim3(a.ntiles > 0 ? a.ntiles : 1),
-                       dim3(kLayoutTile), finalize_lds_bytes(a.E, a.R), stream, a);
+    // the tiles, plus one block for the totals
+    hipLaunchKernelGGL((layout_kernel<KMAX>), dim3(a.ntiles > 0 ? a.ntiles + 1 : 1),
+                       dim3(kLayoutThreads), layout_lds_bytes(a.E, a.R), stream, a);
 }
 
 // The per-token top-k loops are unrolled to KMAX; the common K <= 8 gets a
-// small kernel (instruction fetch matters for these short, few-block kernels).
+// small kernel (instruction fetch matters for a short, few-block kernel).
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream)
 {
     if (a.K <= 8)

@@ -57,6 +57,8 @@ extern "C" {
 #define EPX_DEV_BAD_ROUTE 1   /* a top-k entry outside [-1, E) */
 #define EPX_DEV_OVERFLOW 2    /* a row index reached the caller's capacity */
 #define EPX_DEV_BAD_HANDLE 4  /* a combine handle row >= n_rows */
+#define EPX_DEV_WORKSPACE 8   /* the layout workspace was not zeroed before its
+                                 first use, or is shared by overlapping calls */
 
 /* Limits of this implementation */
 #define EPX_MAX_TOPK 32
@@ -75,7 +77,8 @@ int epx_create(epx_ctx **out, int device);
 int epx_destroy(epx_ctx *ctx);
 const char *epx_strerror(int code);
 
-/* Workspace bytes epx_get_dispatch_layout needs for (T, K, E, R) (host out).
+/* Workspace bytes epx_get_dispatch_layout needs for (T, K, E, R) (host out):
+ * a 128-byte head plus 8 bytes per (256-token tile, expert or rank).
  * [P2] "Buffer 与内存视角": the workspace is allocated up front, once. */
 int epx_workspace_size(int T, int K, int E, int R, size_t *bytes);
 
@@ -118,7 +121,14 @@ size_t epx_ll_size_hint(int max_tokens_per_rank, int h, int R, int E, int fp8);
  *      totals_host_mapped          optional host-pinned int32[2]
  *                                  (hipHostMalloc) that also receives totals;
  *                                  valid once the stream has been synchronised
- * ws:  device workspace of epx_workspace_size bytes (contents scratch). */
+ * ws:  device workspace of epx_workspace_size bytes (0 when T = 0): tile
+ *      tickets and the per-tile counts that later tiles read for their
+ *      prefix. Zero-fill it before its first use; every call leaves it
+ *      ready for the next one (also across graph replays), so it is
+ *      allocated and cleared once. Calls that share a workspace must not
+ *      overlap. A workspace found in another state sets EPX_DEV_WORKSPACE,
+ *      the call's outputs are not valid and the workspace must be
+ *      zero-filled again; no wait inside the kernel is unbounded. */
 int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int E,
                             int R, int C, int32_t *num_tokens_per_expert,
                             int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank,

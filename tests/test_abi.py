@@ -46,7 +46,7 @@ def test_library_is_gfx950_hip():
 def test_workspace_size(lib):
     n = ctypes.c_size_t()
     assert lib.epx_workspace_size(4096, 8, 256, 32, ctypes.byref(n)) == 0
-    assert n.value == 16 * (256 + 32) * 4           # 16 tiles of 256 tokens
+    assert n.value == 128 + 16 * (256 + 32) * 8     # head + 16 tiles of 256 tokens
     assert lib.epx_workspace_size(0, 8, 256, 32, ctypes.byref(n)) == 0
     assert n.value == 0
     assert lib.epx_workspace_size(10, 8, 256, 30, ctypes.byref(n)) == -1   # E % R

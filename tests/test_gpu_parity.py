@@ -69,6 +69,41 @@ def test_layout_edge_cases(kind, T, K, E, R, C, p_drop):
     _check_layout(topk, E, R, C)
 
 
+def test_layout_workspace_reuse_and_recovery():
+    """One workspace across calls of different sizes (each call leaves it
+    ready for the next); then a workspace in a state no call leaves (its
+    arrival count past the tiles) is flagged without any wait, and once it
+    is zero-filled again the next call is correct."""
+    import combine_get_dispatch_counts_amd as epx
+
+    E, R, K, C = 256, 32, 8, 7
+    ws = torch.zeros(epx.workspace_size(4096, K, E, R), dtype=torch.uint8, device="cuda")
+
+    def run_and_check(T, seed):
+        topk = synth.random_routing(T, K, E, seed=seed)
+        lay = epx.get_dispatch_layout(torch.from_numpy(topk).cuda(), E, R, C, workspace=ws)
+        flags = epx.get_error()
+        return topk, lay, flags
+
+    for i, T in enumerate([4096, 1000, 4096, 257, 3000, 1]):
+        say(f"layout workspace reuse call {i} T={T}")
+        topk, lay, flags = run_and_check(T, 100 + i)
+        assert flags == 0
+        o = oracle.layout(topk, E, R, C)
+        for k in LAYOUT_KEYS + ["channel_prefix"]:
+            _eq(host_bits(getattr(lay, k)), o[k], f"call {i} {k}")
+    say("layout workspace with its arrival count past the tiles")
+    ws[:4].view(torch.int32).fill_(1 << 20)
+    _, _, flags = run_and_check(2000, 7)
+    assert flags == 8, f"expected EPX_DEV_WORKSPACE, got {flags:#x}"
+    ws.zero_()
+    topk, lay, flags = run_and_check(2000, 8)
+    assert flags == 0
+    o = oracle.layout(topk, E, R, C)
+    for k in LAYOUT_KEYS + ["channel_prefix"]:
+        _eq(host_bits(getattr(lay, k)), o[k], f"after recovery {k}")
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_layout_workloads(cfg):
     inp = synth.make_inputs(cfg)
