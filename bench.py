@@ -13,6 +13,9 @@ step (each required input read once, each required output written once);
 ``ms_per_step`` is the wall time per step. ``roofline`` covers the dominant
 kernel (dispatch) timed with HIP events on its stream; ``cpu_baseline``
 times the CPU oracle (single thread) on the same workload.
+
+``python bench.py --summarize-profiles <folder>`` instead writes the
+profiles/ summaries from the rocprofv3 runs listed in PROFILE_RUNS.
 """
 from __future__ import annotations
 
@@ -232,7 +235,150 @@ def other_workloads(n=20):
     return out
 
 
+# ---------------------------------------------------------------- profiles
+# The rocprofv3 runs the summaries under profiles/ come from (each run from
+# /tmp with TMPDIR=/tmp, <R> the repository root, <P> the output folder):
+PROFILE_RUNS = {
+    "tr": "rocprofv3 --kernel-trace --stats --output-format csv -d <P>/tr -o run -- "
+          "python3 <R>/bench.py --steps 20 --warmup 5 --no-cpu-baseline --flush-mb 0 --other 0",
+    "tro": "rocprofv3 --kernel-trace --stats --output-format csv -d <P>/tro -o run -- "
+           "python3 <R>/bench.py --steps 2 --warmup 1 --no-cpu-baseline --flush-mb 0 --graph 0 "
+           "--other 1",
+    "pf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <P>/pf -o run -- "
+          "python3 <R>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --flush-mb 0 --graph 0 "
+          "--other 1 --calib-copy-mb 1024",
+    "pw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <P>/pw -o run -- "
+          "python3 <R>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --flush-mb 0 --graph 0 "
+          "--other 1 --calib-copy-mb 1024",
+}
+PREFILL_DISPATCH = ("dispatch_kernel<false, 14>", 4096 * 64)  # kernel, grid (threads)
+
+
+def _short_name(name: str) -> str:
+    for junk in ("void ", "epx::(anonymous namespace)::"):
+        name = name.replace(junk, "")
+    return name.split("(")[0] if name.startswith(("dispatch", "combine", "layout", "ll_", "fill")) \
+        else name
+
+
+def _read_csv(folder: str, suffix: str) -> list[dict]:
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {folder}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _durations(folder: str) -> dict:
+    """(kernel, grid threads) -> list of durations in us, from a kernel trace."""
+    out: dict = {}
+    for r in _read_csv(folder, "kernel_trace.csv"):
+        name = _short_name(r["Kernel_Name"])
+        if not name.startswith(("dispatch", "combine", "layout", "ll_", "fill")):
+            continue
+        key = (name, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        out.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
+def _counter(folder: str, counter: str) -> tuple[dict, float]:
+    """(kernel, grid) -> mean KiB per dispatch, and the calibration copy's KiB."""
+    acc: dict = {}
+    calib = []
+    for r in _read_csv(folder, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"])
+        if "copyBuffer" in r["Kernel_Name"]:
+            calib.append(v)
+            continue
+        name = _short_name(r["Kernel_Name"])
+        if not name.startswith(("dispatch", "combine", "layout", "ll_", "fill")):
+            continue
+        acc.setdefault((name, int(r["Grid_Size"])), []).append(v)
+    return {k: sum(v) / len(v) for k, v in acc.items()}, max(calib) if calib else 0.0
+
+
+def summarize_profiles(folder: str, calib_mb: int = 1024) -> None:
+    """Write the profiles/ summaries from the four rocprofv3 runs in `folder`
+    (subfolders tr, tro, pf, pw; see PROFILE_RUNS)."""
+    prof = os.path.join(ROOT, "profiles")
+    cmds = {k: v.replace("<R>", "<repo>").replace("<P>", "<out>") for k, v in PROFILE_RUNS.items()}
+
+    def table(durs: dict) -> list[str]:
+        total = sum(sum(v) for v in durs.values())
+        rows = ["| Kernel | Grid (threads) | Calls | Average (us) | Median (us) | Min (us) | Max (us) "
+                "| Share |", "|---|---|---|---|---|---|---|---|"]
+        for (name, grid), v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+            v = sorted(v)
+            rows.append(f"| `{name}` | {grid} | {len(v)} | {sum(v) / len(v):.2f} | "
+                        f"{v[len(v) // 2]:.2f} | {v[0]:.2f} | {v[-1]:.2f} | "
+                        f"{100 * sum(v) / total:.1f}% |")
+        return rows
+
+    head = ["Durations in microseconds from `run_kernel_trace.csv`, grouped by kernel and grid",
+            "size (which tells the workloads apart); calls cover warm-up, timed steps, the",
+            "back-to-back loops, graph replays and parity checks of the run.", ""]
+    d = _durations(os.path.join(folder, "tr"))
+    with open(os.path.join(prof, "prefill_T4096_kernel_stats.md"), "w") as f:
+        f.write("\n".join(["# Kernel trace: prefill workload (T=4096, h=7168, E=256, R=32, "
+                           "topk=8, bf16)", "", "```", cmds["tr"], "```", ""] + head
+                          + table(d)) + "\n")
+    d = _durations(os.path.join(folder, "tro"))
+    names = {4096 * 64: "prefill T=4096 bf16", 16384 * 64: "FP8 prefill T=16384",
+             8192 * 64: "skew T=8192 / decode rows", 128 * 64: "decode T=128"}
+    with open(os.path.join(prof, "all_workloads_kernel_stats.md"), "w") as f:
+        f.write("\n".join(["# Kernel trace: every benchmarked workload (prefill bf16, FP8 "
+                           "prefill, low-latency decode, skewed routing)", "", "```", cmds["tro"],
+                           "```", ""] + head + table(d)) + "\n")
+
+    fetch, cal_f = _counter(os.path.join(folder, "pf"), "FETCH_SIZE")
+    write, cal_w = _counter(os.path.join(folder, "pw"), "WRITE_SIZE")
+    kib = calib_mb * 1024.0
+    sf, sw = kib / cal_f, kib / cal_w
+    lines = ["# HBM traffic counters: every benchmarked workload", "",
+             "Two counter passes over the same command, each on its own:", "", "```",
+             cmds["pf"], cmds["pw"], "```", "",
+             f"`--calib-copy-mb {calib_mb}` makes the bench run one device-to-device copy of "
+             f"{calib_mb} MiB (`__amd_rocclr_copyBuffer`), which reads and writes exactly "
+             f"{kib:.0f} KiB. It reads back FETCH_SIZE = {cal_f:.2f} KiB and WRITE_SIZE = "
+             f"{cal_w:.2f} KiB, so the scale factors are **{sf:.4f}** (FETCH_SIZE) and "
+             f"**{sw:.4f}** (WRITE_SIZE). Values are KiB per dispatch, averaged over every "
+             "launch of the kernel at that grid size.", "",
+             "| Kernel | Grid (threads) | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled read (MB) "
+             "| scaled write (MB) | scaled total (MB) |", "|---|---|---|---|---|---|---|"]
+    for key in sorted(set(fetch) | set(write)):
+        fr, wr = fetch.get(key, 0.0), write.get(key, 0.0)
+        rd, wt = fr * sf * 1024 / 1e6, wr * sw * 1024 / 1e6
+        lines.append(f"| `{key[0]}` | {key[1]} | {fr:.1f} | {wr:.1f} | {rd:.1f} | {wt:.1f} | "
+                     f"{rd + wt:.1f} |")
+    with open(os.path.join(prof, "hbm_traffic_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    old = os.path.join(prof, "dispatch_prefill_T4096_counters.md")
+    if os.path.exists(old):
+        os.remove(old)
+
+    fr, wr = fetch[PREFILL_DISPATCH], write[PREFILL_DISPATCH]
+    rec = {"kernel": f"dispatch_kernel<bf16> ({PREFILL_DISPATCH[0]})",
+           "workload": "prefill T=4096 h=7168 E=256 R=32 topk=8 bf16",
+           "bytes_per_launch": round(fr * sf * 1024 + wr * sw * 1024),
+           "read_bytes": round(fr * sf * 1024), "write_bytes": round(wr * sw * 1024),
+           "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+           "source": "profiles/hbm_traffic_counters.md",
+           "kernel_source_sha256": kernel_source_digest()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(f"wrote the profiles/ summaries; dispatch traffic {rec['bytes_per_launch'] / 1e6:.1f} MB")
+
+
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(sys.argv[2])
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
