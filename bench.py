@@ -389,6 +389,8 @@ def main():
                     help="also time the FP8, low-latency and skewed workloads (reported beside the headline)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device copy of this many MB (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--ceilings", type=int, default=1,
+                    help="also time a 1 GiB device copy and fill (the same run's ceilings)")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="MALL flush size for the labelled cold-cache figure (0: skip)")
     args = ap.parse_args()
@@ -448,18 +450,23 @@ def main():
     assert epx.get_error() == 0
     n_rank, n_exp = (int(v) for v in lay.totals.cpu())
 
-    # timed region: K back-to-back steps, events around each kernel group
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: K back-to-back steps, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    assert epx.get_error() == 0
+
+    # per-phase split, from separate steps with events between the kernel groups
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     phase = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3
              for j, name in enumerate(["layout", "dispatch", "combine"])}
-    assert epx.get_error() == 0
 
     # the dominant kernel on its own: the same dispatch launched back to back
     # on the step's stream (it is idempotent), one event pair around them all
@@ -514,6 +521,17 @@ def main():
         cold_us = statistics.median(cold)
         del scratch
 
+    # copy and fill ceilings of this GPU in the same run (1 GiB each)
+    ceil = {}
+    if args.ceilings:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        b.copy_(a)
+        ceil["d2d_copy_gbs"] = round(2 * (1 << 30) / (_loop_us(lambda: b.copy_(a), 10) * 1e3), 1)
+        ceil["fill_gbs"] = round((1 << 30) / (_loop_us(lambda: a.fill_(3), 10) * 1e3), 1)
+        del a, b
+
     by = step_bytes(T, h, K, R, n_rank, n_exp)
     bmin = survey_bmin(T, h, K, R, n_rank, n_exp)
     gbs = bmin / (ms_per_step * 1e-3) / 1e9
@@ -558,6 +576,8 @@ def main():
         "b_flow_gbs": round(b_flow / (ms_per_step * 1e-3) / 1e9, 1),
         "phase_us": {k: round(v, 2) for k, v in phase.items()},
         "phase_gbs": {"dispatch": round(disp_gbs, 1), "combine": round(comb_gbs, 1)},
+        "ceilings": ceil or None,
+        "frac_of_copy_ceiling": round(gbs / ceil["d2d_copy_gbs"], 4) if ceil else None,
         "cold_cache_us_per_layer": round(cold_us, 2) if cold_us else None,
         "graph_us_per_layer": round(graph_us, 2) if graph_us else None,
         "dispatch_kernel_us": round(dispatch_us, 2),
