@@ -69,6 +69,10 @@ def lib() -> ctypes.CDLL:
         L.orc_ll_dispatch.restype = i32
         L.orc_combine.argtypes = [P, i64, i32, P, P, i32, i32, P]
         L.orc_combine.restype = i32
+        L.orc_combine_partial.argtypes = [P, i64, i32, P, P, P, i64, P, i32, i32, P]
+        L.orc_combine_partial.restype = i32
+        L.orc_combine_final.argtypes = [P, i64, i32, P, P, i32, i32, P]
+        L.orc_combine_final.restype = i32
         _lib = L
     return _lib
 
@@ -234,3 +238,37 @@ def combine(expert_out: np.ndarray, topk_w: np.ndarray, pos: np.ndarray) -> np.n
     rc = lib().orc_combine(_p(expert_out), n_rows, h, _p(topk_w), _p(pos), T, K, _p(out))
     _check(rc, "combine")
     return out
+
+
+def combine_partial(expert_out: np.ndarray, send_src: np.ndarray, send_topk_idx: np.ndarray,
+                    send_topk_w: np.ndarray, pos_exp: np.ndarray) -> np.ndarray:
+    """Stage 1 of the two-stage combine: one bf16 partial row per rank-major
+    row (the rows of send_src)."""
+    expert_out = np.ascontiguousarray(expert_out, dtype=np.uint16)
+    send_src = np.ascontiguousarray(send_src, dtype=np.int32)
+    send_topk_idx = np.ascontiguousarray(send_topk_idx, dtype=np.int64)
+    send_topk_w = np.ascontiguousarray(send_topk_w, dtype=np.float32)
+    pos_exp = np.ascontiguousarray(pos_exp, dtype=np.int32)
+    n_rows, h = expert_out.shape
+    T, K = pos_exp.shape
+    n_send = send_src.shape[0]
+    out = np.empty((n_send, h), np.uint16)
+    rc = lib().orc_combine_partial(_p(expert_out), n_rows, h, _p(send_src), _p(send_topk_idx),
+                                   _p(send_topk_w), n_send, _p(pos_exp), T, K, _p(out))
+    _check(rc, "combine_partial")
+    return out
+
+
+def combine_final(partial: np.ndarray, rank_off: np.ndarray, pos_in_rank: np.ndarray) -> np.ndarray:
+    """Stage 2: each token's partial rows summed over ranks ascending."""
+    partial = np.ascontiguousarray(partial, dtype=np.uint16)
+    rank_off = np.ascontiguousarray(rank_off, dtype=np.int32)
+    pos_in_rank = np.ascontiguousarray(pos_in_rank, dtype=np.int32)
+    n_send, h = partial.shape
+    T, R = pos_in_rank.shape
+    out = np.empty((T, h), np.uint16)
+    rc = lib().orc_combine_final(_p(partial), n_send, h, _p(rank_off), _p(pos_in_rank), T, R,
+                                 _p(out))
+    _check(rc, "combine_final")
+    return out
+

@@ -507,3 +507,89 @@ int orc_combine(const uint16_t *expert_out, int64_t n_rows, int h,
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Two-stage combine                                                   */
+/* ------------------------------------------------------------------ */
+
+/* [P2] "DeepEP v2": combine sends a rank-level partial result back to the
+ * source, because one source token may get outputs from several experts of
+ * the same rank; the rank reduces them first, and the source's epilogue
+ * reduces over the destination ranks. Readings: the partial travels in
+ * bf16 (combine stays BF16, [P1] "低延迟模式"), made by the same fp32 fma
+ * chain as the one-stage combine (k ascending, from +0.0f) over the entries
+ * of the row's rank; the final sum adds a token's partials in ascending
+ * rank order in fp32 from +0.0f (the weights are already applied) and
+ * rounds to bf16 nearest even.
+ *
+ * Stage 1, per rank-major row i (the send-buffer layout, token send_src[i]):
+ * partial[i,c] = bf16_rne(fma chain over k with send_topk_idx[i,k] >= 0 of
+ * send_topk_w[i,k] * expert_out[pos_exp[t,k], c]). */
+int orc_combine_partial(const uint16_t *expert_out, int64_t n_rows, int h,
+                        const int32_t *send_src, const int64_t *send_topk_idx,
+                        const float *send_topk_w, int64_t n_send,
+                        const int32_t *pos_exp, int T, int K, uint16_t *partial)
+{
+    if (T < 0 || K < 1 || h < 1 || n_rows < 0 || n_send < 0)
+        return ORC_EINVAL;
+    for (int64_t i = 0; i < n_send; ++i) {
+        const int32_t t = send_src[i];
+        if (t < 0 || t >= T)
+            return ORC_EROUTE;
+        for (int k = 0; k < K; ++k) {
+            if (send_topk_idx[(size_t)i * K + k] < 0)
+                continue;
+            const int32_t p = pos_exp[(size_t)t * K + k];
+            if (p < 0 || p >= n_rows)
+                return ORC_EROUTE;
+        }
+    }
+    for (int64_t i = 0; i < n_send; ++i) {
+        const int32_t t = send_src[i];
+        for (int c = 0; c < h; ++c) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                if (send_topk_idx[(size_t)i * K + k] < 0)
+                    continue;
+                const int32_t p = pos_exp[(size_t)t * K + k];
+                const float y = orc_bf16_to_f32(expert_out[(size_t)p * h + c]);
+                acc = fmaf(send_topk_w[(size_t)i * K + k], y, acc);
+            }
+            partial[(size_t)i * h + c] = orc_bf16_rne(acc);
+        }
+    }
+    return ORC_OK;
+}
+
+/* Stage 2, per source token t: out[t,c] = bf16_rne(sum over ranks r
+ * ascending with pos_in_rank[t,r] >= 0 of partial[rank_off[r] +
+ * pos_in_rank[t,r], c]), fp32 adds from +0.0f. */
+int orc_combine_final(const uint16_t *partial, int64_t n_send, int h,
+                      const int32_t *rank_off, const int32_t *pos_in_rank, int T, int R,
+                      uint16_t *out)
+{
+    if (T < 0 || R < 1 || h < 1 || n_send < 0)
+        return ORC_EINVAL;
+    for (size_t i = 0; i < (size_t)T * R; ++i) {
+        if (pos_in_rank[i] < 0)
+            continue;
+        const int64_t row = (int64_t)rank_off[i % R] + pos_in_rank[i];
+        if (row >= n_send)
+            return ORC_EROUTE;
+    }
+    for (int t = 0; t < T; ++t) {
+        for (int c = 0; c < h; ++c) {
+            float acc = 0.0f;
+            for (int r = 0; r < R; ++r) {
+                const int32_t p = pos_in_rank[(size_t)t * R + r];
+                if (p < 0)
+                    continue;
+                const int64_t row = (int64_t)rank_off[r] + p;
+                acc = acc + orc_bf16_to_f32(partial[(size_t)row * h + c]);
+            }
+            out[(size_t)t * h + c] = orc_bf16_rne(acc);
+        }
+    }
+    return ORC_OK;
+}
+

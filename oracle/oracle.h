@@ -103,6 +103,21 @@ int orc_combine(const uint16_t *expert_out, int64_t n_rows, int h,
                 const float *topk_w, const int32_t *pos, int T, int K,
                 uint16_t *out);
 
+/* Two-stage combine ([P2] "DeepEP v2": a rank-level partial reduce, then a
+ * final reduce over destination ranks at the source).
+ * Stage 1: partial[i,c] = bf16_rne(fma chain, k ascending from +0.0f, over
+ * k with send_topk_idx[i,k] >= 0, of send_topk_w[i,k] *
+ * expert_out[pos_exp[send_src[i],k], c]) for each rank-major row i.
+ * Stage 2: out[t,c] = bf16_rne(fp32 sum from +0.0f, ranks ascending, over r
+ * with pos_in_rank[t,r] >= 0, of partial[rank_off[r] + pos_in_rank[t,r], c]). */
+int orc_combine_partial(const uint16_t *expert_out, int64_t n_rows, int h,
+                        const int32_t *send_src, const int64_t *send_topk_idx,
+                        const float *send_topk_w, int64_t n_send,
+                        const int32_t *pos_exp, int T, int K, uint16_t *partial);
+int orc_combine_final(const uint16_t *partial, int64_t n_send, int h,
+                      const int32_t *rank_off, const int32_t *pos_in_rank, int T, int R,
+                      uint16_t *out);
+
 #ifdef __cplusplus
 }
 #endif
