@@ -128,9 +128,10 @@ def _loop_us(fn, n):
 
 
 def other_workloads(n=20):
-    """The FP8 and low-latency rows on their own workloads: per-kernel time,
-    compulsory GB/s and fraction of the 8 TB/s HBM peak. Not the headline
-    figure (that is the prefill step above); reported beside it."""
+    """The FP8, low-latency, skewed and two-stage-combine rows on their own
+    workloads: per-kernel time, compulsory GB/s and fraction of the 8 TB/s
+    HBM peak. Not the headline figure (that is the prefill step above);
+    reported beside it."""
     import numpy as np
     import torch
 
@@ -174,6 +175,35 @@ def other_workloads(n=20):
         "dispatch_fp8": rec(d_us, d_bytes), "combine": rec(c_us, c_bytes),
         "step_us": round(lay_us + d_us + c_us, 2)}
     del x, tk, w, ws, lay, bufs, y, comb, d
+    torch.cuda.empty_cache()
+
+    # two-stage combine on the prefill workload: T=4096, h=7168, E=256, R=32
+    inp = synth.make_inputs(3)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    tk = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    ws = torch.zeros(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    lay = epx.alloc_layout(T, K, E, R, None, dev)
+    bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, False, dev)
+    epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay)
+    n_rank, n_exp = (int(v) for v in lay.totals.cpu())
+    d = epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs)
+    y = synth.expert_outputs(T * K, h, seed=29, device="cuda")
+    part = torch.empty((T * min(K, R), h), dtype=torch.bfloat16, device=dev)
+    comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    p_us = _loop_us(lambda: epx.combine_partial(y, d, out=part), n)
+    f_us = _loop_us(lambda: epx.combine_final(part, lay, out=comb), n)
+    assert epx.get_error() == 0
+    p_bytes = n_exp * 2 * h + 4 * n_rank + 12 * n_rank * K + 4 * T * K + n_rank * 2 * h
+    f_bytes = n_rank * 2 * h + 4 * T * R + T * 2 * h
+    out["two_stage_combine_prefill"] = {
+        "workload": f"T={T} h={h} E={E} R={R} topk={K}, bf16: rank-level partial rows "
+                    "then the reduce over ranks",
+        "partial": rec(p_us, p_bytes), "final": rec(f_us, f_bytes),
+        "total_us": round(p_us + f_us, 2)}
+    del x, tk, w, ws, lay, bufs, d, y, part, comb
     torch.cuda.empty_cache()
 
     # decode, low-latency: T=128, h=7168, E=256, R=32, topk=8, cap=128, FP8

@@ -17,6 +17,8 @@ from .api import (  # noqa: E402
     alloc_layout,
     alloc_ll,
     combine,
+    combine_final,
+    combine_partial,
     dispatch,
     get_dispatch_layout,
     get_error,
@@ -28,5 +30,6 @@ from .api import (  # noqa: E402
 )
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
-           "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
-           "ll_reset", "alloc_ll", "ll_dispatch"]
+           "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
+           "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
+           "ll_dispatch"]

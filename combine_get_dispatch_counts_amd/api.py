@@ -255,6 +255,45 @@ def combine(expert_out: torch.Tensor, pos: torch.Tensor, topk_weights: torch.Ten
     return out
 
 
+def combine_partial(expert_out: torch.Tensor, dispatched: Dispatched,
+                    out: torch.Tensor | None = None,
+                    num_rows: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage 1 of the two-stage combine: one bf16 partial row per rank-major
+    row of ``dispatched`` (its rank's experts reduced with the token's
+    weights). Rows past the layout's send-row total are not written."""
+    _need(expert_out, torch.bfloat16, "expert_out", 2)
+    dev = expert_out.device
+    d = dispatched
+    cap, K = d.send_topk_idx.shape
+    T = d.pos_exp.shape[0]
+    h = expert_out.shape[1]
+    if out is None:
+        out = torch.empty((cap, h), dtype=torch.bfloat16, device=dev)
+    if num_rows is None:
+        num_rows = d.layout.totals[:1]
+    rc = _lib.load().epx_combine_partial(
+        _ctx(dev), _p(expert_out), expert_out.shape[0], h, _p(d.send_src), _p(d.send_topk_idx),
+        _p(d.send_topk_w), _p(d.pos_exp), T, K, cap, _p(num_rows), _p(out), _stream(dev))
+    check(rc, "epx_combine_partial")
+    return out
+
+
+def combine_final(partial: torch.Tensor, layout: Layout,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage 2: each token's partial rows summed in rank order (fp32) into bf16."""
+    _need(partial, torch.bfloat16, "partial", 2)
+    dev = partial.device
+    T, R = layout.pos_in_rank.shape
+    h = partial.shape[1]
+    if out is None:
+        out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    rc = _lib.load().epx_combine_final(_ctx(dev), _p(partial), partial.shape[0], h,
+                                       _p(layout.rank_off), _p(layout.pos_in_rank), T, R, _p(out),
+                                       _stream(dev))
+    check(rc, "epx_combine_final")
+    return out
+
+
 def ll_reset(ll_count: torch.Tensor) -> None:
     _need(ll_count, torch.int32, "ll_count")
     dev = ll_count.device
@@ -307,6 +346,6 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
 
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
-           "scale_stride",
-           "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch", "dispatch", "combine",
-           "ll_reset", "alloc_ll", "ll_dispatch"]
+           "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
+           "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
+           "ll_dispatch"]

@@ -5,6 +5,12 @@
 // where the outputs are reduced. [P1] "事件驱动 EP 内核的调度策略与零拷贝通信",
 // "低延迟模式：固定缓冲区与信号槽机制": combine stays in BF16.
 //
+// The two-stage form ([P2] "DeepEP v2": the destination rank reduces its own
+// experts' outputs for a token into one rank-level partial result, the
+// source reduces over ranks) uses the same reduction twice: stage 1 per
+// rank-major row over that rank's entries, stage 2 per token over its
+// partial rows in rank order.
+//
 // Many small blocks: block (t, part) is one wave that owns 64 consecutive
 // 16-byte column vectors of token t's output row (h = 7168 gives 14 blocks
 // per token). Lane k < K loads the handle row and weight of entry k; the
@@ -19,14 +25,94 @@
 namespace epx {
 namespace {
 
-constexpr int kBatch = 8;  // row loads in flight per lane
+// Fold the rows named by the lanes into fp32 columns: lane j holds row p
+// (-1 = skip) and weight w of entry j; entries are taken in lane order,
+// acc = fmaf(w, y[p], acc) from +0.0f. The wave covers P slices of 64
+// 16-byte column vectors, slice q being vectors (part*P + q)*64 + lane, and
+// keeps B entries x P vectors of loads in flight per lane; the bf16 result
+// goes to out_row.
+template <int P, int B>
+__device__ __forceinline__ void reduce_rows(const uint16_t *y, int h, int p, float w, int part,
+                                            uint16_t *out_row)
+{
+    const int lane = threadIdx.x;
+    const int nvec = h >> 3;
+    uint64_t todo = uniform64(__ballot(p >= 0));  // valid entries, lane order
+    const size_t row_bytes = (size_t)h * 2;
+    int v[P];
+    bool live[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        v[q] = (part * P + q) * kWave + lane;
+        live[q] = v[q] < nvec;
+    }
+    const char *ybase = reinterpret_cast<const char *>(y);
+
+    float acc[P][8];
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[q][i] = 0.0f;
+    while (todo) {
+        u32x4 yv[B][P];
+        float wk[B];
+        bool use[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            use[j] = todo != 0;
+            wk[j] = 0.0f;
+            int row = -1;
+            if (use[j]) {
+                const int k = __builtin_ctzll(todo);
+                todo &= todo - 1;
+                row = __builtin_amdgcn_readlane(p, k);
+                wk[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+            }
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+                yv[j][q] = (use[j] && live[q] && row >= 0)
+                               ? load16_stream(ybase + (size_t)row * row_bytes + (size_t)v[q] * 16)
+                               : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (use[j]) {
+#pragma unroll
+                for (int q = 0; q < P; ++q) {
+                    const uint32_t e[4] = {yv[j][q].x, yv[j][q].y, yv[j][q].z, yv[j][q].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[q][2 * i] = __builtin_fmaf(wk[j], bf16_lo(e[i]), acc[q][2 * i]);
+                        acc[q][2 * i + 1] =
+                            __builtin_fmaf(wk[j], bf16_hi(e[i]), acc[q][2 * i + 1]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        if (live[q]) {
+            u32x4 o;
+            o.x = f32_to_bf16(acc[q][0]) | (f32_to_bf16(acc[q][1]) << 16);
+            o.y = f32_to_bf16(acc[q][2]) | (f32_to_bf16(acc[q][3]) << 16);
+            o.z = f32_to_bf16(acc[q][4]) | (f32_to_bf16(acc[q][5]) << 16);
+            o.w = f32_to_bf16(acc[q][6]) | (f32_to_bf16(acc[q][7]) << 16);
+            store16_stream(out_row + (size_t)v[q] * 8, o);
+        }
+    }
+}
+
+// Slices per wave and entries per load batch of each kernel.
+constexpr int kCombP = 1, kCombB = 8;        // one-stage: K entries per token
+constexpr int kPartP = 4, kPartB = 2;        // stage 1: about K/R entries per row
+constexpr int kFinalP = 1, kFinalB = 8;      // stage 2: up to R partial rows per token
 
 __global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a, int split)
 {
     const int t = blockIdx.x / split, part = blockIdx.x - t * split;
     const int lane = threadIdx.x;
-    const int nvec = a.h >> 3;
-    const int v = part * kWave + lane;
     const int64_t tk = (int64_t)t * a.K;
     int p = -1;
     float w = 0.0f;
@@ -39,66 +125,101 @@ __global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a, int split
             p = -1;
         }
     }
-    uint64_t todo = uniform64(__ballot(p >= 0));  // valid entries, k order
-    const size_t row_bytes = (size_t)a.h * 2;
-    const char *ycol = reinterpret_cast<const char *>(a.y) + (size_t)v * 16;
-    const bool live = v < nvec;
+    reduce_rows<kCombP, kCombB>(a.y, a.h, p, w, part, a.out + (size_t)t * a.h);
+}
 
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        acc[i] = 0.0f;
-    while (todo) {
-        u32x4 y[kBatch];
-        float wk[kBatch];
-        bool use[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            use[j] = todo != 0;
-            y[j] = u32x4{0u, 0u, 0u, 0u};
-            wk[j] = 0.0f;
-            if (use[j]) {
-                const int k = __builtin_ctzll(todo);
-                todo &= todo - 1;
-                const int row = __builtin_amdgcn_readlane(p, k);
-                wk[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
-                if (live && row >= 0)
-                    y[j] = load16_stream(ycol + (size_t)row * row_bytes);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            if (use[j]) {
-                const uint32_t q[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] = __builtin_fmaf(wk[j], bf16_lo(q[i]), acc[2 * i]);
-                    acc[2 * i + 1] = __builtin_fmaf(wk[j], bf16_hi(q[i]), acc[2 * i + 1]);
-                }
+// Stage 1 of the two-stage combine: rank-major row i (token send_src[i])
+// reduces the entries of its own rank (send_topk_idx >= 0), whose expert
+// rows the token's handle pos_exp names.
+__global__ __launch_bounds__(kWave) void combine_partial_kernel(PartialArgs a, int split)
+{
+    const int64_t i = blockIdx.x / split;
+    const int part = (int)(blockIdx.x - i * split);
+    if (a.num_rows && i >= *a.num_rows)
+        return;
+    const int lane = threadIdx.x;
+    const int t = a.send_src[i];
+    const bool t_ok = t >= 0 && t < a.T;
+    if (!t_ok && lane == 0 && part == 0)
+        flag_error(a.err, EPX_DEV_BAD_HANDLE);
+    int p = -1;
+    float w = 0.0f;
+    if (t_ok && lane < a.K) {
+        const int64_t idx = a.send_topk_idx[i * a.K + lane];
+        w = a.send_topk_w[i * a.K + lane];
+        if (idx >= 0) {
+            p = a.pos_exp[(int64_t)t * a.K + lane];
+            if (p >= a.n_rows) {
+                if (part == 0)
+                    flag_error(a.err, EPX_DEV_BAD_HANDLE);
+                p = -1;
             }
         }
     }
-    if (live) {
-        u32x4 o;
-        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-        o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-        o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-        store16_stream(a.out + (size_t)t * a.h + (size_t)v * 8, o);
+    reduce_rows<kPartP, kPartB>(a.y, a.h, p, w, part, a.partial + (size_t)i * a.h);
+}
+
+// Stage 2: token t adds its partial rows, one per rank it went to, in rank
+// order (weight 1: fmaf(1, y, acc) rounds exactly like acc + y).
+__global__ __launch_bounds__(kWave) void combine_final_kernel(FinalArgs a, int split)
+{
+    const int t = blockIdx.x / split, part = blockIdx.x - t * split;
+    const int lane = threadIdx.x;
+    int p = -1;
+    if (lane < a.R) {
+        const int32_t pr = a.pos_in_rank[(int64_t)t * a.R + lane];
+        if (pr >= 0) {
+            const int64_t row = (int64_t)a.rank_off[lane] + pr;
+            if (row < a.n_rows) {
+                p = (int)row;
+            } else if (part == 0) {
+                flag_error(a.err, EPX_DEV_BAD_HANDLE);
+            }
+        }
     }
+    reduce_rows<kFinalP, kFinalB>(a.partial, a.h, p, 1.0f, part, a.out + (size_t)t * a.h);
 }
 
 }  // namespace
+
+// Waves per output row when each covers P slices of 64 column vectors.
+static int combine_split(int h, int P) { return ((h >> 3) + P * kWave - 1) / (P * kWave); }
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream)
 {
     if (a.T == 0)
         return hipSuccess;
-    const int split = ((a.h >> 3) + kWave - 1) / kWave;
+    const int split = combine_split(a.h, kCombP);
     const int64_t blocks = (int64_t)a.T * split;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(kWave), 0, stream, a, split);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_partial(const PartialArgs &a, hipStream_t stream)
+{
+    if (a.cap_rows == 0)
+        return hipSuccess;
+    const int split = combine_split(a.h, kPartP);
+    const int64_t blocks = a.cap_rows * split;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_partial_kernel, dim3((unsigned)blocks), dim3(kWave), 0, stream, a,
+                       split);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_final(const FinalArgs &a, hipStream_t stream)
+{
+    if (a.T == 0)
+        return hipSuccess;
+    const int split = combine_split(a.h, kFinalP);
+    const int64_t blocks = (int64_t)a.T * split;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_final_kernel, dim3((unsigned)blocks), dim3(kWave), 0, stream, a,
+                       split);
     return hipGetLastError();
 }
 

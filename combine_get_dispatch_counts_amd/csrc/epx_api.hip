@@ -256,6 +256,59 @@ int epx_combine(epx_ctx *ctx, const uint16_t *expert_out, int64_t n_rows, int h,
     return launched(epx::launch_combine(a, stream));
 }
 
+int epx_combine_partial(epx_ctx *ctx, const uint16_t *expert_out, int64_t n_rows, int h,
+                        const int32_t *send_src, const int64_t *send_topk_idx,
+                        const float *send_topk_w, const int32_t *pos_exp, int T, int K,
+                        int64_t send_cap_rows, const int32_t *num_send_rows, uint16_t *partial,
+                        hipStream_t stream)
+{
+    int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if (T < 0 || K < 1 || K > EPX_MAX_TOPK || n_rows < 0 || send_cap_rows < 0 ||
+        (int64_t)T * K > INT32_MAX || send_cap_rows > INT32_MAX)
+        return EPX_EINVAL;
+    if ((rc = check_hidden(h, 0)) != EPX_OK)
+        return rc;
+    if (send_cap_rows > 0) {
+        if (!send_src || !send_topk_idx || !send_topk_w || !partial || (T > 0 && !pos_exp) ||
+            (n_rows > 0 && !expert_out))
+            return EPX_EINVAL;
+        if (!aligned16(partial) || !aligned16(expert_out))
+            return EPX_EINVAL;
+    }
+    epx::PartialArgs a{};
+    a.y = expert_out; a.n_rows = n_rows; a.h = h; a.T = T; a.K = K;
+    a.send_src = send_src; a.send_topk_idx = send_topk_idx; a.send_topk_w = send_topk_w;
+    a.pos_exp = pos_exp; a.cap_rows = send_cap_rows; a.num_rows = num_send_rows;
+    a.partial = partial; a.err = ctx->d_err;
+    return launched(epx::launch_combine_partial(a, stream));
+}
+
+int epx_combine_final(epx_ctx *ctx, const uint16_t *partial, int64_t n_partial_rows, int h,
+                      const int32_t *rank_off, const int32_t *pos_in_rank, int T, int R,
+                      uint16_t *out, hipStream_t stream)
+{
+    int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if (T < 0 || R < 1 || R > EPX_MAX_RANKS || n_partial_rows < 0 ||
+        n_partial_rows > INT32_MAX)
+        return EPX_EINVAL;
+    if ((rc = check_hidden(h, 0)) != EPX_OK)
+        return rc;
+    if (T > 0) {
+        if (!rank_off || !pos_in_rank || !out || (n_partial_rows > 0 && !partial))
+            return EPX_EINVAL;
+        if (!aligned16(out) || !aligned16(partial))
+            return EPX_EINVAL;
+    }
+    epx::FinalArgs a{};
+    a.partial = partial; a.n_rows = n_partial_rows; a.h = h; a.T = T; a.R = R;
+    a.rank_off = rank_off; a.pos_in_rank = pos_in_rank; a.out = out; a.err = ctx->d_err;
+    return launched(epx::launch_combine_final(a, stream));
+}
+
 int epx_ll_reset(epx_ctx *ctx, int32_t *ll_count, int64_t n, hipStream_t stream)
 {
     const int rc = check_ctx(ctx);

@@ -97,4 +97,30 @@ struct CombineArgs {
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
+struct PartialArgs {
+    const uint16_t *y;  // expert outputs [n_rows, h]
+    int64_t n_rows;
+    int h, T, K;
+    const int32_t *send_src;
+    const int64_t *send_topk_idx;
+    const float *send_topk_w;
+    const int32_t *pos_exp;
+    int64_t cap_rows;         // rank-major rows launched
+    const int32_t *num_rows;  // device row count, or null (all cap_rows)
+    uint16_t *partial;        // [cap_rows, h]
+    int *err;
+};
+
+struct FinalArgs {
+    const uint16_t *partial;  // [n_rows, h]
+    int64_t n_rows;
+    int h, T, R;
+    const int32_t *rank_off, *pos_in_rank;
+    uint16_t *out;
+    int *err;
+};
+
+hipError_t launch_combine_partial(const PartialArgs &a, hipStream_t stream);
+hipError_t launch_combine_final(const FinalArgs &a, hipStream_t stream);
+
 }  // namespace epx

@@ -191,6 +191,42 @@ int epx_combine(epx_ctx *ctx, const uint16_t *expert_out, int64_t n_rows, int h,
                 const float *topk_w, const int32_t *pos, int T, int K, uint16_t *out,
                 hipStream_t stream);
 
+/* Two-stage combine, stage 1: a rank-level partial result per rank-major
+ * row. [P2] "DeepEP v2": combine returns a rank-level partial result -- a
+ * token may get outputs from several experts of one rank, which that rank
+ * reduces first -- and the source's epilogue reduces over the destination
+ * ranks (stage 2, epx_combine_final).
+ * In:  expert_out [n_rows, h] bf16, expert-major (the rows recv_x held);
+ *      from epx_dispatch: send_src [send_cap_rows], send_topk_idx
+ *      [send_cap_rows, K] (local expert index, or -1 for an entry on
+ *      another rank), send_topk_w [send_cap_rows, K], pos_exp [T, K];
+ *      num_send_rows: device int32 with the number of rank-major rows (the
+ *      layout's totals[0]), or NULL if all send_cap_rows rows are in use.
+ * Out: partial [send_cap_rows, h] bf16: row i < rows holds, per column, the
+ *      fp32 chain acc = fmaf(send_topk_w[i,k], expert_out[pos_exp[t,k]],
+ *      acc) over k ascending with send_topk_idx[i,k] >= 0, from +0.0f,
+ *      t = send_src[i], rounded to bf16 nearest even (the bf16 a rank would
+ *      send back). Rows past the count are not written. A send_src outside
+ *      [0, T) (its row becomes +0) or a handle row >= n_rows (the entry is
+ *      skipped) sets EPX_DEV_BAD_HANDLE. */
+int epx_combine_partial(epx_ctx *ctx, const uint16_t *expert_out, int64_t n_rows, int h,
+                        const int32_t *send_src, const int64_t *send_topk_idx,
+                        const float *send_topk_w, const int32_t *pos_exp, int T, int K,
+                        int64_t send_cap_rows, const int32_t *num_send_rows,
+                        uint16_t *partial, hipStream_t stream);
+
+/* Two-stage combine, stage 2 at the source. [P2] "DeepEP v2" (the epilogue
+ * reduces over the destination ranks).
+ * In:  partial [n_partial_rows, h] bf16 from epx_combine_partial; the
+ *      layout outputs rank_off [R+1] and pos_in_rank [T, R].
+ * Out: out [T, h] bf16: per column, acc = +0.0f, then acc = acc +
+ *      partial[rank_off[r] + pos_in_rank[t,r]] for r ascending with
+ *      pos_in_rank[t,r] >= 0 (fp32), rounded to bf16 nearest even. A row
+ *      index >= n_partial_rows sets EPX_DEV_BAD_HANDLE and is skipped. */
+int epx_combine_final(epx_ctx *ctx, const uint16_t *partial, int64_t n_partial_rows, int h,
+                      const int32_t *rank_off, const int32_t *pos_in_rank, int T, int R,
+                      uint16_t *out, hipStream_t stream);
+
 /* Set n int32 counts to -1, the "nothing arrived" value. [P2] "Buffer 与内存
  * 视角" (counters start at -1); [P1] "低延迟模式" (the count slot starts
  * empty). A fill kernel, so it is safe inside a captured graph. */
