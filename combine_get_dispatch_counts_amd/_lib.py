@@ -34,7 +34,7 @@ SIGNATURES = {
     "epx_combine_partial": (_I, [_P, _P, _I64, _I, _P, _P, _P, _P, _I, _I, _I64, _P, _P, _P]),
     "epx_combine_final": (_I, [_P, _P, _I64, _I, _P, _P, _I, _I, _P, _P]),
     "epx_ll_reset": (_I, [_P, _P, _I64, _P]),
-    "epx_ll_dispatch": (_I, [_P, _P, _I, _P] + [_I] * 8 + [_P] * 6),
+    "epx_ll_dispatch": (_I, [_P, _P, _I, _P] + [_I] * 8 + [_P] * 5 + [_P, _I64, _P, _P]),
     "epx_get_error": (_I, [_P, ctypes.POINTER(_I), _P]),
 }
 

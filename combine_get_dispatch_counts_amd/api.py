@@ -326,9 +326,13 @@ def alloc_ll(E: int, R_buf: int, cap: int, h: int, T: int, K: int, fp8: bool,
 
 def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
                 src_rank: int, cap: int, R_buf: int | None = None, fp8: bool = True,
-                buf: LowLatency | None = None) -> LowLatency:
+                buf: LowLatency | None = None, next_buf: LowLatency | None = None,
+                stats: torch.Tensor | None = None) -> LowLatency:
     """Fixed-slot low-latency dispatch (one launch, no host wait). ``buf``
-    must come from alloc_ll (its counts start at -1)."""
+    must come from alloc_ll (its counts start at -1). ``next_buf``, the
+    other buffer of a ping-pong pair, gets its counts reset to -1 by the same
+    launch; ``stats`` (int32 [2] on the device) receives the entries routed
+    and the fullest region's count."""
     _need(x, torch.bfloat16, "x", 2)
     _need(topk_idx, torch.int64, "topk_idx", 2)
     dev = x.device
@@ -337,10 +341,15 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
     R_buf = num_ranks if R_buf is None else R_buf
     if buf is None:
         buf = alloc_ll(num_experts, R_buf, cap, h, T, K, fp8, dev)
+    if stats is not None:
+        _need(stats, torch.int32, "stats")
+        if stats.numel() < 2:
+            raise ValueError("stats needs 2 int32 entries")
+    nxt = next_buf.ll_count if next_buf is not None else None
     rc = _lib.load().epx_ll_dispatch(
         _ctx(dev), _p(x), h, _p(topk_idx), T, K, num_experts, num_ranks, src_rank, cap, R_buf,
         int(fp8), _p(buf.ll_x), _p(buf.ll_scales), _p(buf.ll_src), _p(buf.ll_count),
-        _p(buf.pos_ll), _stream(dev))
+        _p(buf.pos_ll), _p(nxt), nxt.numel() if nxt is not None else 0, _p(stats), _stream(dev))
     check(rc, "epx_ll_dispatch")
     return buf
 

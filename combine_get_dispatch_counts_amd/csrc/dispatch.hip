@@ -370,6 +370,28 @@ __global__ __launch_bounds__(kWave) void ll_dispatch_kernel(LLArgs a)
         const int64_t region = a.R_buf == 1 ? e : (int64_t)e * a.R + a.src_rank;
         a.ll_count[region] = hist_all[e];
     }
+    // the other buffer of a ping-pong pair: its count slots back to empty,
+    // ready for the next step without a separate reset
+    for (int64_t i = (int64_t)blockIdx.x * kWave + lane; i < a.n_clear;
+         i += (int64_t)gridDim.x * kWave)
+        a.clear_count[i] = -1;
+    // fill of this source's regions: entries routed and the fullest region
+    if (blockIdx.x == 0 && a.stats) {
+        int sum = 0, mx = 0;
+        for (int e = lane; e < a.E; e += kWave) {
+            sum += hist_all[e];
+            mx = max(mx, hist_all[e]);
+        }
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            sum += __shfl_xor(sum, d, kWave);
+            mx = max(mx, __shfl_xor(mx, d, kWave));
+        }
+        if (lane == 0) {
+            a.stats[0] = sum;
+            a.stats[1] = mx;
+        }
+    }
     if (!have_token)
         return;
 

@@ -322,6 +322,7 @@ int epx_ll_reset(epx_ctx *ctx, int32_t *ll_count, int64_t n, hipStream_t stream)
 int epx_ll_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx, int T,
                     int K, int E, int R, int src_rank, int cap, int R_buf, int fp8, void *ll_x,
                     float *ll_scales, int32_t *ll_src, int32_t *ll_count, int32_t *pos_ll,
+                    int32_t *next_ll_count, int64_t n_next, int32_t *ll_stats,
                     hipStream_t stream)
 {
     int rc = check_ctx(ctx);
@@ -343,11 +344,20 @@ int epx_ll_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_
         return EPX_EINVAL;
     if (T > 0 && (!aligned16(x) || !aligned16(ll_x)))
         return EPX_EINVAL;
+    if (n_next < 0 || (n_next > 0 && !next_ll_count))
+        return EPX_EINVAL;
+    if (n_next > 0) {  // the two count arrays of a pair must not overlap
+        const int32_t *c0 = ll_count, *c1 = ll_count + (int64_t)E * R_buf;
+        const int32_t *n0 = next_ll_count, *n1 = next_ll_count + n_next;
+        if (n0 < c1 && c0 < n1)
+            return EPX_EINVAL;
+    }
     epx::LLArgs a{};
     a.x = x; a.topk_idx = topk_idx; a.h = h; a.T = T; a.K = K; a.E = E; a.R = R;
     a.src_rank = src_rank; a.cap = cap; a.R_buf = R_buf;
     a.ll_x = ll_x; a.ll_scales = ll_scales; a.ll_src = ll_src; a.ll_count = ll_count;
     a.pos_ll = pos_ll; a.err = ctx->d_err;
+    a.clear_count = next_ll_count; a.n_clear = n_next; a.stats = ll_stats;
     return launched(epx::launch_ll_dispatch(a, fp8 != 0, stream));
 }
 

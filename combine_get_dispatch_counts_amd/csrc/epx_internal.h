@@ -79,6 +79,9 @@ struct LLArgs {
     void *ll_x;
     float *ll_scales;
     int32_t *ll_src, *ll_count, *pos_ll;
+    int32_t *clear_count;  // the other buffer's counts, set to -1 (or null)
+    int64_t n_clear;
+    int32_t *stats;        // [2]: entries routed, fullest region (or null)
     int *err;
 };
 

@@ -252,11 +252,24 @@ int epx_ll_reset(epx_ctx *ctx, int32_t *ll_count, int64_t n, hipStream_t stream)
  *      ll_count [E*R_buf]: count[region(e)] = entries routed to e, for every
  *      e (0 included); counts of other sources' regions are not touched, so
  *      they keep what epx_ll_reset put there.
- *      pos_ll [T,K]: the row of (t,k), or -1: the handle for combine. */
+ *      pos_ll [T,K]: the row of (t,k), or -1: the handle for combine.
+ * Ping-pong ([P2] "三个方法概览", low-latency mode: two buffers flipped by
+ * XOR, reused with no allocation and no host wait):
+ *      next_ll_count [n_next], if n_next > 0, is the other buffer's count
+ *      array; this launch sets it to -1 so the next step can use that buffer
+ *      without an epx_ll_reset. It must not overlap ll_count (EPX_EINVAL)
+ *      and no reader of it may still be running.
+ * Buffer fill ([P1] "工程实践：模式选择与监控要点": buffer utilisation, slots
+ * used over slots available, in low-latency mode): ll_stats, if not
+ *      NULL, is a device int32[2] that receives the entries routed by this
+ *      source (the sum of its counts) and the largest count of any of its
+ *      regions; utilisation = ll_stats[0] / (E * cap), peak region fill =
+ *      ll_stats[1] / cap. */
 int epx_ll_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
                     int T, int K, int E, int R, int src_rank, int cap, int R_buf, int fp8,
                     void *ll_x, float *ll_scales, int32_t *ll_src, int32_t *ll_count,
-                    int32_t *pos_ll, hipStream_t stream);
+                    int32_t *pos_ll, int32_t *next_ll_count, int64_t n_next,
+                    int32_t *ll_stats, hipStream_t stream);
 
 /* Synchronise `stream`, return the device error word in *device_flags (host)
  * and clear it. Returns EPX_EDEVICE if any bit was set, EPX_OK otherwise. */

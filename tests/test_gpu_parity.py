@@ -487,3 +487,42 @@ def test_error_paths():
     epx.ll_dispatch(x[:4].contiguous(), torch.from_numpy(rep).cuda(), wl.E, wl.R, 0, 4, 1, False, buf)
     assert epx.get_error() == 2
     assert bool((buf.ll_x[4:].view(torch.uint8) == CANARY).all())
+
+
+def test_ll_ping_pong_and_fill_stats():
+    """Four decode steps over a ping-pong pair: each step dispatches into one
+    buffer and resets the other's counts in the same launch (garbage written
+    there first must read -1 afterwards); the rows, handles and counts of the
+    step match the oracle, and the fill stats equal the oracle's count sum
+    and largest count."""
+    import combine_get_dispatch_counts_amd as epx
+
+    wl = synth.WORKLOADS[2]
+    E, R, K, h, cap, src = wl.E, wl.R, wl.K, wl.h, wl.cap, 5
+    dev = torch.device("cuda")
+    bufs = [epx.alloc_ll(E, 1, cap, h, wl.T, K, True, dev) for _ in range(2)]
+    stats = torch.zeros(2, dtype=torch.int32, device=dev)
+    for step in range(4):
+        cur, nxt = bufs[step % 2], bufs[(step + 1) % 2]
+        inp = synth.make_inputs(2, seed=500 + step)
+        topk = inp["topk_idx"].copy()
+        topk[np.random.default_rng(step).random(topk.shape) < 0.1 * step] = -1
+        say(f"ll ping-pong step {step}")
+        nxt.ll_count.fill_(7)
+        cur.ll_src.view(torch.uint8).fill_(CANARY)
+        epx.ll_dispatch(dev_bf16(inp["x"]), torch.from_numpy(topk).cuda(), E, R, src, cap, 1,
+                        True, cur, next_buf=nxt, stats=stats)
+        assert epx.get_error() == 0
+        assert bool((nxt.ll_count == -1).all()), "the other buffer's counts were not reset"
+        o = oracle.ll_dispatch(inp["x"], topk, E, R, src, cap, 1, fp8=True)
+        _eq(host_bits(cur.pos_ll), o["pos_ll"], "pos_ll")
+        _eq(host_bits(cur.ll_count), o["ll_count"], "ll_count")
+        _eq(host_bits(cur.ll_src), o["ll_src"], "ll_src")
+        written = o["ll_src"] >= 0
+        _eq(host_bits(cur.ll_x)[written], o["ll_x"][written], "ll_x rows")
+        counts = o["ll_count"]
+        assert host_bits(stats).tolist() == [int(counts.sum()), int(counts.max())]
+    with pytest.raises(epx.EpxError) as ei:
+        epx.ll_dispatch(dev_bf16(inp["x"]), torch.from_numpy(topk).cuda(), E, R, src, cap, 1,
+                        True, bufs[0], next_buf=bufs[0])
+    assert ei.value.code == -1

@@ -155,3 +155,23 @@ def test_empty_and_errors(orc):
     with pytest.raises(orc.OracleError) as ei:
         orc.layout(np.array([[0, 1]]), 8, 3)
     assert ei.value.code == orc.EINVAL
+
+
+def test_two_level_dedup_by_logical_node(orc):
+    """Two-level dedup (the DeepEP study notes' hybrid section: deduplicate by
+    node first, then by GPU inside the node) with R ranks grouped into N
+    logical nodes of R/N ranks: the layout at node granularity (R = N) is the
+    rank-level layout with each node's ranks OR-ed together, and the
+    node-level send rows are one per (token, node)."""
+    inp = synth.make_inputs(3, T=300)
+    E, R, N = 256, 32, 4
+    topk = inp["topk_idx"].copy()
+    topk[np.random.default_rng(1).random(topk.shape) < 0.05] = -1
+    rank_lay = orc.layout(topk, E, R)
+    node_lay = orc.layout(topk, E, N)
+    in_node = rank_lay["is_token_in_rank"].reshape(-1, N, R // N).any(axis=2)
+    np.testing.assert_array_equal(node_lay["is_token_in_rank"], in_node.astype(np.uint8))
+    np.testing.assert_array_equal(node_lay["num_tokens_per_rank"], in_node.sum(axis=0))
+    np.testing.assert_array_equal(node_lay["num_tokens_per_expert"],
+                                  rank_lay["num_tokens_per_expert"])
+    assert int(node_lay["totals"][0]) == int(in_node.sum()) <= int(rank_lay["totals"][0])
