@@ -127,6 +127,29 @@ def _loop_us(fn, n):
     return a.elapsed_time(b) * 1e3 / n
 
 
+def _graph_us(fn, n):
+    """Average microseconds per call of fn, n calls captured in one HIP graph
+    and replayed (no host launch work per call: for kernels shorter than a
+    Python-level launch)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    us = _loop_us(g.replay, 5) / n
+    del g
+    return us
+
+
 def other_workloads(n=20):
     """The FP8, low-latency, skewed and two-stage-combine rows on their own
     workloads: per-kernel time, compulsory GB/s and fraction of the 8 TB/s
@@ -161,7 +184,7 @@ def other_workloads(n=20):
     y = synth.expert_outputs(T * K, h, seed=17, device="cuda")
     comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
     row8 = h + 4 * (h // 128)
-    lay_us = _loop_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay), n)
+    lay_us = _graph_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay), n)
     d_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs), n)
     d = epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs)
     c_us = _loop_us(lambda: epx.combine(y, d.pos_exp, w, out=comb), n)
@@ -216,14 +239,14 @@ def other_workloads(n=20):
     row8 = h + 4 * (h // 128)
     for R_buf in (1, R):
         buf = epx.alloc_ll(E, R_buf, cap, h, T, K, True, dev)
-        ll_us = _loop_us(lambda: epx.ll_dispatch(x, tk, E, R, 0, cap, R_buf, True, buf), n)
+        ll_us = _graph_us(lambda: epx.ll_dispatch(x, tk, E, R, 0, cap, R_buf, True, buf), n)
         n_rows = T * K
         ll_bytes = T * 2 * h + 8 * T * K + n_rows * (row8 + 4) + 4 * T * K + 4 * E
         entry = {"ll_dispatch_fp8": rec(ll_us, ll_bytes)}
         if R_buf == 1:
             y = synth.expert_outputs(E * cap, h, seed=19, device="cuda")
             comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
-            c_us = _loop_us(lambda: epx.combine(y, buf.pos_ll, w, out=comb), n)
+            c_us = _graph_us(lambda: epx.combine(y, buf.pos_ll, w, out=comb), n)
             entry["combine"] = rec(c_us, n_rows * 2 * h + 8 * T * K + T * 2 * h)
             entry["step_us"] = round(ll_us + c_us, 2)
             del y, comb
@@ -249,7 +272,7 @@ def other_workloads(n=20):
     n_rank, n_exp = (int(v) for v in lay.totals.cpu())
     y = synth.expert_outputs(T * K, h, seed=23, device="cuda")
     comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
-    lay_us = _loop_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay), n)
+    lay_us = _graph_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay), n)
     d_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs), n)
     d = epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs)
     c_us = _loop_us(lambda: epx.combine(y, d.pos_exp, w, out=comb), n)

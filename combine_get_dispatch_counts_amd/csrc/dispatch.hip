@@ -39,6 +39,14 @@ __device__ __forceinline__ int readlane(int v, int lane)
     return __builtin_amdgcn_readlane(v, lane);
 }
 
+// A 64-bit value of one lane, both halves moved as unsigned.
+__device__ __forceinline__ int64_t readlane64(int64_t v, int lane)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), lane);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 
 // One pass of a bf16 row held in registers: vector v of the pass is lane +
 // 64*u for u < NV.
@@ -54,6 +62,7 @@ struct RowBf16 {
             r[u] = (v < nvec) ? load16_stream(src + v) : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    __device__ __forceinline__ void quantise(int, int) {}
     __device__ __forceinline__ void store(char *dst_row, int v0, int nvec) const
     {
 #pragma unroll
@@ -116,12 +125,13 @@ template <int NV>
 struct RowFp8 {
     static constexpr int kPerPass = NV * kWave;
     u32x4 q[NV];
+    u32x4 lo[NV], hi[NV];  // the bf16 pass as loaded (lo: channels 0..7, hi: 8..15)
     u32x4 sv;   // scales of groups s0/8 + 4*lane .. +3 of the pass, +0 past the last group
     int n_sv;   // lanes holding a slice of the (padded) scale row in this pass
-    __device__ __forceinline__ void load_quantise(const u32x4 *src, int s0, int nseg)
+    // Issue the pass's loads; quantise() consumes them, so work placed in
+    // between overlaps their latency.
+    __device__ __forceinline__ void load(const u32x4 *src, int s0, int nseg)
     {
-        float sc[NV];
-        u32x4 lo[NV], hi[NV];
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int sg = s0 + u * kWave + lane_id();
@@ -129,6 +139,10 @@ struct RowFp8 {
             lo[u] = active ? load16_stream(src + 2 * sg) : u32x4{0u, 0u, 0u, 0u};
             hi[u] = active ? load16_stream(src + 2 * sg + 1) : u32x4{0u, 0u, 0u, 0u};
         }
+    }
+    __device__ __forceinline__ void quantise(int s0, int nseg)
+    {
+        float sc[NV];
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const uint32_t p[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w,
@@ -237,10 +251,8 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
     const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
     for (int i0 = 0; i0 < nitems; i0 += per_pass) {
         if (i0 > 0) {
-            if constexpr (FP8)
-                row.load_quantise(src, i0, nseg);
-            else
-                row.load(src, i0, nvec);
+            row.load(src, i0, nitems);
+            row.quantise(i0, nitems);
         }
         for (uint64_t m = d.rbits; m; m &= m - 1) {
             const int r = readlane(d.send_row, __builtin_ctzll(m));
@@ -273,12 +285,11 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
     const uint16_t *xrow = a.x + (size_t)t * a.h;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
 
-    // first pass of the row: issued before anything else
+    // first pass of the row: issued before anything else, quantised (FP8)
+    // once the destinations below have been worked out
     typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
-    if constexpr (FP8)
-        row.load_quantise(src, 0, a.h >> 4);
-    else
-        row.load(src, 0, a.h >> 3);
+    const int nitems = FP8 ? a.h >> 4 : a.h >> 3;
+    row.load(src, 0, nitems);
 
     // destinations
     const int64_t e = lane < a.K ? a.topk_idx[tk + lane] : -1;
@@ -320,37 +331,44 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
         }
     }
 
+    row.quantise(0, nitems);
     scatter<FP8>(row, d, xrow, a.h, a.send_x, a.send_scales, a.recv_x, a.recv_scales);
 }
 
-// Low-latency dispatch, one launch. Block t (one wave) handles token t. It
-// first histograms all T*K entries in LDS (decode batches are small): the
-// full histogram gives the count slots, the part before token t gives t's
-// slots. LDS atomics only add, so the result does not depend on their order.
+// Low-latency dispatch, one launch. Block t handles token t with kLLWaves
+// waves: together they histogram all T*K entries in LDS (decode batches are
+// small) -- the full histogram gives the count slots, the part before token
+// t gives t's slots; LDS atomics only add, so the result does not depend on
+// their order -- then wave w loads and quantises the row itself (the other
+// waves' copies come from L2) and writes the entries k with k % kLLWaves ==
+// w. A decode batch has few tokens, so one wave per token would leave most
+// of the chip idle and each wave writing K rows in turn.
+constexpr int kLLWaves = 8;
+
 template <bool FP8, int NV>
-__global__ __launch_bounds__(kWave) void ll_dispatch_kernel(LLArgs a)
+__global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
 {
     extern __shared__ int hist[];  // [E] all entries, [E] entries before token t
-    const int t = blockIdx.x, lane = threadIdx.x;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+    const int nthreads = kLLWaves * kWave;
     int *hist_all = hist, *hist_before = hist + a.E;
     const bool have_token = t < a.T;
     const int64_t tk = (int64_t)t * a.K;
     const uint16_t *xrow = a.x + (size_t)t * a.h;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
 
+    // the token's experts, lane k holding entry k, and its row go out first
+    const int64_t ek = (have_token && lane < a.K) ? a.topk_idx[tk + lane] : -1;
     typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
-    if (have_token) {
-        if constexpr (FP8)
-            row.load_quantise(src, 0, a.h >> 4);
-        else
-            row.load(src, 0, a.h >> 3);
-    }
+    const int nitems = FP8 ? a.h >> 4 : a.h >> 3;
+    if (have_token)
+        row.load(src, 0, nitems);
 
-    for (int i = lane; i < 2 * a.E; i += kWave)
+    for (int i = tid; i < 2 * a.E; i += nthreads)
         hist[i] = 0;
     __syncthreads();
     const int64_t n_ent = (int64_t)a.T * a.K;
-    for (int64_t i = lane; i < n_ent; i += kWave) {
+    for (int64_t i = tid; i < n_ent; i += nthreads) {
         const int64_t e = a.topk_idx[i];
         if (e == -1)
             continue;
@@ -366,17 +384,17 @@ __global__ __launch_bounds__(kWave) void ll_dispatch_kernel(LLArgs a)
     __syncthreads();
 
     // count slots: every expert's count, written by a spread of blocks
-    for (int e = blockIdx.x * kWave + lane; e < a.E; e += gridDim.x * kWave) {
+    for (int e = blockIdx.x * nthreads + tid; e < a.E; e += gridDim.x * nthreads) {
         const int64_t region = a.R_buf == 1 ? e : (int64_t)e * a.R + a.src_rank;
         a.ll_count[region] = hist_all[e];
     }
     // the other buffer of a ping-pong pair: its count slots back to empty,
     // ready for the next step without a separate reset
-    for (int64_t i = (int64_t)blockIdx.x * kWave + lane; i < a.n_clear;
-         i += (int64_t)gridDim.x * kWave)
+    for (int64_t i = (int64_t)blockIdx.x * nthreads + tid; i < a.n_clear;
+         i += (int64_t)gridDim.x * nthreads)
         a.clear_count[i] = -1;
     // fill of this source's regions: entries routed and the fullest region
-    if (blockIdx.x == 0 && a.stats) {
+    if (blockIdx.x == 0 && w == 0 && a.stats) {
         int sum = 0, mx = 0;
         for (int e = lane; e < a.E; e += kWave) {
             sum += hist_all[e];
@@ -395,18 +413,20 @@ __global__ __launch_bounds__(kWave) void ll_dispatch_kernel(LLArgs a)
     if (!have_token)
         return;
 
-    const int64_t e = lane < a.K ? a.topk_idx[tk + lane] : -1;
+    // this wave's entries: lane k < K with k % kLLWaves == w
+    const bool mine = lane < a.K && (lane % kLLWaves) == w;
+    const int64_t e = mine ? ek : -1;
     const bool valid = e >= 0 && e < a.E;
+    int rep = 0;  // earlier entries of this row with the same expert
+    for (int k2 = 0; k2 < a.K; ++k2)
+        rep += (k2 < lane && readlane64(ek, k2) == ek);
     Dests d;
     d.rbits = 0;
     d.vbits = uniform64(__ballot(valid));
     d.send_row = -1;
     d.recv_row = -1;
-    if (lane < a.K) {
+    if (mine) {
         if (valid) {
-            int rep = 0;  // earlier entries of this row with the same expert
-            for (int k2 = 0; k2 < lane; ++k2)
-                rep += (a.topk_idx[tk + k2] == e);
             const int slot = hist_before[e] + rep;
             if (slot < a.cap) {
                 const int64_t region = a.R_buf == 1 ? e : e * a.R + a.src_rank;
@@ -418,7 +438,10 @@ __global__ __launch_bounds__(kWave) void ll_dispatch_kernel(LLArgs a)
         }
         a.pos_ll[tk + lane] = d.recv_row;
     }
-    scatter<FP8>(row, d, xrow, a.h, nullptr, nullptr, a.ll_x, a.ll_scales);
+    if (d.vbits) {
+        row.quantise(0, nitems);
+        scatter<FP8>(row, d, xrow, a.h, nullptr, nullptr, a.ll_x, a.ll_scales);
+    }
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
@@ -466,7 +489,8 @@ static void launch_ll_nv(const LLArgs &a, hipStream_t stream)
 {
     const dim3 grid(a.T > 0 ? a.T : 1);
     const size_t lds = sizeof(int) * 2 * (size_t)a.E;
-    hipLaunchKernelGGL((ll_dispatch_kernel<FP8, NV>), grid, dim3(kWave), lds, stream, a);
+    hipLaunchKernelGGL((ll_dispatch_kernel<FP8, NV>), grid, dim3(kLLWaves * kWave), lds, stream,
+                       a);
 }
 
 hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream)
