@@ -151,10 +151,10 @@ def _graph_us(fn, n):
 
 
 def other_workloads(n=20):
-    """The FP8, low-latency, skewed and two-stage-combine rows on their own
-    workloads: per-kernel time, compulsory GB/s and fraction of the 8 TB/s
-    HBM peak. Not the headline figure (that is the prefill step above);
-    reported beside it."""
+    """The FP8, low-latency, skewed, two-stage-combine and receive rows on
+    their own workloads: per-kernel time, compulsory GB/s and fraction of the
+    8 TB/s HBM peak. Not the headline figure (that is the prefill step
+    above); reported beside it."""
     import numpy as np
     import torch
 
@@ -218,7 +218,14 @@ def other_workloads(n=20):
     comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
     p_us = _loop_us(lambda: epx.combine_partial(y, d, out=part), n)
     f_us = _loop_us(lambda: epx.combine_final(part, lay, out=comb), n)
+    # the receiver's permute at the same scale: a destination of 32 sources
+    # at T=4096 each receives about as many rows as one source sends in all
+    rows, ridx = bufs["send_x"][:n_rank], bufs["send_topk_idx"][:n_rank]
+    rp_us = _loop_us(lambda: epx.recv_permute(rows, ridx, E // R), n)
+    got = epx.recv_permute(rows, ridx, E // R)
+    n_out = int(got.layout.totals[1].item())
     assert epx.get_error() == 0
+    rp_bytes = n_rank * (2 * h + 8 * K) + n_out * (2 * h + 4) + 8 * n_rank * K
     p_bytes = n_exp * 2 * h + 4 * n_rank + 12 * n_rank * K + 4 * T * K + n_rank * 2 * h
     f_bytes = n_rank * 2 * h + 4 * T * R + T * 2 * h
     out["two_stage_combine_prefill"] = {
@@ -226,7 +233,11 @@ def other_workloads(n=20):
                     "then the reduce over ranks",
         "partial": rec(p_us, p_bytes), "final": rec(f_us, f_bytes),
         "total_us": round(p_us + f_us, 2)}
-    del x, tk, w, ws, lay, bufs, d, y, part, comb
+    out["receive_permute_prefill"] = {
+        "workload": f"{n_rank} received bf16 rows of h={h} into {E // R} local experts "
+                    f"({n_out} rows out): layout of the received indices + permute",
+        "layout_and_permute": rec(rp_us, rp_bytes)}
+    del x, tk, w, ws, lay, bufs, d, y, part, comb, rows, ridx, got
     torch.cuda.empty_cache()
 
     # decode, low-latency: T=128, h=7168, E=256, R=32, topk=8, cap=128, FP8

@@ -25,6 +25,8 @@ from .api import (  # noqa: E402
     ll_dispatch,
     ll_reset,
     ll_size_hint,
+    Received,
+    recv_permute,
     scale_stride,
     workspace_size,
 )
@@ -32,4 +34,4 @@ from .api import (  # noqa: E402
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
-           "ll_dispatch"]
+           "ll_dispatch", "Received", "recv_permute"]

@@ -238,6 +238,51 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor
     return Dispatched(layout=layout, **out)
 
 
+@dataclass
+class Received:
+    """A receiver's rows arranged into per-local-expert blocks."""
+    x: torch.Tensor                # [N*K cap, h'] rows, expert-major (row order inside a block)
+    scales: torch.Tensor | None    # FP8 scale rows, arranged alike
+    src_row: torch.Tensor          # [rows] the received row each output row came from
+    pos: torch.Tensor              # [N, K] output row of (received row, k), or -1
+    layout: Layout                 # counts / offsets over the local experts
+
+
+def recv_permute(rows: torch.Tensor, local_topk_idx: torch.Tensor, num_local_experts: int,
+                 scales: torch.Tensor | None = None) -> Received:
+    """The receiver's side of the high-throughput mode: its received rows
+    (one per source token, in source then token order) into contiguous
+    per-local-expert blocks, row order kept inside each block. ``rows`` are
+    bf16 [N, h], or FP8 codes uint8 [N, h] with ``scales`` [N, stride] fp32;
+    ``local_topk_idx`` [N, K] int64 holds each row's local expert indices
+    (-1 for entries of other ranks), as dispatch's send_topk_idx does. The
+    payload is copied bit for bit by the dispatch kernel's permute."""
+    _need(local_topk_idx, torch.int64, "local_topk_idx", 2)
+    dev = rows.device
+    N, K = local_topk_idx.shape
+    L = num_local_experts
+    lay = get_dispatch_layout(local_topk_idx, L, 1)
+    cap = N * K
+    payloads = [rows] + ([scales] if scales is not None else [])
+    outs = []
+    pos = torch.empty((N, K), dtype=torch.int32, device=dev)
+    src_row = torch.empty(cap, dtype=torch.int32, device=dev)
+    for pl in payloads:
+        if not pl.is_contiguous() or pl.shape[0] != N:
+            raise ValueError("payload rows must be contiguous with one row per received row")
+        v = pl.view(torch.uint8).view(N, -1).view(torch.bfloat16)
+        hh = v.shape[1]
+        out = torch.empty((cap, hh), dtype=torch.bfloat16, device=dev)
+        rc = _lib.load().epx_dispatch(
+            _ctx(dev), _p(v), hh, _p(local_topk_idx), None, N, K, L, 1, None,
+            _p(lay.exp_off), None, _p(lay.slot_in_expert), 0, None, None, None, None, None, 0,
+            _p(out), None, _p(src_row), cap, _p(pos), _stream(dev))
+        check(rc, "epx_dispatch (permute)")
+        outs.append(out.view(torch.uint8).view(cap, -1).view(pl.dtype))
+    return Received(x=outs[0], scales=outs[1] if scales is not None else None, src_row=src_row,
+                    pos=pos, layout=lay)
+
+
 def combine(expert_out: torch.Tensor, pos: torch.Tensor, topk_weights: torch.Tensor,
             out: torch.Tensor | None = None) -> torch.Tensor:
     """out[t] = bf16(sum over valid k, in k order, of w[t,k] * expert_out[pos[t,k]])."""
@@ -357,4 +402,4 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
-           "ll_dispatch"]
+           "ll_dispatch", "Received", "recv_permute"]

@@ -296,7 +296,8 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
     const bool valid = e >= 0 && e < a.E;
     const int ei = valid ? (int)e : 0;
     Dests d;
-    d.rbits = uniform64(wave_or(valid ? (1ull << (ei / a.L)) : 0ull));
+    // no send buffer: the permute alone (a receiver arranging its rows)
+    d.rbits = a.send_x ? uniform64(wave_or(valid ? (1ull << (ei / a.L)) : 0ull)) : 0ull;
     d.vbits = uniform64(__ballot(valid));
     d.send_row = -1;
     d.recv_row = -1;

@@ -209,15 +209,17 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
         return rc;
     if (send_cap_rows < 0 || recv_cap_rows < 0)
         return EPX_EINVAL;
+    const bool pack = send_x != nullptr;  // else the permute alone
     if (T > 0) {
-        if (!x || !topk_idx || !topk_w || !rank_off || !exp_off || !pos_in_rank ||
-            !slot_in_expert || !pos_exp || !send_x || !send_src || !send_topk_idx ||
-            !send_topk_w || !recv_x || !recv_src)
+        if (!x || !topk_idx || !exp_off || !slot_in_expert || !pos_exp || !recv_x || !recv_src)
             return EPX_EINVAL;
-        if (fp8 && (!send_scales || !recv_scales || !aligned16(send_scales) ||
-                    !aligned16(recv_scales)))
+        if (pack && (!topk_w || !rank_off || !pos_in_rank || !send_src || !send_topk_idx ||
+                     !send_topk_w))
             return EPX_EINVAL;
-        if (!aligned16(x) || !aligned16(send_x) || !aligned16(recv_x))
+        if (fp8 && (!recv_scales || !aligned16(recv_scales) ||
+                    (pack && (!send_scales || !aligned16(send_scales)))))
+            return EPX_EINVAL;
+        if (!aligned16(x) || !aligned16(recv_x) || (pack && !aligned16(send_x)))
             return EPX_EINVAL;
     }
     epx::DispatchArgs a{};

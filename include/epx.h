@@ -168,7 +168,14 @@ int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K,
  *      recv_scales (fp8, as send_scales), recv_src [rows] source token;
  *      pos_exp [T,K] the recv row of (t,k), or -1: the handle for combine.
  *      A row index >= its capacity is not written and sets
- *      EPX_DEV_OVERFLOW; totals from the layout call say what is needed. */
+ *      EPX_DEV_OVERFLOW; totals from the layout call say what is needed.
+ * send_x = NULL: the permute alone, no send buffer (send_*, topk_w,
+ *      rank_off and pos_in_rank may then be NULL). This is the receiver's
+ *      side of [P1] "高吞吐量模式": given its received rows as x and their
+ *      local expert indices as topk_idx (E = local experts, R = 1, with a
+ *      layout of those indices), it arranges them into per-expert blocks in
+ *      row order. The rows are copied bit for bit, so FP8 payloads (codes,
+ *      scales) can be passed as bf16 rows of half the width. */
 int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
                  const float *topk_w, int T, int K, int E, int R, const int32_t *rank_off,
                  const int32_t *exp_off, const int32_t *pos_in_rank,

@@ -1,0 +1,112 @@
+"""Multi-source receive on one GPU: R logical source ranks, each holding a
+consecutive slice of the tokens, run layout and dispatch on their own
+tokens; each destination receives its segment from every source, in source
+order (the transport itself is a copy here), and arranges the received rows
+into per-local-expert blocks (the receiver's permute of the high-throughput
+mode). Because the sources hold consecutive token ranges, the receiver's
+(source, token) order is global token order, so destination d's blocks must
+equal the oracle's expert-major buffer over d's experts for all tokens.
+The low-latency buffer is filled by every source, region (e, s) by source
+s, and checked against the oracle source by source."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu import CANARY, dev_bf16, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _eq(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    bad = np.flatnonzero((a != b).ravel())
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:5]}"
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_multi_source_receive_permute(fp8):
+    import combine_get_dispatch_counts_amd as epx
+
+    T, h, E, R, K = 512, 1024, 64, 8, 6
+    L, per = E // R, T // R
+    rng = np.random.default_rng(77)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=78, p_drop=0.05)
+    w = rng.random((T, K)).astype(np.float32)
+    say(f"multi-source receive T={T} h={h} E={E} R={R} K={K} fp8={fp8}")
+
+    # every source: layout + dispatch over its own tokens
+    sent = []
+    for s in range(R):
+        sl = slice(s * per, (s + 1) * per)
+        tk = torch.from_numpy(np.ascontiguousarray(topk[sl])).cuda()
+        lay = epx.get_dispatch_layout(tk, E, R)
+        d = epx.dispatch(dev_bf16(np.ascontiguousarray(x[sl])), tk,
+                         torch.from_numpy(np.ascontiguousarray(w[sl])).cuda(), E, R, fp8=fp8,
+                         layout=lay)
+        sent.append((lay.rank_off.cpu().numpy(), d))
+    assert epx.get_error() == 0
+
+    o = oracle.dispatch(x, topk, w, E, R, fp8=fp8)
+    exp_off = o["layout"]["exp_off"]
+    ngrp = h // 128
+    for dst in range(R):
+        seg = [(ro[dst], ro[dst + 1], d) for ro, d in sent]
+        rows = torch.cat([d.send_x[a:b] for a, b, d in seg])
+        idx = torch.cat([d.send_topk_idx[a:b] for a, b, d in seg])
+        sc = torch.cat([d.send_scales[a:b] for a, b, d in seg]) if fp8 else None
+        rec = epx.recv_permute(rows, idx, L, scales=sc)
+        assert epx.get_error() == 0
+        lo, hi = exp_off[dst * L], exp_off[(dst + 1) * L]
+        n = hi - lo
+        _eq(host_bits(rec.layout.num_tokens_per_expert),
+            o["layout"]["num_tokens_per_expert"][dst * L:(dst + 1) * L], f"dst {dst} counts")
+        _eq(host_bits(rec.x)[:n], o["recv_x"][lo:hi], f"dst {dst} rows")
+        if fp8:
+            _eq(host_bits(rec.scales)[:n, :ngrp], o["recv_scales"][lo:hi], f"dst {dst} scales")
+        # each output row came from the received row holding the same token
+        src_tok = np.concatenate([d.send_src[a:b].cpu().numpy() + s * per
+                                  for s, (a, b, d) in enumerate(seg)])
+        _eq(src_tok[host_bits(rec.src_row)[:n]], o["recv_src"][lo:hi], f"dst {dst} sources")
+
+
+def test_low_latency_buffer_filled_by_every_source():
+    import combine_get_dispatch_counts_amd as epx
+
+    T, h, E, R, K, cap = 256, 1024, 64, 8, 6, 64
+    per = T // R
+    rng = np.random.default_rng(91)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=92)
+    say(f"low-latency buffer from all {R} sources, T={T} h={h} E={E} cap={cap}")
+    dev = torch.device("cuda")
+    buf = epx.alloc_ll(E, R, cap, h, per, K, True, dev)
+    buf.ll_x.view(torch.uint8).fill_(CANARY)
+    buf.ll_src.view(torch.uint8).fill_(CANARY)
+    pos = []
+    for s in range(R):
+        sl = slice(s * per, (s + 1) * per)
+        epx.ll_dispatch(dev_bf16(np.ascontiguousarray(x[sl])),
+                        torch.from_numpy(np.ascontiguousarray(topk[sl])).cuda(), E, R, s, cap, R,
+                        True, buf)
+        pos.append(host_bits(buf.pos_ll).copy())
+    assert epx.get_error() == 0
+    counts = host_bits(buf.ll_count).reshape(E, R)
+    assert (counts >= 0).all(), "a region count was left empty"
+    x4 = host_bits(buf.ll_x).reshape(E, R, cap, h)
+    src4 = host_bits(buf.ll_src).reshape(E, R, cap)
+    for s in range(R):
+        sl = slice(s * per, (s + 1) * per)
+        o = oracle.ll_dispatch(np.ascontiguousarray(x[sl]), np.ascontiguousarray(topk[sl]), E, R,
+                               s, cap, 1, fp8=True)
+        _eq(counts[:, s], o["ll_count"], f"source {s} counts")
+        _eq(src4[:, s].reshape(-1), o["ll_src"], f"source {s} sources")
+        written = o["ll_src"] >= 0
+        _eq(x4[:, s].reshape(E * cap, h)[written], o["ll_x"][written], f"source {s} rows")
+        # the handle addresses the full layout: region e*R + s
+        p = o["pos_ll"]
+        full = np.where(p >= 0, ((p // cap) * R + s) * cap + p % cap, -1)
+        _eq(pos[s], full, f"source {s} handle")
