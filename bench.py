@@ -1,17 +1,19 @@
 """Benchmark: dispatch + combine per layer on one MI355X.
 
 One step = one pass of the high-throughput hot path over one batch:
-get_dispatch_layout (counts, is_token_in_rank, prefix offsets) -> dispatch
-(rank-deduplicated pack + expert-major permute) -> combine (top-k weighted
-fp32 reduction back to bf16), on the prefill workload T=4096, h=7168, E=256,
-R=32 (8 experts per logical rank), topk=8, bf16. Buffers are preallocated at
+get_dispatch_layout (counts, is_token_in_rank, prefix offsets) and dispatch
+(rank-deduplicated pack + expert-major permute) in one launch, then combine
+(top-k weighted fp32 reduction back to bf16), on the prefill workload
+T=4096, h=7168, E=256, R=32 (8 experts per logical rank), topk=8, bf16. The
+same step with the layout and the dispatch as two launches is reported
+beside it. Buffers are preallocated at
 worst-case capacity, so the timed region holds no host wait and no
 allocation. Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. ``value`` is HBM GB/s over the compulsory bytes of the
 step (each required input read once, each required output written once);
 ``ms_per_step`` is the wall time per step. ``roofline`` covers the dominant
-kernel (dispatch) timed with HIP events on its stream; ``cpu_baseline``
+kernel (the fused layout + dispatch) timed with HIP events on its stream; ``cpu_baseline``
 times the CPU oracle (single thread) on the same workload.
 
 ``python bench.py --summarize-profiles <folder>`` instead writes the
@@ -32,35 +34,37 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "dispatch+combine µs/layer and HBM GB/s (% peak) at T=4096,h=7168,topk=8"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dispatch_prefill_T4096_traffic.json")
-# the dispatch kernel's sources: measured traffic is reported only while these match
-KERNEL_SOURCES = ["combine_get_dispatch_counts_amd/csrc/dispatch.hip",
-                  "combine_get_dispatch_counts_amd/csrc/epx_device.h",
-                  "combine_get_dispatch_counts_amd/csrc/epx_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T4096_traffic.json")
+# each kernel's sources: its measured traffic is reported only while these match
+_CSRC = "combine_get_dispatch_counts_amd/csrc/"
+KERNEL_SOURCES = {
+    "fused_kernel": [_CSRC + f for f in ("fused.hip", "layout_device.h", "dispatch_device.h",
+                                         "epx_device.h", "epx_internal.h")],
+    "dispatch_kernel": [_CSRC + f for f in ("dispatch.hip", "dispatch_device.h", "epx_device.h",
+                                            "epx_internal.h")],
+}
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(kernel: str) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per dispatch launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a same-run copy of known
-    size), or None when the kernel sources changed since it was taken."""
-    import json
-
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` at the prefill workload from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a
+    same-run copy of known size), or None when its sources changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_digest():
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -315,14 +319,18 @@ PROFILE_RUNS = {
           "python3 <R>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --flush-mb 0 --graph 0 "
           "--other 1 --calib-copy-mb 1024",
 }
-PREFILL_DISPATCH = ("dispatch_kernel<false, 14>", 4096 * 64)  # kernel, grid (threads)
+# the prefill launches the traffic record covers: (kernel, grid in threads)
+PREFILL_KERNELS = {
+    "dispatch_kernel": ("dispatch_kernel<false, 14>", 4096 * 64),
+    "fused_kernel": ("fused_kernel<8, false, 14>", (16 + 1 + 4096 // 8) * 512),
+}
+_KERNEL_PREFIXES = ("dispatch", "combine", "layout", "ll_", "fill", "fused")
 
 
 def _short_name(name: str) -> str:
     for junk in ("void ", "epx::(anonymous namespace)::"):
         name = name.replace(junk, "")
-    return name.split("(")[0] if name.startswith(("dispatch", "combine", "layout", "ll_", "fill")) \
-        else name
+    return name.split("(")[0] if name.startswith(_KERNEL_PREFIXES) else name
 
 
 def _read_csv(folder: str, suffix: str) -> list[dict]:
@@ -341,7 +349,7 @@ def _durations(folder: str) -> dict:
     out: dict = {}
     for r in _read_csv(folder, "kernel_trace.csv"):
         name = _short_name(r["Kernel_Name"])
-        if not name.startswith(("dispatch", "combine", "layout", "ll_", "fill")):
+        if not name.startswith(_KERNEL_PREFIXES):
             continue
         key = (name, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
         out.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -360,7 +368,7 @@ def _counter(folder: str, counter: str) -> tuple[dict, float]:
             calib.append(v)
             continue
         name = _short_name(r["Kernel_Name"])
-        if not name.startswith(("dispatch", "combine", "layout", "ll_", "fill")):
+        if not name.startswith(_KERNEL_PREFIXES):
             continue
         acc.setdefault((name, int(r["Grid_Size"])), []).append(v)
     return {k: sum(v) / len(v) for k, v in acc.items()}, max(calib) if calib else 0.0
@@ -425,18 +433,26 @@ def summarize_profiles(folder: str, calib_mb: int = 1024) -> None:
     if os.path.exists(old):
         os.remove(old)
 
-    fr, wr = fetch[PREFILL_DISPATCH], write[PREFILL_DISPATCH]
-    rec = {"kernel": f"dispatch_kernel<bf16> ({PREFILL_DISPATCH[0]})",
-           "workload": "prefill T=4096 h=7168 E=256 R=32 topk=8 bf16",
-           "bytes_per_launch": round(fr * sf * 1024 + wr * sw * 1024),
-           "read_bytes": round(fr * sf * 1024), "write_bytes": round(wr * sw * 1024),
-           "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
-           "source": "profiles/hbm_traffic_counters.md",
-           "kernel_source_sha256": kernel_source_digest()}
+    recs = {}
+    for kernel, key in PREFILL_KERNELS.items():
+        if key not in fetch or key not in write:
+            continue
+        fr, wr = fetch[key], write[key]
+        recs[kernel] = {"kernel": key[0], "grid_threads": key[1],
+                        "workload": "prefill T=4096 h=7168 E=256 R=32 topk=8 bf16",
+                        "bytes_per_launch": round(fr * sf * 1024 + wr * sw * 1024),
+                        "read_bytes": round(fr * sf * 1024), "write_bytes": round(wr * sw * 1024),
+                        "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+                        "source": "profiles/hbm_traffic_counters.md",
+                        "kernel_source_sha256": kernel_source_digest(kernel)}
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump(recs, f, indent=1)
         f.write("\n")
-    print(f"wrote the profiles/ summaries; dispatch traffic {rec['bytes_per_launch'] / 1e6:.1f} MB")
+    old = os.path.join(prof, "dispatch_prefill_T4096_traffic.json")
+    if os.path.exists(old):
+        os.remove(old)
+    print("wrote the profiles/ summaries; " + ", ".join(
+        f"{k} traffic {v['bytes_per_launch'] / 1e6:.1f} MB" for k, v in recs.items()))
 
 
 def main():
@@ -485,8 +501,23 @@ def main():
     out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
 
     lay_buf = epx.alloc_layout(T, K, E, R, None, dev)
+    fws = torch.zeros(max(epx.fused_workspace_size(T, K, E, R), 1), dtype=torch.uint8,
+                      device=dev)
 
     def step(ev=None):
+        """The step: layout and dispatch in one launch, then combine."""
+        if ev:
+            ev[0].record()
+        d = epx.dispatch_fused(x, tk, w, E, R, layout=lay_buf, out=bufs, workspace=fws)
+        if ev:
+            ev[1].record()
+        epx.combine(expert_out, d.pos_exp, w, out=out)
+        if ev:
+            ev[2].record()
+        return d.layout
+
+    def step_two(ev=None):
+        """The same step with the layout and the dispatch as two launches."""
         if ev:
             ev[0].record()
         lay = epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay_buf)
@@ -501,6 +532,7 @@ def main():
         return lay
 
     for _ in range(args.warmup):
+        step_two()
         lay = step()
     torch.cuda.synchronize()
     if args.calib_copy_mb > 0:
@@ -524,25 +556,46 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     assert epx.get_error() == 0
 
+    # the two-launch form of the same step, timed the same way
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_two()
+    torch.cuda.synchronize()
+    two_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    assert epx.get_error() == 0
+
     # per-phase split, from separate steps with events between the kernel groups
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     phase = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3
-             for j, name in enumerate(["layout", "dispatch", "combine"])}
+             for j, name in enumerate(["layout+dispatch", "combine"])}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_two(evs[i])
+    torch.cuda.synchronize()
+    phase_two = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3
+                 for j, name in enumerate(["layout", "dispatch", "combine"])}
 
-    # the dominant kernel on its own: the same dispatch launched back to back
-    # on the step's stream (it is idempotent), one event pair around them all
+    # the dominant kernels on their own, launched back to back on the step's
+    # stream (both are idempotent), one event pair around them all
+    def back_to_back_us(fn):
+        fn()
+        torch.cuda.synchronize()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k0.record()
+        for _ in range(args.steps):
+            fn()
+        k1.record()
+        torch.cuda.synchronize()
+        return k0.elapsed_time(k1) * 1e3 / args.steps
+
+    fused_us = back_to_back_us(
+        lambda: epx.dispatch_fused(x, tk, w, E, R, layout=lay_buf, out=bufs, workspace=fws))
     lay = epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay_buf)
-    torch.cuda.synchronize()
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record()
-    for _ in range(args.steps):
-        epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs)
-    k1.record()
-    torch.cuda.synchronize()
-    dispatch_us = k0.elapsed_time(k1) * 1e3 / args.steps
+    dispatch_us = back_to_back_us(lambda: epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs))
     assert epx.get_error() == 0
 
     # the same step captured once in a HIP graph and replayed (no host launch
@@ -578,10 +631,10 @@ def main():
         cold = []
         for i in range(min(args.steps, 20)):
             scratch.fill_(i & 0xFF)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             step(e)
             torch.cuda.synchronize()
-            cold.append(e[0].elapsed_time(e[3]) * 1e3)
+            cold.append(e[0].elapsed_time(e[-1]) * 1e3)
         cold_us = statistics.median(cold)
         del scratch
 
@@ -599,6 +652,8 @@ def main():
     by = step_bytes(T, h, K, R, n_rank, n_exp)
     bmin = survey_bmin(T, h, K, R, n_rank, n_exp)
     gbs = bmin / (ms_per_step * 1e-3) / 1e9
+    fused_bytes = by["layout"] + by["dispatch"]
+    fused_gbs = fused_bytes / (fused_us * 1e-6) / 1e9
     disp_gbs = by["dispatch"] / (dispatch_us * 1e-6) / 1e9
     comb_gbs = by["combine"] / (phase["combine"] * 1e-6) / 1e9
     b_flow = bmin + n_rank * 2 * h
@@ -631,7 +686,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"prefill T={T} h={h} E={E} R={R} topk={K} bf16, "
-                               "high-throughput layout+dispatch+combine",
+                               "high-throughput layout+dispatch (one launch) + combine",
                    "T": T, "hidden": h, "num_experts": E, "num_ranks": R, "topk": K,
                    "n_rank_rows": n_rank, "n_expert_rows": n_exp},
         "us_per_layer": round(ms_per_step * 1e3, 2),
@@ -639,16 +694,23 @@ def main():
         "b_min_bytes": bmin,
         "b_flow_gbs": round(b_flow / (ms_per_step * 1e-3) / 1e9, 1),
         "phase_us": {k: round(v, 2) for k, v in phase.items()},
-        "phase_gbs": {"dispatch": round(disp_gbs, 1), "combine": round(comb_gbs, 1)},
+        "phase_gbs": {"layout+dispatch": round(fused_gbs, 1), "combine": round(comb_gbs, 1)},
+        "two_launch": {"us_per_layer": round(two_ms * 1e3, 2),
+                       "value": round(bmin / (two_ms * 1e-3) / 1e9, 1),
+                       "phase_us": {k: round(v, 2) for k, v in phase_two.items()},
+                       "dispatch_kernel_us": round(dispatch_us, 2),
+                       "dispatch_gbs": round(disp_gbs, 1),
+                       "dispatch_traffic": measured_traffic("dispatch_kernel")},
         "ceilings": ceil or None,
         "frac_of_copy_ceiling": round(gbs / ceil["d2d_copy_gbs"], 4) if ceil else None,
         "cold_cache_us_per_layer": round(cold_us, 2) if cold_us else None,
         "graph_us_per_layer": round(graph_us, 2) if graph_us else None,
-        "dispatch_kernel_us": round(dispatch_us, 2),
-        "roofline": {"bound": "hbm", "achieved": round(disp_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(disp_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(), "kernel": "dispatch_kernel<bf16>",
-                     "bytes_per_launch": by["dispatch"]},
+        "fused_kernel_us": round(fused_us, 2),
+        "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("fused_kernel"),
+                     "kernel": "fused_kernel<bf16> (layout + dispatch)",
+                     "bytes_per_launch": fused_bytes},
         "cpu_baseline": cpu,
         "other_workloads": others,
     }

@@ -20,6 +20,8 @@ from .api import (  # noqa: E402
     combine_final,
     combine_partial,
     dispatch,
+    dispatch_fused,
+    fused_workspace_size,
     get_dispatch_layout,
     get_error,
     ll_dispatch,
@@ -34,4 +36,5 @@ from .api import (  # noqa: E402
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
-           "ll_dispatch", "Received", "recv_permute"]
+           "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
+           "dispatch_fused"]

@@ -283,6 +283,56 @@ def recv_permute(rows: torch.Tensor, local_topk_idx: torch.Tensor, num_local_exp
                     pos=pos, layout=lay)
 
 
+def fused_workspace_size(T: int, K: int, E: int, R: int) -> int:
+    n = ctypes.c_size_t()
+    check(_lib.load().epx_fused_workspace_size(T, K, E, R, ctypes.byref(n)),
+          "epx_fused_workspace_size")
+    return n.value
+
+
+def dispatch_fused(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
+                   num_experts: int, num_ranks: int, fp8: bool = False,
+                   num_channels: int | None = None, layout: Layout | None = None,
+                   out: dict | None = None, workspace: torch.Tensor | None = None,
+                   totals_host: torch.Tensor | None = None) -> Dispatched:
+    """get_dispatch_layout and dispatch in one launch (no host wait): the
+    same outputs as the two calls. ``layout`` (from alloc_layout) and
+    ``out`` (from alloc_dispatch) avoid allocating; without ``out`` the
+    buffers get the worst-case capacities T*min(K,R) and T*K rows.
+    ``workspace`` must hold fused_workspace_size(T, K, E, R) bytes and be
+    zero-filled before its first use (without one, a cached workspace per
+    device and stream is used)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(topk_idx, torch.int64, "topk_idx", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    dev = x.device
+    T, h = x.shape
+    K = topk_idx.shape[1]
+    E, R = num_experts, num_ranks
+    if topk_idx.shape[0] != T or tuple(topk_weights.shape) != (T, K):
+        raise ValueError("x, topk_idx and topk_weights disagree on T or K")
+    lay = layout if layout is not None else alloc_layout(T, K, E, R, num_channels, dev)
+    if out is None:
+        out = alloc_dispatch(T, h, K, T * min(K, R), T * K, fp8, dev)
+    if workspace is None:
+        workspace = _layout_workspace(dev, fused_workspace_size(T, K, E, R))
+    if totals_host is not None and not (totals_host.is_pinned() and totals_host.numel() >= 2
+                                        and totals_host.dtype == torch.int32):
+        raise ValueError("totals_host must be a pinned int32 tensor of >= 2 elements")
+    cp = lay.channel_prefix if num_channels else None
+    rc = _lib.load().epx_dispatch_fused(
+        _ctx(dev), _p(x), h, _p(topk_idx), _p(topk_weights), T, K, E, R, num_channels or 0,
+        _p(lay.num_tokens_per_expert), _p(lay.num_tokens_per_rank), _p(lay.is_token_in_rank),
+        _p(lay.rank_off), _p(lay.exp_off), _p(lay.pos_in_rank), _p(lay.slot_in_expert),
+        _p(cp), _p(lay.totals), _p(totals_host), _p(workspace), workspace.numel(), int(fp8),
+        _p(out["send_x"]), _p(out["send_scales"]), _p(out["send_src"]),
+        _p(out["send_topk_idx"]), _p(out["send_topk_w"]), out["send_x"].shape[0],
+        _p(out["recv_x"]), _p(out["recv_scales"]), _p(out["recv_src"]), out["recv_x"].shape[0],
+        _p(out["pos_exp"]), _stream(dev))
+    check(rc, "epx_dispatch_fused")
+    return Dispatched(layout=lay, **out)
+
+
 def combine(expert_out: torch.Tensor, pos: torch.Tensor, topk_weights: torch.Tensor,
             out: torch.Tensor | None = None) -> torch.Tensor:
     """out[t] = bf16(sum over valid k, in k order, of w[t,k] * expert_out[pos[t,k]])."""
@@ -402,4 +452,5 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
-           "ll_dispatch", "Received", "recv_permute"]
+           "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
+           "dispatch_fused"]

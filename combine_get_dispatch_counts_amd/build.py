@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libepx.so")
-SOURCES = ["epx_api.hip", "layout.hip", "dispatch.hip", "combine.hip"]
+SOURCES = ["epx_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "fused.hip"]
 ARCH = "gfx950"
 
 

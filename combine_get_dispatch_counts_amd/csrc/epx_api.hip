@@ -143,13 +143,14 @@ size_t epx_ll_size_hint(int max_tokens_per_rank, int h, int R, int E, int fp8)
     return up(total);
 }
 
-int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int E, int R,
-                            int C, int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
-                            uint8_t *is_token_in_rank, int32_t *rank_off, int32_t *exp_off,
-                            int32_t *pos_in_rank, int32_t *slot_in_expert,
-                            int32_t *channel_prefix, int32_t *totals,
-                            int32_t *totals_host_mapped, void *ws, size_t ws_bytes,
-                            hipStream_t stream)
+// Checks and packs the layout call's arguments (the workspace is checked by
+// the caller, against its own size).
+static int layout_args(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int E, int R, int C,
+                       int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                       uint8_t *is_token_in_rank, int32_t *rank_off, int32_t *exp_off,
+                       int32_t *pos_in_rank, int32_t *slot_in_expert, int32_t *channel_prefix,
+                       int32_t *totals, int32_t *totals_host_mapped, void *ws,
+                       epx::LayoutArgs &a)
 {
     int rc = check_ctx(ctx);
     if (rc != EPX_OK)
@@ -166,11 +167,9 @@ int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K,
                   !aligned16(slot_in_expert)))
         return EPX_EINVAL;
     const size_t need = epx::layout_workspace_bytes(T, E, R);
-    if (ws_bytes < need)
-        return EPX_ECAPACITY;
     if (need > 0 && !ws)
         return EPX_EINVAL;
-    epx::LayoutArgs a{};
+    a = epx::LayoutArgs{};
     a.topk_idx = topk_idx;
     a.T = T; a.K = K; a.E = E; a.R = R; a.L = E / R;
     a.C = channel_prefix ? C : 0;
@@ -189,16 +188,38 @@ int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K,
     a.totals = totals;
     a.totals_host_mapped = totals_host_mapped;
     a.err = ctx->d_err;
+    return EPX_OK;
+}
+
+int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int E, int R,
+                            int C, int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                            uint8_t *is_token_in_rank, int32_t *rank_off, int32_t *exp_off,
+                            int32_t *pos_in_rank, int32_t *slot_in_expert,
+                            int32_t *channel_prefix, int32_t *totals,
+                            int32_t *totals_host_mapped, void *ws, size_t ws_bytes,
+                            hipStream_t stream)
+{
+    epx::LayoutArgs a;
+    const int rc = layout_args(ctx, topk_idx, T, K, E, R, C, num_tokens_per_expert,
+                               num_tokens_per_rank, is_token_in_rank, rank_off, exp_off,
+                               pos_in_rank, slot_in_expert, channel_prefix, totals,
+                               totals_host_mapped, ws, a);
+    if (rc != EPX_OK)
+        return rc;
+    if (ws_bytes < epx::layout_workspace_bytes(T, E, R))
+        return EPX_ECAPACITY;
     return launched(epx::launch_layout(a, stream));
 }
 
-int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
-                 const float *topk_w, int T, int K, int E, int R, const int32_t *rank_off,
-                 const int32_t *exp_off, const int32_t *pos_in_rank,
-                 const int32_t *slot_in_expert, int fp8, void *send_x, float *send_scales,
-                 int32_t *send_src, int64_t *send_topk_idx, float *send_topk_w,
-                 int64_t send_cap_rows, void *recv_x, float *recv_scales, int32_t *recv_src,
-                 int64_t recv_cap_rows, int32_t *pos_exp, hipStream_t stream)
+// Checks and packs the dispatch call's arguments.
+static int dispatch_args(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
+                         const float *topk_w, int T, int K, int E, int R,
+                         const int32_t *rank_off, const int32_t *exp_off,
+                         const int32_t *pos_in_rank, const int32_t *slot_in_expert, int fp8,
+                         void *send_x, float *send_scales, int32_t *send_src,
+                         int64_t *send_topk_idx, float *send_topk_w, int64_t send_cap_rows,
+                         void *recv_x, float *recv_scales, int32_t *recv_src,
+                         int64_t recv_cap_rows, int32_t *pos_exp, epx::DispatchArgs &a)
 {
     int rc = check_ctx(ctx);
     if (rc != EPX_OK)
@@ -222,7 +243,7 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
         if (!aligned16(x) || !aligned16(recv_x) || (pack && !aligned16(send_x)))
             return EPX_EINVAL;
     }
-    epx::DispatchArgs a{};
+    a = epx::DispatchArgs{};
     a.x = x; a.topk_idx = topk_idx; a.topk_w = topk_w;
     a.h = h; a.T = T; a.K = K; a.E = E; a.R = R; a.L = E / R;
     a.rank_off = rank_off; a.exp_off = exp_off;
@@ -232,7 +253,72 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
     a.recv_x = recv_x; a.recv_scales = recv_scales; a.recv_src = recv_src;
     a.recv_cap = recv_cap_rows; a.pos_exp = pos_exp;
     a.err = ctx->d_err;
+    return EPX_OK;
+}
+
+int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
+                 const float *topk_w, int T, int K, int E, int R, const int32_t *rank_off,
+                 const int32_t *exp_off, const int32_t *pos_in_rank,
+                 const int32_t *slot_in_expert, int fp8, void *send_x, float *send_scales,
+                 int32_t *send_src, int64_t *send_topk_idx, float *send_topk_w,
+                 int64_t send_cap_rows, void *recv_x, float *recv_scales, int32_t *recv_src,
+                 int64_t recv_cap_rows, int32_t *pos_exp, hipStream_t stream)
+{
+    epx::DispatchArgs a;
+    const int rc = dispatch_args(ctx, x, h, topk_idx, topk_w, T, K, E, R, rank_off, exp_off,
+                                 pos_in_rank, slot_in_expert, fp8, send_x, send_scales, send_src,
+                                 send_topk_idx, send_topk_w, send_cap_rows, recv_x, recv_scales,
+                                 recv_src, recv_cap_rows, pos_exp, a);
+    if (rc != EPX_OK)
+        return rc;
     return launched(epx::launch_dispatch(a, fp8 != 0, stream));
+}
+
+int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes)
+{
+    if (!bytes)
+        return EPX_EINVAL;
+    const int rc = check_routing(T, K, E, R);
+    if (rc != EPX_OK)
+        return rc;
+    *bytes = epx::fused_workspace_bytes(T, K, E, R);
+    return EPX_OK;
+}
+
+int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
+                       const float *topk_w, int T, int K, int E, int R, int C,
+                       int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                       uint8_t *is_token_in_rank, int32_t *rank_off, int32_t *exp_off,
+                       int32_t *pos_in_rank, int32_t *slot_in_expert, int32_t *channel_prefix,
+                       int32_t *totals, int32_t *totals_host_mapped, void *ws, size_t ws_bytes,
+                       int fp8, void *send_x, float *send_scales, int32_t *send_src,
+                       int64_t *send_topk_idx, float *send_topk_w, int64_t send_cap_rows,
+                       void *recv_x, float *recv_scales, int32_t *recv_src,
+                       int64_t recv_cap_rows, int32_t *pos_exp, hipStream_t stream)
+{
+    epx::FusedArgs f{};
+    int rc = layout_args(ctx, topk_idx, T, K, E, R, C, num_tokens_per_expert,
+                         num_tokens_per_rank, is_token_in_rank, rank_off, exp_off, pos_in_rank,
+                         slot_in_expert, channel_prefix, totals, totals_host_mapped, ws, f.lay);
+    if (rc != EPX_OK)
+        return rc;
+    if (T > 0 && !send_x)  // the fused call always packs
+        return EPX_EINVAL;
+    rc = dispatch_args(ctx, x, h, topk_idx, topk_w, T, K, E, R, rank_off, exp_off, pos_in_rank,
+                       slot_in_expert, fp8, send_x, send_scales, send_src, send_topk_idx,
+                       send_topk_w, send_cap_rows, recv_x, recv_scales, recv_src, recv_cap_rows,
+                       pos_exp, f.disp);
+    if (rc != EPX_OK)
+        return rc;
+    const size_t need = epx::fused_workspace_bytes(T, K, E, R);
+    if (ws_bytes < need)
+        return EPX_ECAPACITY;
+    if (need > 0) {
+        char *base = static_cast<char *>(ws) + epx::layout_workspace_bytes(T, E, R);
+        f.tot = reinterpret_cast<uint64_t *>(base);
+        f.tok = f.tot + (E + R);
+    }
+    return launched(epx::launch_fused(f, fp8 != 0, stream));
 }
 
 int epx_combine(epx_ctx *ctx, const uint16_t *expert_out, int64_t n_rows, int h,

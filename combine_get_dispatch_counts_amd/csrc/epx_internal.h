@@ -86,6 +86,19 @@ struct LLArgs {
 };
 
 hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream);
+
+// Layout and dispatch in one launch: the layout's arguments (workspace head
+// and tile words included), the dispatch's (its layout pointers unused),
+// and the two extra parts of the workspace the dispatch blocks read.
+struct FusedArgs {
+    LayoutArgs lay;
+    DispatchArgs disp;
+    uint64_t *tot;  // [E + R] tagged totals
+    uint64_t *tok;  // [T, R + K] tagged final positions, then slots
+};
+
+size_t fused_workspace_bytes(int T, int K, int E, int R);
+hipError_t launch_fused(const FusedArgs &f, bool fp8, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
 
 struct CombineArgs {

@@ -185,6 +185,35 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
                  int32_t *recv_src, int64_t recv_cap_rows, int32_t *pos_exp,
                  hipStream_t stream);
 
+/* Workspace bytes epx_dispatch_fused needs for (T, K, E, R) (host out): the
+ * layout's workspace, then 8 bytes per (expert or rank) and per (token, rank
+ * or top-k entry). Zero-filled before its first use, like the layout's. */
+int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
+
+/* get_dispatch_layout and the high-throughput dispatch in one launch. [P2]
+ * "DeepEP v2": the v2 dispatch kernel computes is_token_in_rank itself
+ * (notify warps in place of get_dispatch_layout) while its dispatch warps
+ * move the data. Arguments and outputs are those of epx_get_dispatch_layout
+ * (topk_idx, C, the counts, is_token_in_rank, offsets, pos_in_rank,
+ * slot_in_expert, channel_prefix, totals, totals_host_mapped) followed by
+ * those of epx_dispatch (x, h, topk_w, fp8 and every send / recv output;
+ * send_x must not be NULL), with the same meaning, layout and errors; the
+ * results are bit-identical to the two calls in sequence. ws: a workspace
+ * of epx_fused_workspace_size bytes, zero-filled before its first use and
+ * left ready by every call; calls that share it must not overlap. The
+ * capacities must be known up front (no host wait happens): T*min(K,R) send
+ * rows and T*K receive rows always suffice. */
+int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
+                       const float *topk_w, int T, int K, int E, int R, int C,
+                       int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
+                       uint8_t *is_token_in_rank, int32_t *rank_off, int32_t *exp_off,
+                       int32_t *pos_in_rank, int32_t *slot_in_expert, int32_t *channel_prefix,
+                       int32_t *totals, int32_t *totals_host_mapped, void *ws, size_t ws_bytes,
+                       int fp8, void *send_x, float *send_scales, int32_t *send_src,
+                       int64_t *send_topk_idx, float *send_topk_w, int64_t send_cap_rows,
+                       void *recv_x, float *recv_scales, int32_t *recv_src,
+                       int64_t recv_cap_rows, int32_t *pos_exp, hipStream_t stream);
+
 /* Combine: reduce expert outputs back to source-token order. [P2] "combine
  * 过程" (route back through the handle, reduce per source token); [P1]
  * "低延迟模式" (combine stays BF16).

@@ -104,3 +104,13 @@ def test_binding_scale_stride():
     with pytest.raises(epx.EpxError) as ei:
         epx.scale_stride(4)
     assert ei.value.code == -1
+
+
+def test_fused_workspace_size(lib):
+    n = ctypes.c_size_t()
+    assert lib.epx_fused_workspace_size(4096, 8, 256, 32, ctypes.byref(n)) == 0
+    # the layout's workspace, the totals row, the tokens' words
+    assert n.value == (128 + 16 * 288 * 8) + 288 * 8 + 4096 * (32 + 8) * 8
+    assert lib.epx_fused_workspace_size(0, 8, 256, 32, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.epx_fused_workspace_size(10, 8, 256, 30, ctypes.byref(n)) == -1

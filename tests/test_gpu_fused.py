@@ -1,0 +1,151 @@
+"""The fused layout + dispatch launch against the oracle: every layout
+output and every dispatch output bit for bit, at full size in the bench's
+launch configuration and on edge shapes; its workspace shared with the
+two-launch layout call; and the step replayed from a HIP graph."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu import CANARY, dev_bf16, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+LAYOUT_KEYS = ["num_tokens_per_expert", "num_tokens_per_rank", "is_token_in_rank", "rank_off",
+               "exp_off", "pos_in_rank", "slot_in_expert", "totals"]
+
+
+def _eq(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    if a.dtype.kind == "f":
+        a, b = a.view(np.uint32), b.view(np.uint32)
+    bad = np.flatnonzero((a != b).ravel())
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:5]}"
+
+
+def _fused_check(x, topk, w, E, R, fp8, C=None, ws=None):
+    import combine_get_dispatch_counts_amd as epx
+
+    T, h = x.shape
+    K = topk.shape[1]
+    dev = torch.device("cuda")
+    cap_s, cap_r = T * min(K, R), T * K
+    bufs = epx.alloc_dispatch(T, h, K, cap_s, cap_r, fp8, dev)
+    for v in bufs.values():
+        if v is not None:
+            v.view(torch.uint8).fill_(CANARY)
+    d = epx.dispatch_fused(dev_bf16(x), torch.from_numpy(topk).cuda(), torch.from_numpy(w).cuda(),
+                           E, R, fp8=fp8, num_channels=C, out=bufs, workspace=ws)
+    flags = epx.get_error()
+    assert flags == 0, f"device flags {flags:#x}"
+    o = oracle.dispatch(x, topk, w, E, R, fp8=fp8)
+    ol = oracle.layout(topk, E, R, C)
+    for k in LAYOUT_KEYS + (["channel_prefix"] if C else []):
+        _eq(host_bits(getattr(d.layout, k)), ol[k], k)
+    n_send, n_recv = (int(v) for v in ol["totals"])
+    keys = ["send_x", "send_src", "send_topk_idx", "send_topk_w", "recv_x", "recv_src"]
+    for k in keys:
+        n = n_send if k.startswith("send") else n_recv
+        _eq(host_bits(getattr(d, k))[:n], o[k], k)
+        rest = host_bits(getattr(d, k))[n:]
+        assert (rest.view(np.uint8) == CANARY).all(), f"rows of {k} past the total were written"
+    _eq(host_bits(d.pos_exp), o["pos_exp"], "pos_exp")
+    if fp8:
+        ngrp = h // 128
+        _eq(host_bits(d.send_scales)[:n_send, :ngrp], o["send_scales"], "send_scales")
+        _eq(host_bits(d.recv_scales)[:n_recv, :ngrp], o["recv_scales"], "recv_scales")
+    return d
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4, 5])
+def test_fused_workloads_full_size(cfg):
+    inp = synth.make_inputs(cfg)
+    wl = inp["workload"]
+    fp8 = wl.fp8 or cfg == 1
+    say(f"fused layout+dispatch {wl.describe()} fp8={fp8}")
+    _fused_check(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, fp8, C=24)
+
+
+@pytest.mark.parametrize("T,K,E,R,h,fp8,kind", [
+    (1, 8, 256, 32, 7168, False, "uniform"), (63, 2, 8, 4, 128, True, "uniform"),
+    (65, 6, 64, 8, 4096, True, "uniform"), (257, 8, 256, 64, 256, True, "dropped"),
+    (200, 4, 16, 1, 1024, False, "dropped"), (300, 32, 64, 8, 136, False, "uniform"),
+    (300, 4, 16, 4, 128, False, "repeats"), (0, 4, 16, 4, 128, False, "uniform"),
+    (513, 4, 128, 8, 512, False, "uniform"),
+])
+def test_fused_edge_cases(T, K, E, R, h, fp8, kind):
+    say(f"fused T={T} K={K} E={E} R={R} h={h} fp8={fp8} {kind}")
+    rng = np.random.default_rng(T + K)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    if kind == "repeats":
+        topk = rng.integers(-1, E, (T, K)).astype(np.int64)
+    else:
+        topk = synth.random_routing(T, K, E, seed=T + 3, p_drop=0.2 if kind == "dropped" else 0.0)
+    w = rng.random((T, K)).astype(np.float32)
+    _fused_check(x, topk, w, E, R, fp8, C=5 if T else None)
+
+
+def test_fused_shares_workspace_with_layout():
+    """One workspace for fused calls and two-launch layout calls in turn."""
+    import combine_get_dispatch_counts_amd as epx
+
+    E, R, K, h = 64, 8, 6, 512
+    ws = torch.zeros(epx.fused_workspace_size(2048, K, E, R), dtype=torch.uint8, device="cuda")
+    for i, T in enumerate([2048, 700, 2048, 1]):
+        rng = np.random.default_rng(40 + i)
+        x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+        topk = synth.random_routing(T, K, E, seed=50 + i)
+        w = rng.random((T, K)).astype(np.float32)
+        say(f"fused call {i} T={T} on a shared workspace")
+        _fused_check(x, topk, w, E, R, False, ws=ws)
+        lay = epx.get_dispatch_layout(torch.from_numpy(topk).cuda(), E, R, workspace=ws)
+        assert epx.get_error() == 0
+        ol = oracle.layout(topk, E, R)
+        for k in LAYOUT_KEYS:
+            _eq(host_bits(getattr(lay, k)), ol[k], f"layout call {i} {k}")
+
+
+def test_fused_step_in_graph():
+    import combine_get_dispatch_counts_amd as epx
+
+    inp = synth.make_inputs(4, T=1024)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    say(f"fused step in a graph T={T}")
+    dev = torch.device("cuda")
+    x, tk, w = dev_bf16(inp["x"]), torch.from_numpy(inp["topk_idx"]).cuda(), \
+        torch.from_numpy(inp["topk_w"]).cuda()
+    ws = torch.zeros(epx.fused_workspace_size(T, K, E, R), dtype=torch.uint8, device=dev)
+    lay = epx.alloc_layout(T, K, E, R, None, dev)
+    bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, False, dev)
+    y = synth.expert_outputs(T * K, h, seed=3, device="cuda")
+    out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        d = epx.dispatch_fused(x, tk, w, E, R, layout=lay, out=bufs, workspace=ws)
+        epx.combine(y, d.pos_exp, w, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [out.clone(), bufs["recv_x"].clone(), lay.pos_in_rank.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for replay in range(3):
+        out.fill_(0)
+        bufs["recv_x"].fill_(0)
+        lay.pos_in_rank.fill_(-7)
+        torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert epx.get_error() == 0
+        for a, b in zip([out, bufs["recv_x"], lay.pos_in_rank], ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {replay} differs"
