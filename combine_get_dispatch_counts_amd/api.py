@@ -295,8 +295,9 @@ def dispatch_fused(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.
                    num_channels: int | None = None, layout: Layout | None = None,
                    out: dict | None = None, workspace: torch.Tensor | None = None,
                    totals_host: torch.Tensor | None = None) -> Dispatched:
-    """get_dispatch_layout and dispatch in one launch (no host wait): the
-    same outputs as the two calls. ``layout`` (from alloc_layout) and
+    """get_dispatch_layout and dispatch in one launch (two when the
+    layout's 256-token tiles outnumber the compute units; no host wait
+    either way): the same outputs as the two calls. ``layout`` (from alloc_layout) and
     ``out`` (from alloc_dispatch) avoid allocating; without ``out`` the
     buffers get the worst-case capacities T*min(K,R) and T*K rows.
     ``workspace`` must hold fused_workspace_size(T, K, E, R) bytes and be

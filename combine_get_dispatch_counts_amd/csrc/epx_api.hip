@@ -69,7 +69,9 @@ int epx_create(epx_ctx **out, int device)
         rc = EPX_EHIP;
     } else {
         c->device = device;
-        if (hipMalloc(reinterpret_cast<void **>(&c->d_err), sizeof(int)) != hipSuccess ||
+        if (hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, device) !=
+                hipSuccess ||
+            hipMalloc(reinterpret_cast<void **>(&c->d_err), sizeof(int)) != hipSuccess ||
             hipMemset(c->d_err, 0, sizeof(int)) != hipSuccess) {
             if (c->d_err)
                 (void)hipFree(c->d_err);
@@ -318,6 +320,7 @@ int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *to
         f.tot = reinterpret_cast<uint64_t *>(base);
         f.tok = f.tot + (E + R);
     }
+    f.cus = ctx->cus;
     return launched(epx::launch_fused(f, fp8 != 0, stream));
 }
 

@@ -8,6 +8,7 @@
 
 struct epx_ctx {
     int device;
+    int cus;     // compute units of the device
     int *d_err;  // device error word (EPX_DEV_* bits)
 };
 
@@ -29,9 +30,11 @@ constexpr int kLayoutThreads = 2 * kLayoutTile;  // two threads per token of a t
 // Head of the layout workspace (the rest: published words [ntiles, E + R]).
 // Zero before the first call; every call leaves it ready for the next.
 struct LayoutHdr {
-    unsigned long long calls;  // calls completed << 32 | blocks of this call arrived;
+    unsigned long long calls;  // calls completed << 32 | layout blocks of this call arrived;
                                // the call's tag (in published words) is calls >> 32, + 1
-    int pad[30];
+    int pad[14];
+    unsigned int done;  // blocks of the current fused call that have finished
+    int pad2[15];
 };
 
 struct LayoutArgs {
@@ -93,8 +96,9 @@ hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream);
 struct FusedArgs {
     LayoutArgs lay;
     DispatchArgs disp;
-    uint64_t *tot;  // [E + R] tagged totals
-    uint64_t *tok;  // [T, R + K] tagged final positions, then slots
+    uint64_t *tot;   // [E + R] tagged totals
+    uint64_t *tok;   // [T, R + K] tagged final positions, then slots
+    int cus;         // compute units of the device
 };
 
 size_t fused_workspace_bytes(int T, int K, int E, int R);

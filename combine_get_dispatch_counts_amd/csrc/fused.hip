@@ -5,27 +5,41 @@
 // notify warps take the place of get_dispatch_layout) while its dispatch
 // warps move the data, in one launch. Here the first blocks of the grid are
 // the layout's blocks (layout_device.h: one per 256-token tile, then the
-// totals block) and the rest are dispatch blocks of kLayoutThreads threads,
-// one wave per token. A dispatch wave issues its row's loads at once, then
-// waits for two things the layout blocks publish as self-contained tagged
-// 64-bit words (tag << 32 | value, the same scheme as the tiles' look-back,
-// so no ordering between different addresses is relied on): the totals
-// (from which each dispatch block scans the offsets into LDS) and its
-// token's final in-rank positions and in-expert slots. It then goes on
-// exactly as the two-launch dispatch does (dispatch_device.h). The layout's
-// own outputs are written as by epx_get_dispatch_layout, for the caller.
+// totals block), and every block of kLayoutThreads threads then dispatches
+// up to one token per wave (dispatch_device.h), so the grid is no larger
+// than the dispatch alone needs: its work is all in flight at once, and
+// extra blocks would only start late and leave a tail that cannot fill HBM.
 //
-// The waits are bounded (flagging EPX_DEV_WORKSPACE), and the layout blocks
-// come first in the grid, so the blocks they wait for are dispatched first.
-// The row loads overlap the layout's critical path; the second launch and
-// the re-read of pos_in_rank / slot_in_expert from memory disappear.
+// Hand-over. The layout blocks publish, beside their usual outputs, the
+// totals and each token's final in-rank positions and in-expert slots as
+// self-contained words (tag << 32 | value, the scheme of the tiles'
+// look-back), so no ordering between different addresses is relied on, and
+// words left in the workspace by earlier calls, of any shape, carry older
+// tags. A block, once the totals are out, scans them into the rank and
+// expert offsets in LDS; each of its waves then waits for its token's
+// R + K words and moves the row.
+//
+// The call's tag. Only the layout blocks take an arrival on the call
+// counter (one word: every block of the grid hitting it at once would
+// serialise for microseconds), and the counter moves on to the next call
+// only when the last block of the grid has finished (a second counter
+// counts finished blocks). The call number is therefore fixed for the
+// whole launch, and a dispatch-only block reads it with one plain load.
+//
+// The layout blocks, once their layout part is done, wait for the totals
+// block like the others, so all layout blocks must be on the chip
+// together: the host uses this kernel only while there are no more of them
+// than compute units (one block per unit always fits), and otherwise runs
+// the layout and the dispatch as two launches. Layout blocks come first in
+// the grid; dispatch-only blocks issue their row loads before waiting, so
+// the loads overlap the layout. Every wait is bounded.
 #include "dispatch_device.h"
 #include "layout_device.h"
 
 namespace epx {
 namespace {
 
-constexpr int kFusedTokens = kLayoutThreads / kWave;  // tokens per dispatch block
+constexpr int kFusedTokens = kLayoutThreads / kWave;  // tokens per block
 
 // Wait until the word each needing lane reads carries the call's tag
 // (bounded; false on time-out). Wave-uniform loop.
@@ -47,95 +61,92 @@ template <int KMAX, bool FP8, int NV>
 __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    if ((int)blockIdx.x <= f.lay.ntiles) {  // the layout's blocks (or T = 0)
-        layout_block<KMAX>(f.lay, lds, f.tok, f.tot);
-        return;
-    }
     const DispatchArgs &a = f.disp;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
-    const int t = (blockIdx.x - f.lay.ntiles - 1) * kFusedTokens + w;
+    const int t = blockIdx.x * kFusedTokens + w;
     const bool have = t < a.T;
     const int ER = a.E + a.R;
     int *tot = reinterpret_cast<int *>(lds + count_lds_bytes(a.E, a.R));
-    int *off = tot + 2 * ER;  // [E+1] expert offsets, then [R+1] rank offsets
-    __shared__ int s_ok;
-    __shared__ uint32_t s_tag;
+    int *off = tot + ER;  // [E+1] expert offsets, then [R+1] rank offsets
 
-    // the row and the token's experts go out first
-    const int64_t tk = (int64_t)t * a.K;
-    const uint16_t *xrow = a.x + (size_t)(have ? t : 0) * a.h;
+    bool go = true;  // block-uniform: false once the layout part was refused
+    uint32_t tag;
     typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
-    if (have)
-        row.load(reinterpret_cast<const u32x4 *>(xrow), 0, FP8 ? a.h >> 4 : a.h >> 3);
-    const int64_t e = (have && lane < a.K) ? a.topk_idx[tk + lane] : -1;
-
-    // this block's arrival on the call counter (every block of the grid takes one)
-    if (tid == 0) {
-        const unsigned long long v = atomicAdd(&f.lay.hdr->calls, 1ull);
-        const uint32_t arrived = (uint32_t)v;
-        s_ok = arrived < gridDim.x;
-        s_tag = (uint32_t)(v >> 32) + 1u;
-        if (arrived == gridDim.x - 1)
-            atomicAdd(&f.lay.hdr->calls, (1ull << 32) - (unsigned long long)gridDim.x);
+    const uint16_t *xrow = a.x + (size_t)(have ? t : 0) * a.h;
+    if ((int)blockIdx.x <= f.lay.ntiles) {  // a layout block (or T = 0)
+        go = layout_block<KMAX>(f.lay, lds, f.tok, f.tot, false, tag);
+        if (f.lay.ntiles == 0)  // T = 0: one block, no counters involved
+            return;
+        __syncthreads();  // the layout's LDS is reused below
+        if (go && have)
+            row.load(reinterpret_cast<const u32x4 *>(xrow), 0, FP8 ? a.h >> 4 : a.h >> 3);
+    } else {
+        if (have)
+            row.load(reinterpret_cast<const u32x4 *>(xrow), 0, FP8 ? a.h >> 4 : a.h >> 3);
+        tag = (uint32_t)(__hip_atomic_load(&f.lay.hdr->calls, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) >> 32) + 1u;
     }
-    __syncthreads();
-    const uint32_t tag = s_tag;
-    if (!s_ok) {
-        if (tid == 0)
-            flag_error(a.err, EPX_DEV_WORKSPACE);
-        return;
-    }
+    const int64_t e = (have && lane < a.K) ? a.topk_idx[(int64_t)t * a.K + lane] : -1;
 
-    // the totals, then the offsets scanned once per block into LDS
-    if (w == 0) {
-        bool ok = true;
-        for (int c0 = 0; c0 < ER; c0 += kWave) {
+    if (go) {
+        // the totals, 64 words per wave, then the offsets scanned into LDS
+        for (int c0 = w * kWave; c0 < ER; c0 += kFusedTokens * kWave) {
             const int c = c0 + lane;
             uint64_t word;
-            ok &= wait_tagged(f.tot + min(c, ER - 1), c < ER, tag, word);
+            if (!wait_tagged(f.tot + min(c, ER - 1), c < ER, tag, word) && lane == 0)
+                flag_error(a.err, EPX_DEV_WORKSPACE);
             if (c < ER)
                 tot[c] = (int)((uint32_t)word & 0x7FFFFFFFu);
         }
-        if (!ok && lane == 0)
+        __syncthreads();
+        if (tid < kWave)
+            wave_exclusive_scan(tot, a.E, off);
+        else if (tid < 2 * kWave)
+            wave_exclusive_scan(tot + a.E, a.R, off + a.E + 1);
+        __syncthreads();
+    }
+    if (go && have) {
+        // the token's final positions (lane r < R) and slots (lane k < K)
+        const uint64_t *tw = f.tok + (int64_t)t * (a.R + a.K);
+        uint64_t pw, sw;
+        const bool ok_p = wait_tagged(tw + min(lane, a.R - 1), lane < a.R, tag, pw);
+        const bool ok_s = wait_tagged(tw + a.R + min(lane, a.K - 1), lane < a.K, tag, sw);
+        if (!(ok_p && ok_s) && lane == 0)
             flag_error(a.err, EPX_DEV_WORKSPACE);
+        int64_t send_r = -1, recv_r = -1;
+        if (ok_p && lane < a.R) {
+            const int p = (int)(uint32_t)pw;
+            if (p >= 0)
+                send_r = (int64_t)off[a.E + 1 + lane] + p;
+        }
+        if (ok_s && e >= 0 && e < a.E) {
+            const int sl = (int)(uint32_t)sw;
+            recv_r = sl >= 0 ? (int64_t)off[(int)e] + sl : -1;
+        }
+        dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r);
     }
-    __syncthreads();
-    if (tid < kWave)
-        wave_exclusive_scan(tot, a.E, off);
-    else if (tid < 2 * kWave)
-        wave_exclusive_scan(tot + a.E, a.R, off + a.E + 1);
-    __syncthreads();
-    if (!have)
-        return;
 
-    // the token's final positions (lane r < R) and slots (lane k < K)
-    const uint64_t *tw = f.tok + (int64_t)t * (a.R + a.K);
-    uint64_t pw, sw;
-    const bool ok_p = wait_tagged(tw + min(lane, a.R - 1), lane < a.R, tag, pw);
-    const bool ok_s = wait_tagged(tw + a.R + min(lane, a.K - 1), lane < a.K, tag, sw);
-    if (!(ok_p && ok_s) && lane == 0)
-        flag_error(a.err, EPX_DEV_WORKSPACE);
-    int64_t send_r = -1, recv_r = -1;
-    if (ok_p && lane < a.R) {
-        const int p = (int)(uint32_t)pw;
-        if (p >= 0)
-            send_r = (int64_t)off[a.E + 1 + lane] + p;
+    // this block is done: the last block of the grid opens the next call
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned int n = atomicAdd(&f.lay.hdr->done, 1u);
+        if (n == gridDim.x - 1) {
+            __hip_atomic_store(&f.lay.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            atomicAdd(&f.lay.hdr->calls,
+                      (1ull << 32) - (unsigned long long)(f.lay.ntiles + 1));
+        }
     }
-    const bool valid = e >= 0 && e < a.E;
-    if (ok_s && valid) {
-        const int sl = (int)(uint32_t)sw;
-        recv_r = sl >= 0 ? (int64_t)off[(int)e] + sl : -1;
-    }
-    dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r);
 }
 
 template <int KMAX, bool FP8, int NV>
 void launch_fused_k(const FusedArgs &f, hipStream_t stream)
 {
     const int64_t disp_blocks = (f.disp.T + kFusedTokens - 1) / kFusedTokens;
-    const int64_t blocks = f.lay.ntiles > 0 ? f.lay.ntiles + 1 + disp_blocks : 1;
+    const int64_t nlay = f.lay.ntiles + 1;
+    const int64_t blocks = f.lay.ntiles == 0 ? 1 : (disp_blocks > nlay ? disp_blocks : nlay);
     hipLaunchKernelGGL((fused_kernel<KMAX, FP8, NV>), dim3((unsigned)blocks),
-                       dim3(kLayoutThreads), layout_lds_bytes(f.lay.E, f.lay.R), stream, f);
+                       dim3(kLayoutThreads), layout_tok_lds_bytes(f.lay.E, f.lay.R, f.lay.K), stream,
+                       f);
 }
 
 template <int KMAX>
@@ -164,6 +175,10 @@ size_t fused_workspace_bytes(int T, int K, int E, int R)
 
 hipError_t launch_fused(const FusedArgs &f, bool fp8, hipStream_t stream)
 {
+    if (f.lay.ntiles + 1 > f.cus) {  // the layout blocks might not all fit at once
+        const hipError_t e = launch_layout(f.lay, stream);
+        return e != hipSuccess ? e : launch_dispatch(f.disp, fp8, stream);
+    }
     if (f.lay.K <= 8)
         launch_fused_kmax<8>(f, fp8, stream);
     else

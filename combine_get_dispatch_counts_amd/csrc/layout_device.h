@@ -8,7 +8,8 @@
 // [P2] "DeepEP v2": a token counts once per destination rank.
 //
 // One launch, deterministic results:
-//   Block b handles tile b of 256 tokens (4 waves, one token per lane).
+//   Block b handles tile b of 256 tokens (8 waves; two threads per token:
+//   the first 256 count, all share the writes).
 //   Workgroups are dispatched in index order, so a tile waits only for
 //   tiles that are running or done; with a few hundred tiles they are all
 //   resident at once anyway. Each wave ORs its lanes into LDS bitmaps:
@@ -25,8 +26,10 @@
 //   from past the last tile: that prefix is the totals, from which it
 //   writes the counts, offsets and totals while the tiles write rows.
 //   A 64-bit counter in the workspace (call number << 32 | blocks arrived)
-//   gives every block the call's tag in one atomic, issued beside the topk
-//   loads; the last block to arrive moves it on to the next call. Waits are
+//   gives every layout block (tiles and the totals block) the call's tag in
+//   one atomic, issued beside the topk loads; the last of them to arrive
+//   moves it on to the next call (in the fused launch, the last block of
+//   the grid to finish does). Waits are
 //   bounded: a tile that waits too long flags EPX_DEV_WORKSPACE and goes
 //   on, so the kernel always ends.
 // A wave in which some token lists one expert twice counts earlier entries
@@ -76,6 +79,13 @@ __device__ CountLds carve_count(char *base, int E, int R)
 __host__ __device__ inline size_t layout_lds_bytes(int E, int R)
 {
     return count_lds_bytes(E, R) + sizeof(int) * (3 * (size_t)(E + R) + 2);
+}
+
+// With the per-token words published (the fused launch): the tile's slot
+// values staged after that.
+__host__ __device__ inline size_t layout_tok_lds_bytes(int E, int R, int K)
+{
+    return layout_lds_bytes(E, R) + sizeof(int) * (size_t)kLayoutTile * K;
 }
 
 // Published words: (tag << 32) | inclusive bit 31 | value (< 2^31). A word
@@ -148,14 +158,6 @@ __device__ bool look_back(const uint64_t *pub, int ER, int tile, int self, int c
     }
     *out = (int)acc;
     return true;
-}
-
-// Publish 4 consecutive values of a token's tagged word row (tok != null).
-__device__ __forceinline__ void publish4(uint64_t *tok_words, uint64_t tagw, const int (&v)[4])
-{
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        pub_store(tok_words + j, tagw | (uint32_t)v[j]);
 }
 
 // Flat index walker over a [rows, cols] row-major block: thread tid starts
@@ -310,18 +312,26 @@ __device__ void write_totals(const LayoutArgs &a, const int *tot, int *off)
 }
 
 // The work of one layout block: the totals for T = 0, the totals block
-// (blockIdx == ntiles), or tile blockIdx. Every block of the launch takes
-// one arrival on the workspace counter (see the kernel's header comment).
-// tok, if not null, also receives each token's final pos_in_rank and
-// slot_in_expert values as tagged words [T][R + K] (tag << 32 | value), and
-// tot_row the totals as tagged words [E + R]: published so blocks of the
-// same launch can read them without waiting for the launch to end.
+// (blockIdx == ntiles), or tile blockIdx. Every layout block of the launch
+// takes one arrival on the workspace counter (see the kernel's header
+// comment). tot_row, if not null, also receives the totals as tagged words
+// [E + R] (tag << 32 | inclusive bit | value), and tok each token's final
+// pos_in_rank and slot_in_expert values as tagged words [T][R + K]
+// (tag << 32 | value): published so blocks of the same launch can read them
+// without waiting for the launch to end. With tok, the block's LDS must
+// hold layout_tok_lds_bytes.
+// Returns false when the block's arrival was refused (flagged), else true
+// with the call's tag in tag_out (T = 0 takes no arrival: tag_out is 0).
+// With advance, the last layout block to arrive opens the next call; the
+// fused kernel passes false and opens it when its last block has finished.
 template <int KMAX>
-__device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uint64_t *tok,
-                                             uint64_t *tot_row)
+__device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uint64_t *tok,
+                                             uint64_t *tot_row, bool advance, uint32_t &tag_out)
 {
     const CountLds s = carve_count(lds, a.E, a.R);
     const int ER = a.E + a.R;
+    // the tile's slot values, staged for the word run (with tok only)
+    int *slot_lds = tok ? reinterpret_cast<int *>(lds + layout_lds_bytes(a.E, a.R)) : nullptr;
     int *agg = reinterpret_cast<int *>(lds + count_lds_bytes(a.E, a.R));
     int *pre = agg + ER, *off = pre + ER;
     __shared__ int s_ok;
@@ -336,7 +346,8 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
         if (a.channel_prefix)
             for (int i = tid; i < a.R * a.C; i += blockDim.x)
                 a.channel_prefix[i] = 0;
-        return;
+        tag_out = 0;
+        return true;
     }
 
     // Threads tid and tid + 256 both hold token tid of the tile: the first
@@ -354,10 +365,11 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
     if (tid == 0) {
         const unsigned long long v = atomicAdd(&a.hdr->calls, 1ull);
         const uint32_t arrived = (uint32_t)v;
-        s_ok = arrived < gridDim.x;
+        const uint32_t nblk = (uint32_t)a.ntiles + 1u;  // the layout blocks
+        s_ok = arrived < nblk;
         s_tag = (uint32_t)(v >> 32) + 1u;
-        if (arrived == gridDim.x - 1)  // all blocks are in: open the next call
-            atomicAdd(&a.hdr->calls, (1ull << 32) - (unsigned long long)gridDim.x);
+        if (advance && arrived == nblk - 1)  // all layout blocks are in: open the next call
+            atomicAdd(&a.hdr->calls, (1ull << 32) - (unsigned long long)nblk);
     }
 
     // The block after the last tile: the totals are the inclusive prefix
@@ -367,8 +379,9 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
         if (!s_ok) {
             if (tid == 0)
                 flag_error(a.err, EPX_DEV_WORKSPACE);
-            return;
+            return false;
         }
+        tag_out = s_tag;
         for (int c = tid; c < ER; c += blockDim.x) {
             int p = 0;
             if (!look_back(a.pub, ER, a.ntiles, a.ntiles - 1, c, s_tag, &p))
@@ -379,7 +392,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
         }
         __syncthreads();
         write_totals(a, agg, off);
-        return;
+        return true;
     }
     for (int i = tid; i < W * a.E; i += blockDim.x) {
         s.emask[i] = 0;
@@ -418,10 +431,11 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
         s.dupwave[w] = 1;
     __syncthreads();
     const uint32_t tag = s_tag;
+    tag_out = tag;
     if (!s_ok) {  // the counter was not left by a previous call: give up
         if (tid == 0)
             flag_error(a.err, EPX_DEV_WORKSPACE);
-        return;
+        return false;
     }
 
     // wave prefixes inside the tile and the tile's counts, published at
@@ -495,9 +509,6 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
                     v[j] = ((rbt >> j) & 1ull) ? base[j] + __popcll(rm[j] & below) : -1;
                 *reinterpret_cast<u32x4 *>(dst + (int64_t)q * 4) =
                     u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
-                if (tok)
-                    publish4(tok + (int64_t)(tile_base + tt) * (a.R + a.K) + r0,
-                             (uint64_t)tag << 32, v);
             }
         }
     } else if ((a.R & 3) == 0) {
@@ -518,22 +529,14 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
             }
             *reinterpret_cast<u32x4 *>(dst + (int64_t)q * 4) =
                 u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
-            if (tok)
-                publish4(tok + (int64_t)(tile_base + tt) * (a.R + a.K) + r0, (uint64_t)tag << 32,
-                         v);
         }
     } else if (counter && t < a.T) {
         const uint64_t below = lanes_below(lane);
         int32_t *pir = a.pos_in_rank + (int64_t)t * a.R;
-        for (int r = 0; r < a.R; ++r) {
-            const int pv = ((rbits >> r) & 1ull) ? pre[a.E + r] + s.wpre_r[w * a.R + r] +
-                                                       __popcll(s.rmask[w * a.R + r] & below)
-                                                 : -1;
-            pir[r] = pv;
-            if (tok)
-                pub_store(tok + (int64_t)t * (a.R + a.K) + r,
-                          ((uint64_t)tag << 32) | (uint32_t)pv);
-        }
+        for (int r = 0; r < a.R; ++r)
+            pir[r] = ((rbits >> r) & 1ull) ? pre[a.E + r] + s.wpre_r[w * a.R + r] +
+                                                 __popcll(s.rmask[w * a.R + r] & below)
+                                           : -1;
     }
 
     if (t < a.T) {
@@ -552,12 +555,11 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
                        ? pre[e] + s.wpre_e[wt * a.E + e] + wave_rank(a, s, tile_base, tt0, k, e)
                        : -1;
         }
-        if (tok) {
+        if (slot_lds) {
 #pragma unroll
             for (int k = 0; k < KMAX; ++k)
                 if (k >= k_lo && k < k_hi)
-                    pub_store(tok + (int64_t)t * (a.R + a.K) + a.R + k,
-                              ((uint64_t)tag << 32) | (uint32_t)v[k]);
+                    slot_lds[tt0 * a.K + k] = v[k];
         }
         if ((a.K & 3) == 0) {
 #pragma unroll
@@ -571,6 +573,29 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
             for (int k = 0; k < KMAX; ++k)
                 if (k >= k_lo && k < k_hi)
                     sie[k] = v[k];
+        }
+    }
+
+    // the tile's tokens' words, one contiguous run (consecutive lanes,
+    // consecutive words): positions recomputed from the bitmaps, then slots
+    if (tok) {
+        __syncthreads();
+        const int RK = a.R + a.K;
+        uint64_t *dst = tok + (int64_t)tile_base * RK;
+        const uint64_t tagw = (uint64_t)tag << 32;
+        for (int i = tid; i < ntok * RK; i += blockDim.x) {
+            const int tt = i / RK, j = i - tt * RK;
+            int v;
+            if (j < a.R) {
+                const int ww = tt >> 6;
+                v = ((s.rb[tt] >> j) & 1ull) ? pre[a.E + j] + s.wpre_r[ww * a.R + j] +
+                                                   __popcll(s.rmask[ww * a.R + j] &
+                                                            lanes_below(tt & 63))
+                                             : -1;
+            } else {
+                v = slot_lds[tt * a.K + (j - a.R)];
+            }
+            pub_store(dst + i, tagw | (uint32_t)v);
         }
     }
 
@@ -594,7 +619,7 @@ __device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds, uin
             a.channel_prefix[i] = v;
         }
     }
-
+    return true;
 }
 
 }  // namespace

@@ -186,8 +186,9 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
                  hipStream_t stream);
 
 /* Workspace bytes epx_dispatch_fused needs for (T, K, E, R) (host out): the
- * layout's workspace, then 8 bytes per (expert or rank) and per (token, rank
- * or top-k entry). Zero-filled before its first use, like the layout's. */
+ * layout's workspace, then 8 bytes per expert and per rank and per (token,
+ * rank or top-k entry). Zero-filled before its first use, like the
+ * layout's. */
 int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
 
 /* get_dispatch_layout and the high-throughput dispatch in one launch. [P2]
@@ -200,9 +201,13 @@ int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
  * send_x must not be NULL), with the same meaning, layout and errors; the
  * results are bit-identical to the two calls in sequence. ws: a workspace
  * of epx_fused_workspace_size bytes, zero-filled before its first use and
- * left ready by every call; calls that share it must not overlap. The
+ * left ready by every call (after an EPX_DEV_WORKSPACE flag, zero it
+ * again); calls that share it must not overlap, and it may be shared with
+ * epx_get_dispatch_layout calls of any shape. The
  * capacities must be known up front (no host wait happens): T*min(K,R) send
- * rows and T*K receive rows always suffice. */
+ * rows and T*K receive rows always suffice. One launch while the layout's
+ * tiles (ceil(T/256)) number fewer than the device's compute units, else the
+ * layout and the dispatch are launched one after the other. */
 int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
                        const float *topk_w, int T, int K, int E, int R, int C,
                        int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,

@@ -87,6 +87,21 @@ def test_fused_edge_cases(T, K, E, R, h, fp8, kind):
     _fused_check(x, topk, w, E, R, fp8, C=5 if T else None)
 
 
+@pytest.mark.parametrize("extra", [0, 1])
+def test_fused_both_grid_shapes(extra):
+    """One launch while the layout blocks fit on the chip at one block per
+    compute unit (tiles + 1 <= CUs); one tile more and the layout and the
+    dispatch run as two launches. Both sides of that edge."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    T, K, E, R, h = (cus - 1) * 256 + extra, 4, 64, 8, 128
+    say(f"fused T={T} ({'two launches' if extra else 'one launch'}, {cus} CUs)")
+    rng = np.random.default_rng(T)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=T + 1, p_drop=0.1)
+    w = rng.random((T, K)).astype(np.float32)
+    _fused_check(x, topk, w, E, R, bool(extra))
+
+
 def test_fused_shares_workspace_with_layout():
     """One workspace for fused calls and two-launch layout calls in turn."""
     import combine_get_dispatch_counts_amd as epx
@@ -100,8 +115,16 @@ def test_fused_shares_workspace_with_layout():
         w = rng.random((T, K)).astype(np.float32)
         say(f"fused call {i} T={T} on a shared workspace")
         _fused_check(x, topk, w, E, R, False, ws=ws)
+        # the counters are left ready: one more call completed, no block of
+        # a call pending (head: calls << 32 | arrivals at byte 0, finished
+        # blocks of a fused call at byte 64)
+        head = ws[:128].cpu().numpy()
+        calls = int(head[:8].view(np.uint64)[0])
+        assert calls == (2 * i + 1) << 32, f"call counter {calls:#x} after fused call {i}"
+        assert int(head[64:68].view(np.uint32)[0]) == 0, "finished-block counter not reset"
         lay = epx.get_dispatch_layout(torch.from_numpy(topk).cuda(), E, R, workspace=ws)
         assert epx.get_error() == 0
+        assert int(ws[:8].cpu().numpy().view(np.uint64)[0]) == (2 * i + 2) << 32
         ol = oracle.layout(topk, E, R)
         for k in LAYOUT_KEYS:
             _eq(host_bits(getattr(lay, k)), ol[k], f"layout call {i} {k}")
