@@ -124,3 +124,57 @@ def test_low_latency_step_in_graph():
         assert epx.get_error() == 0
         _same(_snapshot(watched), ref, f"replay {replay}")
     assert np.all(buf.ll_count.cpu().numpy() >= 0)
+
+
+def test_low_latency_ping_pong_in_graph():
+    """Two low-latency steps on a ping-pong pair captured in one graph: each
+    dispatch resets the other buffer's counts, so no reset launch is
+    captured. Every replay reproduces the eager outputs, and the counts of
+    the buffer filled last match the oracle."""
+    import combine_get_dispatch_counts_amd as epx
+    import oracle
+
+    inp = synth.make_inputs(2, T=64)
+    wl = inp["workload"]
+    T, h, E, R, K, cap = wl.T, wl.h, wl.E, wl.R, wl.K, 64
+    say(f"graph LL ping-pong T={T} h={h} E={E} R={R} K={K} cap={cap}")
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(6)
+    x2 = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk2 = synth.random_routing(T, K, E, seed=7, p_drop=0.1)
+    xs = [dev_bf16(inp["x"]), dev_bf16(x2)]
+    tks = [torch.from_numpy(inp["topk_idx"]).cuda(), torch.from_numpy(topk2).cuda()]
+    ws = [torch.from_numpy(inp["topk_w"]).cuda(), torch.from_numpy(rng.random((T, K)).astype(
+        np.float32)).cuda()]
+    bufs = [epx.alloc_ll(E, 1, cap, h, T, K, True, dev) for _ in range(2)]
+    ys = [synth.expert_outputs(E * cap, h, seed=8 + i, device="cuda") for i in range(2)]
+    outs = [torch.empty((T, h), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    for b in bufs:
+        _scribble([b.ll_x, b.ll_scales, b.ll_src])
+
+    def step():
+        for i in range(2):
+            epx.ll_dispatch(xs[i], tks[i], E, R, 3, cap, 1, True, bufs[i], next_buf=bufs[1 - i])
+            epx.combine(ys[i], bufs[i].pos_ll, ws[i], out=outs[i])
+
+    watched = [bufs[1].ll_count, bufs[0].ll_count] + outs + [b.pos_ll for b in bufs]
+    step()
+    step()
+    torch.cuda.synchronize()
+    assert epx.get_error() == 0
+    ref = _snapshot(watched)
+    o = oracle.ll_dispatch(x2, topk2, E, R, 3, cap, 1, fp8=True)
+    np.testing.assert_array_equal(bufs[1].ll_count.cpu().numpy(), o["ll_count"])
+    assert (bufs[0].ll_count.cpu().numpy() == -1).all(), "the first buffer was not reset"
+    g = _capture(step)
+    for replay in range(3):
+        for t in outs:
+            t.zero_()
+        for b in bufs:
+            b.pos_ll.fill_(-3)
+        torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert epx.get_error() == 0
+        _same(_snapshot(watched), ref, f"replay {replay}")
