@@ -19,12 +19,13 @@
 // expert offsets in LDS; each of its waves then waits for its token's
 // R + K words and moves the row.
 //
-// The call's tag. Only the layout blocks take an arrival on the call
-// counter (one word: every block of the grid hitting it at once would
-// serialise for microseconds), and the counter moves on to the next call
-// only when the last block of the grid has finished (a second counter
-// counts finished blocks). The call number is therefore fixed for the
-// whole launch, and a dispatch-only block reads it with one plain load.
+// The call's tag. No block takes an arrival on the call counter (one
+// word: every block of the grid hitting it at once would serialise for
+// microseconds): the counter moves on to the next call only when the last
+// block of the grid has finished (a second counter counts finished
+// blocks), so the call number is fixed for the whole launch and every
+// block reads it with one plain load, checking on the way that no layout
+// call was left unfinished (arrivals 0).
 //
 // The layout blocks, once their layout part is done, wait for the totals
 // block like the others, so all layout blocks must be on the chip
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
     const uint16_t *xrow = a.x + (size_t)(have ? t : 0) * a.h;
     if ((int)blockIdx.x <= f.lay.ntiles) {  // a layout block (or T = 0)
-        go = layout_block<KMAX>(f.lay, lds, f.tok, f.tot, false, tag);
+        go = layout_block<KMAX>(f.lay, lds, f.tok, f.tot, false, tag);  // flags if refused
         if (f.lay.ntiles == 0)  // T = 0: one block, no counters involved
             return;
         __syncthreads();  // the layout's LDS is reused below
@@ -83,8 +84,17 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     } else {
         if (have)
             row.load(reinterpret_cast<const u32x4 *>(xrow), 0, FP8 ? a.h >> 4 : a.h >> 3);
-        tag = (uint32_t)(__hip_atomic_load(&f.lay.hdr->calls, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) >> 32) + 1u;
+        __shared__ int s_go;
+        const unsigned long long v =
+            __hip_atomic_load(&f.lay.hdr->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tag = (uint32_t)(v >> 32) + 1u;
+        if (tid == 0) {
+            s_go = (uint32_t)v == 0u;
+            if (!s_go)
+                flag_error(a.err, EPX_DEV_WORKSPACE);
+        }
+        __syncthreads();
+        go = s_go;
     }
     const int64_t e = (have && lane < a.K) ? a.topk_idx[(int64_t)t * a.K + lane] : -1;
 
@@ -132,8 +142,7 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
         const unsigned int n = atomicAdd(&f.lay.hdr->done, 1u);
         if (n == gridDim.x - 1) {
             __hip_atomic_store(&f.lay.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            atomicAdd(&f.lay.hdr->calls,
-                      (1ull << 32) - (unsigned long long)(f.lay.ntiles + 1));
+            atomicAdd(&f.lay.hdr->calls, 1ull << 32);
         }
     }
 }

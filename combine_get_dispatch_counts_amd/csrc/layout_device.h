@@ -28,10 +28,10 @@
 //   A 64-bit counter in the workspace (call number << 32 | blocks arrived)
 //   gives every layout block (tiles and the totals block) the call's tag in
 //   one atomic, issued beside the topk loads; the last of them to arrive
-//   moves it on to the next call (in the fused launch, the last block of
-//   the grid to finish does). Waits are
-//   bounded: a tile that waits too long flags EPX_DEV_WORKSPACE and goes
-//   on, so the kernel always ends.
+//   moves it on to the next call. (The fused launch takes no arrivals: its
+//   blocks read the call number, and its last block to finish moves it
+//   on.) Waits are bounded: a tile that waits too long flags
+//   EPX_DEV_WORKSPACE and goes on, so the kernel always ends.
 // A wave in which some token lists one expert twice counts earlier entries
 // directly instead, so a slot stays "entries before (t,k)" exactly.
 #pragma once
@@ -320,13 +320,16 @@ __device__ void write_totals(const LayoutArgs &a, const int *tot, int *off)
 // (tag << 32 | value): published so blocks of the same launch can read them
 // without waiting for the launch to end. With tok, the block's LDS must
 // hold layout_tok_lds_bytes.
-// Returns false when the block's arrival was refused (flagged), else true
-// with the call's tag in tag_out (T = 0 takes no arrival: tag_out is 0).
-// With advance, the last layout block to arrive opens the next call; the
-// fused kernel passes false and opens it when its last block has finished.
+// With arrive, the block takes an arrival on the call counter and the last
+// layout block to arrive opens the next call. Without (the fused kernel,
+// whose last block to finish opens it), the block reads the call number,
+// which stays fixed for the whole launch, and checks that no call was left
+// unfinished. Returns false when the workspace was not left ready
+// (flagged), else true with the call's tag in tag_out (T = 0 touches no
+// counter: tag_out is 0).
 template <int KMAX>
 __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uint64_t *tok,
-                                             uint64_t *tot_row, bool advance, uint32_t &tag_out)
+                                             uint64_t *tot_row, bool arrive, uint32_t &tag_out)
 {
     const CountLds s = carve_count(lds, a.E, a.R);
     const int ER = a.E + a.R;
@@ -363,13 +366,20 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
     if (tile < a.ntiles)
         load_row_experts<KMAX>(a, t, ek);
     if (tid == 0) {
-        const unsigned long long v = atomicAdd(&a.hdr->calls, 1ull);
-        const uint32_t arrived = (uint32_t)v;
         const uint32_t nblk = (uint32_t)a.ntiles + 1u;  // the layout blocks
-        s_ok = arrived < nblk;
-        s_tag = (uint32_t)(v >> 32) + 1u;
-        if (advance && arrived == nblk - 1)  // all layout blocks are in: open the next call
-            atomicAdd(&a.hdr->calls, (1ull << 32) - (unsigned long long)nblk);
+        if (arrive) {
+            const unsigned long long v = atomicAdd(&a.hdr->calls, 1ull);
+            const uint32_t arrived = (uint32_t)v;
+            s_ok = arrived < nblk;
+            s_tag = (uint32_t)(v >> 32) + 1u;
+            if (arrived == nblk - 1)  // all layout blocks are in: open the next call
+                atomicAdd(&a.hdr->calls, (1ull << 32) - (unsigned long long)nblk);
+        } else {
+            const unsigned long long v =
+                __hip_atomic_load(&a.hdr->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_ok = (uint32_t)v == 0u;
+            s_tag = (uint32_t)(v >> 32) + 1u;
+        }
     }
 
     // The block after the last tile: the totals are the inclusive prefix
@@ -471,6 +481,67 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
     }
     __syncthreads();
 
+    if (t < a.T) {
+        // slot of each entry among the entries of its expert, else -1; the
+        // two threads of a token take half the entries each when K % 8 == 0
+        const int wt = tt0 >> 6;
+        const bool halves = (a.K & 7) == 0;
+        const int k_lo = halves ? (tid >> 8) * (a.K >> 1) : 0;
+        const int k_hi = halves ? k_lo + (a.K >> 1) : (counter ? a.K : 0);
+        int32_t *sie = a.slot_in_expert + (int64_t)t * a.K;
+        int v[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int e = ek[k];
+            v[k] = (e >= 0 && k >= k_lo && k < k_hi)
+                       ? pre[e] + s.wpre_e[wt * a.E + e] + wave_rank(a, s, tile_base, tt0, k, e)
+                       : -1;
+        }
+        if (slot_lds) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (k >= k_lo && k < k_hi)
+                    slot_lds[tt0 * a.K + k] = v[k];
+        }
+        if ((a.K & 3) == 0) {
+#pragma unroll
+            for (int k0 = 0; k0 < KMAX; k0 += 4)
+                if (k0 >= k_lo && k0 < k_hi)
+                    *reinterpret_cast<u32x4 *>(sie + k0) =
+                        u32x4{(uint32_t)v[k0], (uint32_t)v[k0 + 1], (uint32_t)v[k0 + 2],
+                              (uint32_t)v[k0 + 3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (k >= k_lo && k < k_hi)
+                    sie[k] = v[k];
+        }
+    }
+
+    // the tile's tokens' words, one contiguous run (consecutive lanes,
+    // consecutive words): positions recomputed from the bitmaps, then slots;
+    // published before the tile's own output rows, which only the caller reads
+    if (tok) {
+        __syncthreads();
+        const int RK = a.R + a.K;
+        uint64_t *dst = tok + (int64_t)tile_base * RK;
+        const uint64_t tagw = (uint64_t)tag << 32;
+        for (int i = tid; i < ntok * RK; i += blockDim.x) {
+            const int tt = i / RK, j = i - tt * RK;
+            int v;
+            if (j < a.R) {
+                const int ww = tt >> 6;
+                v = ((s.rb[tt] >> j) & 1ull) ? pre[a.E + j] + s.wpre_r[ww * a.R + j] +
+                                                   __popcll(s.rmask[ww * a.R + j] &
+                                                            lanes_below(tt & 63))
+                                             : -1;
+            } else {
+                v = slot_lds[tt * a.K + (j - a.R)];
+            }
+            pub_store(dst + i, tagw | (uint32_t)v);
+        }
+    }
+
     // is_token_in_rank and pos_in_rank rows of the tile are contiguous:
     // write them as one block, 16 bytes per thread per step
     if ((a.R & 15) == 0) {
@@ -537,66 +608,6 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
             pir[r] = ((rbits >> r) & 1ull) ? pre[a.E + r] + s.wpre_r[w * a.R + r] +
                                                  __popcll(s.rmask[w * a.R + r] & below)
                                            : -1;
-    }
-
-    if (t < a.T) {
-        // slot of each entry among the entries of its expert, else -1; the
-        // two threads of a token take half the entries each when K % 8 == 0
-        const int wt = tt0 >> 6;
-        const bool halves = (a.K & 7) == 0;
-        const int k_lo = halves ? (tid >> 8) * (a.K >> 1) : 0;
-        const int k_hi = halves ? k_lo + (a.K >> 1) : (counter ? a.K : 0);
-        int32_t *sie = a.slot_in_expert + (int64_t)t * a.K;
-        int v[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const int e = ek[k];
-            v[k] = (e >= 0 && k >= k_lo && k < k_hi)
-                       ? pre[e] + s.wpre_e[wt * a.E + e] + wave_rank(a, s, tile_base, tt0, k, e)
-                       : -1;
-        }
-        if (slot_lds) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (k >= k_lo && k < k_hi)
-                    slot_lds[tt0 * a.K + k] = v[k];
-        }
-        if ((a.K & 3) == 0) {
-#pragma unroll
-            for (int k0 = 0; k0 < KMAX; k0 += 4)
-                if (k0 >= k_lo && k0 < k_hi)
-                    *reinterpret_cast<u32x4 *>(sie + k0) =
-                        u32x4{(uint32_t)v[k0], (uint32_t)v[k0 + 1], (uint32_t)v[k0 + 2],
-                              (uint32_t)v[k0 + 3]};
-        } else {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (k >= k_lo && k < k_hi)
-                    sie[k] = v[k];
-        }
-    }
-
-    // the tile's tokens' words, one contiguous run (consecutive lanes,
-    // consecutive words): positions recomputed from the bitmaps, then slots
-    if (tok) {
-        __syncthreads();
-        const int RK = a.R + a.K;
-        uint64_t *dst = tok + (int64_t)tile_base * RK;
-        const uint64_t tagw = (uint64_t)tag << 32;
-        for (int i = tid; i < ntok * RK; i += blockDim.x) {
-            const int tt = i / RK, j = i - tt * RK;
-            int v;
-            if (j < a.R) {
-                const int ww = tt >> 6;
-                v = ((s.rb[tt] >> j) & 1ull) ? pre[a.E + j] + s.wpre_r[ww * a.R + j] +
-                                                   __popcll(s.rmask[ww * a.R + j] &
-                                                            lanes_below(tt & 63))
-                                             : -1;
-            } else {
-                v = slot_lds[tt * a.K + (j - a.R)];
-            }
-            pub_store(dst + i, tagw | (uint32_t)v);
-        }
     }
 
     // the channel columns whose last token lies in this tile
