@@ -55,13 +55,14 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
 // waves: together they histogram all T*K entries in LDS (decode batches are
 // small) -- the full histogram gives the count slots, the part before token
 // t gives t's slots; LDS atomics only add, so the result does not depend on
-// their order -- then wave w loads and quantises the row itself (the other
-// waves' copies come from L2) and writes the entries k with k % kLLWaves ==
-// w. A decode batch has few tokens, so one wave per token would leave most
-// of the chip idle and each wave writing K rows in turn.
+// their order. The row is cut into 1024-channel slices (eight 128-channel
+// scale groups): wave w loads, quantises and stores slices w, w + kLLWaves,
+// .. to every destination of the token, so the row is read once, each
+// element is quantised once, and a decode batch's few tokens still spread
+// their work over many waves.
 constexpr int kLLWaves = 8;
 
-template <bool FP8, int NV>
+template <bool FP8>
 __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
 {
     extern __shared__ int hist[];  // [E] all entries, [E] entries before token t
@@ -70,15 +71,18 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
     int *hist_all = hist, *hist_before = hist + a.E;
     const bool have_token = t < a.T;
     const int64_t tk = (int64_t)t * a.K;
-    const uint16_t *xrow = a.x + (size_t)t * a.h;
+    const uint16_t *xrow = a.x + (size_t)(have_token ? t : 0) * a.h;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
 
-    // the token's experts, lane k holding entry k, and its row go out first
+    // the token's experts, lane k holding entry k, and the wave's first
+    // slice go out first
     const int64_t ek = (have_token && lane < a.K) ? a.topk_idx[tk + lane] : -1;
-    typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
+    typename std::conditional<FP8, RowFp8<1>, RowBf16<2>>::type row;
+    constexpr int per = decltype(row)::kPerPass;  // 1024 channels
     const int nitems = FP8 ? a.h >> 4 : a.h >> 3;
-    if (have_token)
-        row.load(src, 0, nitems);
+    const int nslices = (nitems + per - 1) / per;
+    if (have_token && w < nslices)
+        row.load(src, w * per, nitems);
 
     for (int i = tid; i < 2 * a.E; i += nthreads)
         hist[i] = 0;
@@ -129,34 +133,43 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
     if (!have_token)
         return;
 
-    // this wave's entries: lane k < K with k % kLLWaves == w
-    const bool mine = lane < a.K && (lane % kLLWaves) == w;
-    const int64_t e = mine ? ek : -1;
-    const bool valid = e >= 0 && e < a.E;
+    // the token's rows, lane k < K holding entry k's (the same in every
+    // wave); wave 0 writes the handle and the source index
+    const bool valid = lane < a.K && ek >= 0 && ek < a.E;
     int rep = 0;  // earlier entries of this row with the same expert
     for (int k2 = 0; k2 < a.K; ++k2)
         rep += (k2 < lane && readlane64(ek, k2) == ek);
-    Dests d;
-    d.rbits = 0;
-    d.vbits = uniform64(__ballot(valid));
-    d.send_row = -1;
-    d.recv_row = -1;
-    if (mine) {
-        if (valid) {
-            const int slot = hist_before[e] + rep;
-            if (slot < a.cap) {
-                const int64_t region = a.R_buf == 1 ? e : e * a.R + a.src_rank;
-                d.recv_row = (int)(region * a.cap + slot);
-                a.ll_src[d.recv_row] = t;
-            } else {
-                flag_error(a.err, EPX_DEV_OVERFLOW);
-            }
+    int dst = -1;
+    if (valid) {
+        const int slot = hist_before[ek] + rep;
+        if (slot < a.cap) {
+            const int64_t region = a.R_buf == 1 ? ek : ek * a.R + a.src_rank;
+            dst = (int)(region * a.cap + slot);
+        } else if (w == 0) {
+            flag_error(a.err, EPX_DEV_OVERFLOW);
         }
-        a.pos_ll[tk + lane] = d.recv_row;
     }
-    if (d.vbits) {
-        row.quantise(0, nitems);
-        scatter<FP8>(row, d, xrow, a.h, nullptr, nullptr, a.ll_x, a.ll_scales);
+    if (w == 0 && lane < a.K) {
+        a.pos_ll[tk + lane] = dst;
+        if (dst >= 0)
+            a.ll_src[dst] = t;
+    }
+    const uint64_t dbits = uniform64(__ballot(dst >= 0));
+    const size_t row_bytes = FP8 ? (size_t)a.h : (size_t)a.h * 2;
+    const int ld_s = scale_stride(a.h);
+    for (int sl = w; sl < nslices; sl += kLLWaves) {
+        if (sl != w)
+            row.load(src, sl * per, nitems);
+        row.quantise(sl * per, nitems);
+        for (uint64_t m = dbits; m; m &= m - 1) {
+            const int r = readlane(dst, __builtin_ctzll(m));
+            if constexpr (FP8)
+                row.store(reinterpret_cast<uint8_t *>(a.ll_x) + (size_t)r * row_bytes,
+                          a.ll_scales + (size_t)r * ld_s, sl * per, nitems);
+            else
+                row.store(reinterpret_cast<char *>(a.ll_x) + (size_t)r * row_bytes, sl * per,
+                          nitems);
+        }
     }
 }
 
@@ -191,25 +204,20 @@ hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <bool FP8, int NV>
-static void launch_ll_nv(const LLArgs &a, hipStream_t stream)
+template <bool FP8>
+static void launch_ll(const LLArgs &a, hipStream_t stream)
 {
     const dim3 grid(a.T > 0 ? a.T : 1);
     const size_t lds = sizeof(int) * 2 * (size_t)a.E;
-    hipLaunchKernelGGL((ll_dispatch_kernel<FP8, NV>), grid, dim3(kLLWaves * kWave), lds, stream,
-                       a);
+    hipLaunchKernelGGL((ll_dispatch_kernel<FP8>), grid, dim3(kLLWaves * kWave), lds, stream, a);
 }
 
 hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream)
 {
-    switch (pick_nv(a.h, fp8) + (fp8 ? 100 : 0)) {
-    case 8: launch_ll_nv<false, 8>(a, stream); break;
-    case 14: launch_ll_nv<false, 14>(a, stream); break;
-    case 16: launch_ll_nv<false, 16>(a, stream); break;
-    case 104: launch_ll_nv<true, 4>(a, stream); break;
-    case 107: launch_ll_nv<true, 7>(a, stream); break;
-    default: launch_ll_nv<true, 8>(a, stream); break;
-    }
+    if (fp8)
+        launch_ll<true>(a, stream);
+    else
+        launch_ll<false>(a, stream);
     return hipGetLastError();
 }
 

@@ -198,7 +198,10 @@ struct RowFp8 {
         }
         sv = u32x4{__float_as_uint(g4[0]), __float_as_uint(g4[1]), __float_as_uint(g4[2]),
                    __float_as_uint(g4[3])};
-        n_sv = min(16, (scale_stride(nseg << 4) - g0) >> 2);
+        // the pass's own groups (2 lanes per item); the last pass also
+        // writes the zero padding up to the scale stride
+        const bool last = s0 + kPerPass >= nseg;
+        n_sv = min(16, last ? (scale_stride(nseg << 4) - g0) >> 2 : 2 * NV);
     }
     // Codes of the pass to one destination row, plus that row's slice of
     // the scale row (one 16-byte store by the first lanes).
