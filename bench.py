@@ -72,7 +72,7 @@ def measured_traffic(kernel: str):
 def step_bytes(T, h, K, R, n_rank, n_exp):
     """Compulsory bytes per kernel (bf16 rows of 2h bytes)."""
     row = 2 * h
-    layout = 8 * T * K + T * R + 4 * T * R + 4 * T * K
+    layout = layout_bytes(T, K, 0, R)
     dispatch = (T * row + 8 * T * K + 4 * T * K          # x, topk_idx, topk_w
                 + 4 * T * K + 4 * n_rank                  # slot_in_expert, the pos_in_rank hits
                 + n_rank * row + n_exp * row              # send_x, recv_x
@@ -80,6 +80,13 @@ def step_bytes(T, h, K, R, n_rank, n_exp):
                 + 4 * n_exp + 4 * T * K)                  # recv_src, pos_exp
     combine = n_exp * row + 8 * T * K + T * row          # rows, pos + weights, out
     return dict(layout=layout, dispatch=dispatch, combine=combine)
+
+
+def layout_bytes(T, K, E, R):
+    """Compulsory bytes of the layout (topk_idx in; is_token_in_rank,
+    pos_in_rank, slot_in_expert out; the small count and offset arrays
+    left out)."""
+    return 8 * T * K + T * R + 4 * T * R + 4 * T * K
 
 
 def survey_bmin(T, h, K, R, n_rank, n_exp):
@@ -192,16 +199,21 @@ def other_workloads(n=20):
     d_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs), n)
     d = epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs)
     c_us = _loop_us(lambda: epx.combine(y, d.pos_exp, w, out=comb), n)
+    fws = torch.zeros(max(epx.fused_workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    f_us = _loop_us(lambda: epx.dispatch_fused(x, tk, w, E, R, fp8=True, layout=lay, out=bufs,
+                                               workspace=fws), n)
     assert epx.get_error() == 0
     d_bytes = (T * 2 * h + 12 * T * K + (n_rank + n_exp) * row8 + 4 * (n_rank + n_exp)
                + 12 * n_rank * K + 8 * T * K)
     c_bytes = n_exp * 2 * h + 8 * T * K + T * 2 * h
+    l_bytes = layout_bytes(T, K, E, R)
     out["fp8_prefill"] = {
         "workload": f"T={T} h={h} E={E} R={R} topk={K}, FP8 e4m3 dispatch, bf16 combine",
         "n_rank_rows": n_rank, "n_expert_rows": n_exp, "layout_us": round(lay_us, 2),
-        "dispatch_fp8": rec(d_us, d_bytes), "combine": rec(c_us, c_bytes),
-        "step_us": round(lay_us + d_us + c_us, 2)}
-    del x, tk, w, ws, lay, bufs, y, comb, d
+        "dispatch_fp8": rec(d_us, d_bytes), "fused_layout_dispatch_fp8": rec(f_us, d_bytes + l_bytes),
+        "combine": rec(c_us, c_bytes),
+        "step_us": round(f_us + c_us, 2), "two_launch_step_us": round(lay_us + d_us + c_us, 2)}
+    del x, tk, w, ws, fws, lay, bufs, y, comb, d
     torch.cuda.empty_cache()
 
     # two-stage combine on the prefill workload: T=4096, h=7168, E=256, R=32

@@ -21,6 +21,7 @@ from .api import (  # noqa: E402
     combine_partial,
     dispatch,
     dispatch_fused,
+    fused_launches,
     fused_workspace_size,
     get_dispatch_layout,
     get_error,
@@ -37,4 +38,4 @@ __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
            "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
-           "dispatch_fused"]
+           "fused_launches", "dispatch_fused"]

@@ -31,6 +31,7 @@ SIGNATURES = {
     "epx_dispatch": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I] + [_P] * 4 + [_I]
                      + [_P] * 5 + [_I64] + [_P] * 3 + [_I64, _P, _P]),
     "epx_fused_workspace_size": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "epx_fused_launches": (_I, [_P] + [_I] * 6 + [ctypes.POINTER(_I)]),
     "epx_dispatch_fused": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _I] + [_P] * 11 + [_SZ, _I]
                            + [_P] * 5 + [_I64] + [_P] * 3 + [_I64, _P, _P]),
     "epx_combine": (_I, [_P, _P, _I64, _I, _P, _P, _I, _I, _P, _P]),

@@ -290,13 +290,24 @@ def fused_workspace_size(T: int, K: int, E: int, R: int) -> int:
     return n.value
 
 
+def fused_launches(T: int, h: int, K: int, E: int, R: int, fp8: bool = False,
+                   device: torch.device | None = None) -> int:
+    """How many launches dispatch_fused takes for this shape (1, or 2 when
+    its grid would not fit on the device at once)."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    n = ctypes.c_int()
+    check(_lib.load().epx_fused_launches(_ctx(device), T, h, K, E, R, int(fp8), ctypes.byref(n)),
+          "epx_fused_launches")
+    return n.value
+
+
 def dispatch_fused(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
                    num_experts: int, num_ranks: int, fp8: bool = False,
                    num_channels: int | None = None, layout: Layout | None = None,
                    out: dict | None = None, workspace: torch.Tensor | None = None,
                    totals_host: torch.Tensor | None = None) -> Dispatched:
-    """get_dispatch_layout and dispatch in one launch (two when the
-    layout's 256-token tiles outnumber the compute units; no host wait
+    """get_dispatch_layout and dispatch in one launch (two when its grid
+    would not fit on the device at once, see fused_launches; no host wait
     either way): the same outputs as the two calls. ``layout`` (from alloc_layout) and
     ``out`` (from alloc_dispatch) avoid allocating; without ``out`` the
     buffers get the worst-case capacities T*min(K,R) and T*K rows.
@@ -454,4 +465,4 @@ __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
            "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
-           "dispatch_fused"]
+           "fused_launches", "dispatch_fused"]

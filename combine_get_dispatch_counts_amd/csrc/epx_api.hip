@@ -287,6 +287,27 @@ int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes)
     return EPX_OK;
 }
 
+int epx_fused_launches(epx_ctx *ctx, int T, int h, int K, int E, int R, int fp8, int *launches)
+{
+    if (!launches)
+        return EPX_EINVAL;
+    int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if ((rc = check_routing(T, K, E, R)) != EPX_OK || (rc = check_hidden(h, fp8)) != EPX_OK)
+        return rc;
+    epx::FusedArgs f{};
+    f.lay.T = T;
+    f.lay.K = K;
+    f.lay.E = E;
+    f.lay.R = R;
+    f.lay.ntiles = (T + epx::kLayoutTile - 1) / epx::kLayoutTile;
+    f.disp.T = T;
+    f.disp.h = h;
+    f.cus = ctx->cus;
+    return epx::fused_launches(f, fp8 != 0, launches) == hipSuccess ? EPX_OK : EPX_EHIP;
+}
+
 int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
                        const float *topk_w, int T, int K, int E, int R, int C,
                        int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,

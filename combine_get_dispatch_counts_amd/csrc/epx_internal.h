@@ -103,6 +103,7 @@ struct FusedArgs {
 
 size_t fused_workspace_bytes(int T, int K, int E, int R);
 hipError_t launch_fused(const FusedArgs &f, bool fp8, hipStream_t stream);
+hipError_t fused_launches(const FusedArgs &f, bool fp8, int *launches);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
 
 struct CombineArgs {

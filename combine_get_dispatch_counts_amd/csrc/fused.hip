@@ -6,9 +6,8 @@
 // warps move the data, in one launch. Here the first blocks of the grid are
 // the layout's blocks (layout_device.h: one per 256-token tile, then the
 // totals block), and every block of kLayoutThreads threads then dispatches
-// up to one token per wave (dispatch_device.h), so the grid is no larger
-// than the dispatch alone needs: its work is all in flight at once, and
-// extra blocks would only start late and leave a tail that cannot fill HBM.
+// one token per wave (dispatch_device.h), so the grid is no larger than
+// the dispatch alone needs.
 //
 // Hand-over. The layout blocks publish, beside their usual outputs, the
 // totals and each token's final in-rank positions and in-expert slots as
@@ -27,13 +26,20 @@
 // block reads it with one plain load, checking on the way that no layout
 // call was left unfinished (arrivals 0).
 //
-// The layout blocks, once their layout part is done, wait for the totals
-// block like the others, so all layout blocks must be on the chip
-// together: the host uses this kernel only while there are no more of them
-// than compute units (one block per unit always fits), and otherwise runs
-// the layout and the dispatch as two launches. Layout blocks come first in
-// the grid; dispatch-only blocks issue their row loads before waiting, so
-// the loads overlap the layout. Every wait is bounded.
+// When it is used. The layout blocks, once their layout part is done, wait
+// for the totals block like the others, so all layout blocks must be on the
+// chip together; and the dispatch work is all in flight at once only while
+// the whole grid is: a block keeps its place until its slowest wave ends,
+// so later rounds of blocks would each start behind a tail (a loop over
+// several tokens per wave instead costs registers: 175 rather than 124 at
+// h = 7168, half the waves). The host therefore launches this kernel when
+// the occupancy query says the whole grid fits at once, and otherwise runs
+// the layout and the dispatch as two launches, whose 64-thread dispatch
+// blocks free their place wave by wave. Layout blocks come first in the
+// grid; dispatch-only blocks issue their row loads before waiting, so the
+// loads overlap the layout. Every wait is bounded.
+#include <atomic>
+
 #include "dispatch_device.h"
 #include "layout_device.h"
 
@@ -147,27 +153,65 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     }
 }
 
+// Blocks of this kernel one compute unit holds at once for a dynamic LDS
+// size (the occupancy query, cached for the last size asked).
 template <int KMAX, bool FP8, int NV>
-void launch_fused_k(const FusedArgs &f, hipStream_t stream)
+int fused_blocks_per_cu(size_t lds)
+{
+    static std::atomic<uint64_t> cache{0};  // (lds + 1) << 8 | blocks
+    const uint64_t c = cache.load(std::memory_order_relaxed);
+    if ((c >> 8) == lds + 1)
+        return (int)(c & 0xFF);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_kernel<KMAX, FP8, NV>,
+                                                     kLayoutThreads, lds) != hipSuccess)
+        return 0;
+    n = n < 0 ? 0 : (n > 255 ? 255 : n);
+    cache.store(((uint64_t)(lds + 1) << 8) | (uint64_t)n, std::memory_order_relaxed);
+    return n;
+}
+
+// The grid: the layout's blocks, or the dispatch's one block per
+// kFusedTokens tokens if more (one block for T = 0).
+int64_t fused_grid(const FusedArgs &f)
 {
     const int64_t disp_blocks = (f.disp.T + kFusedTokens - 1) / kFusedTokens;
     const int64_t nlay = f.lay.ntiles + 1;
-    const int64_t blocks = f.lay.ntiles == 0 ? 1 : (disp_blocks > nlay ? disp_blocks : nlay);
+    return f.lay.ntiles == 0 ? 1 : (disp_blocks > nlay ? disp_blocks : nlay);
+}
+
+// With launch false, only say how many launches the call takes (1 or 2).
+template <int KMAX, bool FP8, int NV>
+hipError_t launch_fused_k(const FusedArgs &f, hipStream_t stream, bool launch, int *launches)
+{
+    const size_t lds = layout_tok_lds_bytes(f.lay.E, f.lay.R, f.lay.K);
+    const int64_t blocks = fused_grid(f);
+    const bool one = f.lay.ntiles == 0 ||
+                     blocks <= (int64_t)fused_blocks_per_cu<KMAX, FP8, NV>(lds) * f.cus;
+    if (launches)
+        *launches = one ? 1 : 2;
+    if (!launch)
+        return hipSuccess;
+    if (!one) {
+        const hipError_t e = launch_layout(f.lay, stream);
+        return e != hipSuccess ? e : launch_dispatch(f.disp, FP8, stream);
+    }
     hipLaunchKernelGGL((fused_kernel<KMAX, FP8, NV>), dim3((unsigned)blocks),
-                       dim3(kLayoutThreads), layout_tok_lds_bytes(f.lay.E, f.lay.R, f.lay.K), stream,
-                       f);
+                       dim3(kLayoutThreads), lds, stream, f);
+    return hipGetLastError();
 }
 
 template <int KMAX>
-void launch_fused_kmax(const FusedArgs &f, bool fp8, hipStream_t stream)
+hipError_t launch_fused_kmax(const FusedArgs &f, bool fp8, hipStream_t stream, bool launch,
+                             int *launches)
 {
     switch (pick_nv(f.disp.h, fp8) + (fp8 ? 100 : 0)) {
-    case 8: launch_fused_k<KMAX, false, 8>(f, stream); break;
-    case 14: launch_fused_k<KMAX, false, 14>(f, stream); break;
-    case 16: launch_fused_k<KMAX, false, 16>(f, stream); break;
-    case 104: launch_fused_k<KMAX, true, 4>(f, stream); break;
-    case 107: launch_fused_k<KMAX, true, 7>(f, stream); break;
-    default: launch_fused_k<KMAX, true, 8>(f, stream); break;
+    case 8: return launch_fused_k<KMAX, false, 8>(f, stream, launch, launches);
+    case 14: return launch_fused_k<KMAX, false, 14>(f, stream, launch, launches);
+    case 16: return launch_fused_k<KMAX, false, 16>(f, stream, launch, launches);
+    case 104: return launch_fused_k<KMAX, true, 4>(f, stream, launch, launches);
+    case 107: return launch_fused_k<KMAX, true, 7>(f, stream, launch, launches);
+    default: return launch_fused_k<KMAX, true, 8>(f, stream, launch, launches);
     }
 }
 
@@ -184,15 +228,14 @@ size_t fused_workspace_bytes(int T, int K, int E, int R)
 
 hipError_t launch_fused(const FusedArgs &f, bool fp8, hipStream_t stream)
 {
-    if (f.lay.ntiles + 1 > f.cus) {  // the layout blocks might not all fit at once
-        const hipError_t e = launch_layout(f.lay, stream);
-        return e != hipSuccess ? e : launch_dispatch(f.disp, fp8, stream);
-    }
-    if (f.lay.K <= 8)
-        launch_fused_kmax<8>(f, fp8, stream);
-    else
-        launch_fused_kmax<EPX_MAX_TOPK>(f, fp8, stream);
-    return hipGetLastError();
+    return f.lay.K <= 8 ? launch_fused_kmax<8>(f, fp8, stream, true, nullptr)
+                        : launch_fused_kmax<EPX_MAX_TOPK>(f, fp8, stream, true, nullptr);
+}
+
+hipError_t fused_launches(const FusedArgs &f, bool fp8, int *launches)
+{
+    return f.lay.K <= 8 ? launch_fused_kmax<8>(f, fp8, nullptr, false, launches)
+                        : launch_fused_kmax<EPX_MAX_TOPK>(f, fp8, nullptr, false, launches);
 }
 
 }  // namespace epx

@@ -205,9 +205,15 @@ int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
  * again); calls that share it must not overlap, and it may be shared with
  * epx_get_dispatch_layout calls of any shape. The
  * capacities must be known up front (no host wait happens): T*min(K,R) send
- * rows and T*K receive rows always suffice. One launch while the layout's
- * tiles (ceil(T/256)) number fewer than the device's compute units, else the
- * layout and the dispatch are launched one after the other. */
+ * rows and T*K receive rows always suffice. One launch while its whole
+ * grid (max(ceil(T/256) + 1, ceil(T/8)) blocks of 512 threads) fits on the
+ * device at once, else the layout and the dispatch are launched one after
+ * the other (epx_fused_launches says which). */
+/* How many launches epx_dispatch_fused takes for this shape on the
+ * context's device (host out: 1 or 2, see above); arguments as there.
+ * Nothing is launched. */
+int epx_fused_launches(epx_ctx *ctx, int T, int h, int K, int E, int R, int fp8, int *launches);
+
 int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
                        const float *topk_w, int T, int K, int E, int R, int C,
                        int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,

@@ -106,6 +106,14 @@ def test_binding_scale_stride():
     assert ei.value.code == -1
 
 
+def test_fused_launches_rejects(lib):
+    """Argument checks come before any device call: no context, no output."""
+    n = ctypes.c_int(-5)
+    assert lib.epx_fused_launches(None, 4096, 7168, 8, 256, 32, 0, ctypes.byref(n)) == -1
+    assert lib.epx_fused_launches(None, 4096, 7168, 8, 256, 32, 0, None) == -1
+    assert n.value == -5
+
+
 def test_fused_workspace_size(lib):
     n = ctypes.c_size_t()
     assert lib.epx_fused_workspace_size(4096, 8, 256, 32, ctypes.byref(n)) == 0

@@ -87,19 +87,42 @@ def test_fused_edge_cases(T, K, E, R, h, fp8, kind):
     _fused_check(x, topk, w, E, R, fp8, C=5 if T else None)
 
 
-@pytest.mark.parametrize("extra", [0, 1])
-def test_fused_both_grid_shapes(extra):
-    """One launch while the layout blocks fit on the chip at one block per
-    compute unit (tiles + 1 <= CUs); one tile more and the layout and the
-    dispatch run as two launches. Both sides of that edge."""
+def _one_launch_limit(h, K, E, R, fp8):
+    """The largest T that epx_dispatch_fused still does in one launch."""
+    import combine_get_dispatch_counts_amd as epx
+
+    lo, hi = 1, 1 << 22
+    assert epx.fused_launches(lo, h, K, E, R, fp8) == 1
+    assert epx.fused_launches(hi, h, K, E, R, fp8) == 2
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if epx.fused_launches(mid, h, K, E, R, fp8) == 1:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("past", [0, 1])
+def test_fused_one_and_two_launches(fp8, past):
+    """One launch while the whole grid fits on the device at once, two past
+    that: the largest one-launch T and the next, both against the oracle.
+    The limit is monotonic in T and at least one block per compute unit."""
+    import combine_get_dispatch_counts_amd as epx
+
+    h, K, E, R = 128, 4, 16, 4
+    limit = _one_launch_limit(h, K, E, R, fp8)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    T, K, E, R, h = (cus - 1) * 256 + extra, 4, 64, 8, 128
-    say(f"fused T={T} ({'two launches' if extra else 'one launch'}, {cus} CUs)")
-    rng = np.random.default_rng(T)
+    assert limit >= 8 * cus, f"one-launch limit {limit} below one block per unit"
+    assert all(epx.fused_launches(T, h, K, E, R, fp8) == 1 for T in (0, 1, limit // 2, limit))
+    T = limit + past
+    say(f"fused T={T} h={h} K={K} fp8={fp8} ({'two launches' if past else 'one launch'})")
+    rng = np.random.default_rng(T + h)
     x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
     topk = synth.random_routing(T, K, E, seed=T + 1, p_drop=0.1)
     w = rng.random((T, K)).astype(np.float32)
-    _fused_check(x, topk, w, E, R, bool(extra))
+    _fused_check(x, topk, w, E, R, fp8)
 
 
 def test_fused_shares_workspace_with_layout():

@@ -364,6 +364,28 @@ def test_ll_dispatch_small(cfg, T, src, R_buf_full, fp8, cap):
         _check_ll_scales(host_bits(buf.ll_scales), o["ll_scales"], o["ll_src"], "ll_scales")
 
 
+@pytest.mark.parametrize("h,fp8,K", [(1152, True, 4), (1152, False, 4), (9216, True, 8),
+                                      (10368, True, 32), (10368, False, 6), (136, False, 3)])
+def test_ll_dispatch_row_slices(h, fp8, K):
+    """Rows cut into 1024-channel slices over the block's waves: a partial
+    last slice, more slices than waves (each wave then takes several), and
+    K above the wave count."""
+    T, E, R, src, cap = 40, 32, 8, 5, 40
+    rng = np.random.default_rng(h + K)
+    x = synth.to_bf16_bits((rng.standard_normal((T, h)) *
+                            np.exp(rng.normal(0, 3, (T, 1)))).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=h, p_drop=0.1)
+    say(f"ll_dispatch slices T={T} h={h} E={E} R={R} K={K} fp8={fp8}")
+    buf = _ll_gpu(x, topk, E, R, src, cap, 1, fp8)
+    o = oracle.ll_dispatch(x, topk, E, R, src, cap, 1, fp8=fp8)
+    _eq(host_bits(buf.pos_ll), o["pos_ll"], "pos_ll")
+    _eq(host_bits(buf.ll_count), o["ll_count"], "ll_count")
+    _eq(host_bits(buf.ll_src), o["ll_src"], "ll_src")
+    _eq(host_bits(buf.ll_x), o["ll_x"], "ll_x")
+    if fp8:
+        _check_ll_scales(host_bits(buf.ll_scales), o["ll_scales"], o["ll_src"], "ll_scales")
+
+
 def test_ll_dispatch_decode_full_buffer():
     """Decode workload at full size: T=128, E=256, R=32, cap=128, FP8, the
     full logical buffer of all 32 destinations (1,048,576 rows, 7.75 GB).
