@@ -195,3 +195,27 @@ def test_fused_step_in_graph():
         assert epx.get_error() == 0
         for a, b in zip([out, bufs["recv_x"], lay.pos_in_rank], ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {replay} differs"
+
+
+def test_fused_workspace_recovery():
+    """A workspace in a state no call leaves (a layout call's arrivals left
+    pending) is flagged by the fused call with no wait at all, and once it is
+    zero-filled again the next call is correct."""
+    import combine_get_dispatch_counts_amd as epx
+
+    T, E, R, K, h = 2048, 64, 8, 6, 512
+    ws = torch.zeros(epx.fused_workspace_size(T, K, E, R), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(61)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=62)
+    w = rng.random((T, K)).astype(np.float32)
+    say("fused call on a workspace with pending arrivals")
+    _fused_check(x, topk, w, E, R, False, ws=ws)
+    ws[:4].view(torch.int32).fill_(3)
+    epx.dispatch_fused(dev_bf16(x), torch.from_numpy(topk).cuda(), torch.from_numpy(w).cuda(), E,
+                       R, workspace=ws)
+    flags = epx.get_error()
+    assert flags == epx._lib.DEV_WORKSPACE, f"expected EPX_DEV_WORKSPACE, got {flags:#x}"
+    ws.zero_()
+    say("fused call after the workspace was zeroed")
+    _fused_check(x, topk, w, E, R, False, ws=ws)
