@@ -285,6 +285,49 @@ def other_workloads(n=20):
         del buf
         torch.cuda.empty_cache()
 
+    # whole decode steps (same shape): the low-latency step as a ping-pong
+    # pair (each dispatch resets the other buffer's counts, so no reset
+    # launch), and the high-throughput step with the layout in its own launch
+    # or fused into the dispatch's; each launched eagerly from Python and
+    # replayed from a HIP graph (no host launch work)
+    ll_bufs = [epx.alloc_ll(E, 1, cap, h, T, K, True, dev) for _ in range(2)]
+    y = synth.expert_outputs(E * cap, h, seed=19, device="cuda")
+    comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+
+    def ll_pair():
+        for i in range(2):
+            epx.ll_dispatch(x, tk, E, R, 0, cap, 1, True, ll_bufs[i], next_buf=ll_bufs[1 - i])
+            epx.combine(y, ll_bufs[i].pos_ll, w, out=comb)
+
+    ws_d = torch.zeros(max(epx.workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
+    fws_d = torch.zeros(max(epx.fused_workspace_size(T, K, E, R), 1), dtype=torch.uint8,
+                        device=dev)
+    lay_d = epx.alloc_layout(T, K, E, R, None, dev)
+    bufs_d = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, False, dev)
+    y2 = synth.expert_outputs(T * K, h, seed=29, device="cuda")
+
+    def ht_two():
+        lay = epx.get_dispatch_layout(tk, E, R, workspace=ws_d, out=lay_d)
+        d = epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs_d)
+        epx.combine(y2, d.pos_exp, w, out=comb)
+
+    def ht_fused():
+        d = epx.dispatch_fused(x, tk, w, E, R, layout=lay_d, out=bufs_d, workspace=fws_d)
+        epx.combine(y2, d.pos_exp, w, out=comb)
+
+    out["decode_steps"] = {
+        "workload": f"T={T} h={h} E={E} R={R} topk={K}: dispatch + combine per step",
+        "ll_fp8_step_us": {"eager": round(_loop_us(ll_pair, n) / 2, 2),
+                           "graph": round(_graph_us(ll_pair, n) / 2, 2)},
+        "ht_bf16_two_launch_step_us": {"eager": round(_loop_us(ht_two, n), 2),
+                                       "graph": round(_graph_us(ht_two, n), 2)},
+        "ht_bf16_fused_step_us": {"eager": round(_loop_us(ht_fused, n), 2),
+                                  "graph": round(_graph_us(ht_fused, n), 2)},
+    }
+    assert epx.get_error() == 0
+    del ll_bufs, y, comb, ws_d, fws_d, lay_d, bufs_d, y2
+    torch.cuda.empty_cache()
+
     # skewed routing, bf16: T=8192, h=4096, E=64, R=8, topk=6
     inp = synth.make_inputs(4)
     wl = inp["workload"]

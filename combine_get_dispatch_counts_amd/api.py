@@ -292,8 +292,8 @@ def fused_workspace_size(T: int, K: int, E: int, R: int) -> int:
 
 def fused_launches(T: int, h: int, K: int, E: int, R: int, fp8: bool = False,
                    device: torch.device | None = None) -> int:
-    """How many launches dispatch_fused takes for this shape (1, or 2 when
-    its grid would not fit on the device at once)."""
+    """How many launches dispatch_fused takes for this shape (1 while its
+    grid covers every compute unit and fits on the device at once, else 2)."""
     device = device or torch.device("cuda", torch.cuda.current_device())
     n = ctypes.c_int()
     check(_lib.load().epx_fused_launches(_ctx(device), T, h, K, E, R, int(fp8), ctypes.byref(n)),
@@ -306,9 +306,9 @@ def dispatch_fused(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.
                    num_channels: int | None = None, layout: Layout | None = None,
                    out: dict | None = None, workspace: torch.Tensor | None = None,
                    totals_host: torch.Tensor | None = None) -> Dispatched:
-    """get_dispatch_layout and dispatch in one launch (two when its grid
-    would not fit on the device at once, see fused_launches; no host wait
-    either way): the same outputs as the two calls. ``layout`` (from alloc_layout) and
+    """get_dispatch_layout and dispatch in one launch (two outside the
+    shapes fused_launches reports as one; no host wait either way): the same
+    outputs as the two calls. ``layout`` (from alloc_layout) and
     ``out`` (from alloc_dispatch) avoid allocating; without ``out`` the
     buffers get the worst-case capacities T*min(K,R) and T*K rows.
     ``workspace`` must hold fused_workspace_size(T, K, E, R) bytes and be

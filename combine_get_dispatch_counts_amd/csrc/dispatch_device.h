@@ -48,13 +48,14 @@ struct RowBf16 {
         }
     }
     __device__ __forceinline__ void quantise(int, int) {}
+    template <StorePolicy POL = StorePolicy::WT>
     __device__ __forceinline__ void store(char *dst_row, int v0, int nvec) const
     {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int v = v0 + u * kWave + lane_id();
             if (v < nvec)
-                store16_wt(dst_row + (size_t)v * 16, r[u]);
+                store16_row<POL>(dst_row, (uint32_t)v * 16, r[u]);
         }
     }
 };
@@ -205,16 +206,17 @@ struct RowFp8 {
     }
     // Codes of the pass to one destination row, plus that row's slice of
     // the scale row (one 16-byte store by the first lanes).
+    template <StorePolicy POL = StorePolicy::WT>
     __device__ __forceinline__ void store(uint8_t *q_row, float *s_row, int s0, int nseg) const
     {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int sg = s0 + u * kWave + lane_id();
             if (sg < nseg)
-                store16_wt(q_row + (size_t)sg * 16, q[u]);
+                store16_row<POL>(q_row, (uint32_t)sg * 16, q[u]);
         }
         if (lane_id() < n_sv)
-            store16_wt(s_row + (s0 >> 3) + 4 * lane_id(), sv);
+            store16_row<POL>(s_row, (uint32_t)((s0 >> 3) + 4 * lane_id()) * 4, sv);
     }
 };
 
@@ -228,6 +230,7 @@ struct Dests {
 
 // Write the token's row (the pass held in `row`, plus any further passes
 // loaded here) to every destination: send rows in buffer a, recv rows in b.
+// FP8 rows go out with the nontemporal policy, bf16 rows write-through.
 template <bool FP8, typename Row>
 __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t *xrow, int h,
                                         void *a_x, float *a_s, void *b_x, float *b_s)
@@ -247,8 +250,8 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
             if (r < 0)
                 continue;
             if constexpr (FP8)
-                row.store(static_cast<uint8_t *>(a_x) + (size_t)r * row_bytes,
-                          a_s + (size_t)r * ld_s, i0, nseg);
+                row.template store<StorePolicy::NT>(static_cast<uint8_t *>(a_x) + (size_t)r * row_bytes,
+                                                    a_s + (size_t)r * ld_s, i0, nseg);
             else
                 row.store(static_cast<char *>(a_x) + (size_t)r * row_bytes, i0, nvec);
         }
@@ -257,8 +260,8 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
             if (r < 0)
                 continue;
             if constexpr (FP8)
-                row.store(static_cast<uint8_t *>(b_x) + (size_t)r * row_bytes,
-                          b_s + (size_t)r * ld_s, i0, nseg);
+                row.template store<StorePolicy::NT>(static_cast<uint8_t *>(b_x) + (size_t)r * row_bytes,
+                                                    b_s + (size_t)r * ld_s, i0, nseg);
             else
                 row.store(static_cast<char *>(b_x) + (size_t)r * row_bytes, i0, nvec);
         }

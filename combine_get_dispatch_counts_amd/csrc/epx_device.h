@@ -57,15 +57,29 @@ __device__ __forceinline__ void store16_stream(void *p, u32x4 v)
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 
-// 16-byte vector store with the sc1 cache-policy bit (device-coherent
-// write-through), which measured ~4% faster than the nontemporal policy for
-// the scattered whole-row writes of dispatch (the combine's interleaved
-// reads and writes prefer nontemporal). A vector-memory store: nothing in
-// the kernel reads the data back, and the kernel's end makes it visible to
-// later work.
-__device__ __forceinline__ void store16_wt(void *p, u32x4 v)
+// Row stores of the dispatch kernels: 16 bytes at byte offset off (per
+// lane) of a row whose base is the same for the whole wave. Policy WT: the
+// sc1 cache-policy bit (device-coherent write-through), through a buffer
+// store on a descriptor built from the row base, so the compiler knows it
+// for a store (an inline-assembly store made it wait for every earlier
+// memory operation before each one: one store in flight per wave, 5x slower
+// when few tokens are dispatched). Policy NT: the nontemporal hint, 4-5%
+// faster for the FP8 scatter's 7 KB rows and 256-byte scale rows. Both are
+// vector-memory stores; nothing in the kernel reads the data back, and the
+// kernel's end makes it visible to later work.
+enum class StorePolicy { WT, NT };
+
+template <StorePolicy POL>
+__device__ __forceinline__ void store16_row(void *row, uint32_t off, u32x4 v)
 {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+    if constexpr (POL == StorePolicy::NT) {
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<char *>(row) + off));
+    } else {
+        // raw buffer: stride 0, the largest record count, 32-bit data format
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(row, 0, 0x7FFFFFF0, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16 /* sc1 */);
+    }
 }
 
 // Inclusive sum over the 64 lanes of a wave.

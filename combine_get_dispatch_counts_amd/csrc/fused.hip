@@ -32,12 +32,15 @@
 // the whole grid is: a block keeps its place until its slowest wave ends,
 // so later rounds of blocks would each start behind a tail (a loop over
 // several tokens per wave instead costs registers: 175 rather than 124 at
-// h = 7168, half the waves). The host therefore launches this kernel when
-// the occupancy query says the whole grid fits at once, and otherwise runs
-// the layout and the dispatch as two launches, whose 64-thread dispatch
-// blocks free their place wave by wave. Layout blocks come first in the
-// grid; dispatch-only blocks issue their row loads before waiting, so the
-// loads overlap the layout. Every wait is bounded.
+// h = 7168, half the waves). With fewer blocks than compute units, on the
+// other hand, a token's eight waves share one unit's store path while other
+// units idle. The host therefore launches this kernel when its grid covers
+// every compute unit and, by the occupancy query, fits on the chip at once,
+// and otherwise runs the layout and the dispatch as two launches, whose
+// 64-thread dispatch blocks spread one wave per token over the chip and
+// free their place wave by wave. Layout blocks come first in the grid;
+// dispatch-only blocks issue their row loads before waiting, so the loads
+// overlap the layout. Every wait is bounded.
 #include <atomic>
 
 #include "dispatch_device.h"
@@ -187,7 +190,8 @@ hipError_t launch_fused_k(const FusedArgs &f, hipStream_t stream, bool launch, i
     const size_t lds = layout_tok_lds_bytes(f.lay.E, f.lay.R, f.lay.K);
     const int64_t blocks = fused_grid(f);
     const bool one = f.lay.ntiles == 0 ||
-                     blocks <= (int64_t)fused_blocks_per_cu<KMAX, FP8, NV>(lds) * f.cus;
+                     (blocks >= f.cus &&
+                      blocks <= (int64_t)fused_blocks_per_cu<KMAX, FP8, NV>(lds) * f.cus);
     if (launches)
         *launches = one ? 1 : 2;
     if (!launch)

@@ -87,42 +87,74 @@ def test_fused_edge_cases(T, K, E, R, h, fp8, kind):
     _fused_check(x, topk, w, E, R, fp8, C=5 if T else None)
 
 
-def _one_launch_limit(h, K, E, R, fp8):
-    """The largest T that epx_dispatch_fused still does in one launch."""
+def _one_launch_window(h, K, E, R, fp8):
+    """The smallest and the largest T > 0 that epx_dispatch_fused does in
+    one launch (the grid must cover every compute unit and fit at once)."""
     import combine_get_dispatch_counts_amd as epx
 
-    lo, hi = 1, 1 << 22
-    assert epx.fused_launches(lo, h, K, E, R, fp8) == 1
-    assert epx.fused_launches(hi, h, K, E, R, fp8) == 2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    one = 8 * cus  # one block per unit: covers all, always fits
+    assert epx.fused_launches(one, h, K, E, R, fp8) == 1
+    assert epx.fused_launches(1, h, K, E, R, fp8) == 2
+    assert epx.fused_launches(1 << 22, h, K, E, R, fp8) == 2
+    lo, hi = 1, one  # launches(lo) == 2, launches(hi) == 1
     while hi - lo > 1:
         mid = (lo + hi) // 2
-        if epx.fused_launches(mid, h, K, E, R, fp8) == 1:
-            lo = mid
-        else:
-            hi = mid
-    return lo
+        lo, hi = (lo, mid) if epx.fused_launches(mid, h, K, E, R, fp8) == 1 else (mid, hi)
+    first = hi
+    lo, hi = one, 1 << 22  # launches(lo) == 1, launches(hi) == 2
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if epx.fused_launches(mid, h, K, E, R, fp8) == 1 else (lo, mid)
+    return first, lo
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("past", [0, 1])
-def test_fused_one_and_two_launches(fp8, past):
-    """One launch while the whole grid fits on the device at once, two past
-    that: the largest one-launch T and the next, both against the oracle.
-    The limit is monotonic in T and at least one block per compute unit."""
+@pytest.mark.parametrize("edge", ["below", "first", "last", "above"])
+def test_fused_one_and_two_launches(fp8, edge):
+    """One launch for T in a window (the grid covers every compute unit and
+    fits on the device at once), two on either side; both edges of the
+    window and the shapes just outside it against the oracle."""
     import combine_get_dispatch_counts_amd as epx
 
     h, K, E, R = 128, 4, 16, 4
-    limit = _one_launch_limit(h, K, E, R, fp8)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert limit >= 8 * cus, f"one-launch limit {limit} below one block per unit"
-    assert all(epx.fused_launches(T, h, K, E, R, fp8) == 1 for T in (0, 1, limit // 2, limit))
-    T = limit + past
-    say(f"fused T={T} h={h} K={K} fp8={fp8} ({'two launches' if past else 'one launch'})")
+    first, last = _one_launch_window(h, K, E, R, fp8)
+    assert first <= last
+    assert epx.fused_launches(0, h, K, E, R, fp8) == 1
+    T = {"below": first - 1, "first": first, "last": last, "above": last + 1}[edge]
+    want = 1 if edge in ("first", "last") else 2
+    assert epx.fused_launches(T, h, K, E, R, fp8) == want
+    say(f"fused T={T} h={h} K={K} fp8={fp8} (window {first}..{last}, {want} launch(es))")
     rng = np.random.default_rng(T + h)
     x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
     topk = synth.random_routing(T, K, E, seed=T + 1, p_drop=0.1)
     w = rng.random((T, K)).astype(np.float32)
     _fused_check(x, topk, w, E, R, fp8)
+
+
+@pytest.mark.parametrize("K,E,R,h,fp8,kind", [
+    (8, 256, 64, 256, True, "dropped"), (32, 64, 8, 136, False, "uniform"),
+    (4, 16, 4, 128, False, "repeats"), (6, 64, 8, 4096, True, "uniform"),
+    (8, 128, 32, 512, False, "uniform"), (2, 8, 1, 128, True, "dropped"),
+])
+def test_fused_kernel_edge_cases(K, E, R, h, fp8, kind):
+    """The one-launch kernel itself on edge shapes: T inside its window,
+    with a ragged last tile (T % 256 != 0), K = 32, R = 1 and 64, repeated
+    experts in a row, dropped routes, FP8."""
+    import combine_get_dispatch_counts_amd as epx
+
+    first, last = _one_launch_window(h, K, E, R, fp8)
+    T = min(first + 37, last)
+    assert epx.fused_launches(T, h, K, E, R, fp8) == 1
+    say(f"fused kernel T={T} K={K} E={E} R={R} h={h} fp8={fp8} {kind}")
+    rng = np.random.default_rng(T + K)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    if kind == "repeats":
+        topk = rng.integers(-1, E, (T, K)).astype(np.int64)
+    else:
+        topk = synth.random_routing(T, K, E, seed=T + 3, p_drop=0.2 if kind == "dropped" else 0.0)
+    w = rng.random((T, K)).astype(np.float32)
+    _fused_check(x, topk, w, E, R, fp8, C=5)
 
 
 def test_fused_shares_workspace_with_layout():
@@ -156,9 +188,10 @@ def test_fused_shares_workspace_with_layout():
 def test_fused_step_in_graph():
     import combine_get_dispatch_counts_amd as epx
 
-    inp = synth.make_inputs(4, T=1024)
+    inp = synth.make_inputs(4, T=2048)
     wl = inp["workload"]
     T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    assert epx.fused_launches(T, h, K, E, R) == 1
     say(f"fused step in a graph T={T}")
     dev = torch.device("cuda")
     x, tk, w = dev_bf16(inp["x"]), torch.from_numpy(inp["topk_idx"]).cuda(), \
