@@ -268,17 +268,16 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
     }
 }
 
-// The per-token part of the high-throughput dispatch, for a wave holding
-// token t's row (first pass loaded, not yet quantised). Lane k < K holds the
-// token's expert e (or -1) and recv_r, its expert-major row (exp_off[e] +
-// slot), or -1; lane r < R holds send_r, its rank-major row (rank_off[r] +
-// pos_in_rank[t, r]) if the token goes to rank r, else -1 (always -1 when
-// there is no send buffer). Checks the rows against the capacities, writes
-// the handle and the metadata, and stores the row to every destination.
-template <bool FP8, typename Row>
-__device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row &row,
-                                               const uint16_t *xrow, int64_t e, int64_t send_r,
-                                               int64_t recv_r)
+// The destinations of token t in the high-throughput dispatch, from one
+// wave: lane k < K holds the token's expert e (or -1) and recv_r, its
+// expert-major row (exp_off[e] + slot), or -1; lane r < R holds send_r, its
+// rank-major row (rank_off[r] + pos_in_rank[t, r]) if the token goes to rank
+// r, else -1 (always -1 when there is no send buffer). Rows are checked
+// against the capacities (a row past one is dropped). With meta, the wave
+// also flags overflows and writes the handle and the per-row metadata; when
+// several waves share a token, exactly one of them passes meta.
+__device__ __forceinline__ Dests token_dests(const DispatchArgs &a, int t, int64_t e,
+                                             int64_t send_r, int64_t recv_r, bool meta)
 {
     const int lane = lane_id();
     const int64_t tk = (int64_t)t * a.K;
@@ -291,22 +290,24 @@ __device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row
     if (lane < a.R && send_r >= 0) {
         if (send_r < a.send_cap)
             d.send_row = (int)send_r;
-        else
+        else if (meta)
             flag_error(a.err, EPX_DEV_OVERFLOW);
     }
     if (lane < a.K) {
         if (valid) {
             if (recv_r >= 0 && recv_r < a.recv_cap)
                 d.recv_row = (int)recv_r;
-            else
+            else if (meta)
                 flag_error(a.err, EPX_DEV_OVERFLOW);
         }
-        a.pos_exp[tk + lane] = d.recv_row;
-        if (d.recv_row >= 0)
-            a.recv_src[d.recv_row] = t;
+        if (meta) {
+            a.pos_exp[tk + lane] = d.recv_row;
+            if (d.recv_row >= 0)
+                a.recv_src[d.recv_row] = t;
+        }
     }
     // per send row: source token and the top-k list seen from that rank
-    if (d.send_row >= 0) {
+    if (meta && d.send_row >= 0) {
         const int64_t row_i = d.send_row;
         a.send_src[row_i] = t;
         for (int k = 0; k < a.K; ++k) {
@@ -316,8 +317,52 @@ __device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row
             a.send_topk_w[row_i * a.K + k] = on_r ? a.topk_w[tk + k] : 0.0f;
         }
     }
+    return d;
+}
+
+// The per-token part of the high-throughput dispatch, for a wave holding
+// token t's row (first pass loaded, not yet quantised) and its lanes as in
+// token_dests: checks, handle and metadata, then the row to every
+// destination.
+template <bool FP8, typename Row>
+__device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row &row,
+                                               const uint16_t *xrow, int64_t e, int64_t send_r,
+                                               int64_t recv_r)
+{
+    const Dests d = token_dests(a, t, e, send_r, recv_r, true);
     row.quantise(0, FP8 ? a.h >> 4 : a.h >> 3);
     scatter<FP8>(row, d, xrow, a.h, a.send_x, a.send_scales, a.recv_x, a.recv_scales);
+}
+
+// One slice of a token's row (items s0 .. s0 + Row::kPerPass - 1, loaded in
+// `row`, whole 128-channel groups for FP8) to every destination in d.
+template <bool FP8, typename Row>
+__device__ __forceinline__ void scatter_slice(Row &row, const Dests &d, int s0,
+                                              const DispatchArgs &a)
+{
+    const int nitems = FP8 ? a.h >> 4 : a.h >> 3, ld_s = scale_stride(a.h);
+    const size_t row_bytes = FP8 ? (size_t)a.h : (size_t)a.h * 2;
+    row.quantise(s0, nitems);
+    for (uint64_t m = d.rbits; m; m &= m - 1) {
+        const int r = readlane(d.send_row, __builtin_ctzll(m));
+        if (r < 0)
+            continue;
+        if constexpr (FP8)
+            row.template store<StorePolicy::NT>(static_cast<uint8_t *>(a.send_x) + (size_t)r * row_bytes,
+                                                a.send_scales + (size_t)r * ld_s, s0, nitems);
+        else
+            row.store(static_cast<char *>(a.send_x) + (size_t)r * row_bytes, s0, nitems);
+    }
+    for (uint64_t m = d.vbits; m; m &= m - 1) {
+        const int r = readlane(d.recv_row, __builtin_ctzll(m));
+        if (r < 0)
+            continue;
+        if constexpr (FP8)
+            row.template store<StorePolicy::NT>(static_cast<uint8_t *>(a.recv_x) + (size_t)r * row_bytes,
+                                                a.recv_scales + (size_t)r * ld_s, s0, nitems);
+        else
+            row.store(static_cast<char *>(a.recv_x) + (size_t)r * row_bytes, s0, nitems);
+    }
 }
 
 }  // namespace

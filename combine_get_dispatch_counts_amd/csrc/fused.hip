@@ -156,6 +156,132 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     }
 }
 
+// Small batches (T <= kSmallMaxT): one block of kLayoutThreads per token,
+// and every block computes the layout of the whole batch itself in LDS from
+// all T*K entries (as the low-latency kernel does), so no block waits for
+// another and no workspace is touched. Block t then writes token t's rows of
+// is_token_in_rank / pos_in_rank / slot_in_expert (block 0 also the counts,
+// offsets, totals and channel_prefix), and its waves move the token's row in
+// 1024-channel slices w, w + 8, ... to every destination (wave 0 writes the
+// handle and the metadata). The counts are the layout's definition: per
+// expert every valid entry, per rank every token once; positions and slots
+// count the tokens, or entries, before t.
+constexpr int kSmallMaxT = 1024;
+
+__host__ __device__ inline size_t small_lds_bytes(int T, int E, int R)
+{
+    // token rank masks [T], counts [E + R], counts before t [E + R], offsets [E + R + 2]
+    return sizeof(uint64_t) * (size_t)T + sizeof(int) * (3 * (size_t)(E + R) + 2);
+}
+
+template <int KMAX, bool FP8>
+__global__ __launch_bounds__(kLayoutThreads) void fused_small_kernel(FusedArgs f)
+{
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const LayoutArgs &l = f.lay;
+    const DispatchArgs &a = f.disp;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+    const int E = a.E, R = a.R, K = a.K, T = a.T;
+    uint64_t *mask = reinterpret_cast<uint64_t *>(lds);
+    int *cnt = reinterpret_cast<int *>(mask + T);  // [E] per expert, then [R] per rank
+    int *before = cnt + E + R;
+    int *off = before + E + R;  // [E+1] expert offsets, then [R+1] rank offsets
+
+    // the token's experts (lane k) and the wave's first slice go out first
+    const int64_t ek = lane < K ? a.topk_idx[(int64_t)t * K + lane] : -1;
+    typename std::conditional<FP8, RowFp8<1>, RowBf16<2>>::type row;
+    constexpr int per = decltype(row)::kPerPass;  // 1024 channels
+    const int nitems = FP8 ? a.h >> 4 : a.h >> 3;
+    const int nslices = (nitems + per - 1) / per;
+    const uint16_t *xrow = a.x + (size_t)t * a.h;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
+    if (w < nslices)
+        row.load(src, w * per, nitems);
+
+    for (int i = tid; i < 2 * (E + R); i += blockDim.x)
+        cnt[i] = 0;  // cnt and before
+    __syncthreads();
+    // every token of the batch, one thread each
+    int bad = 0;
+    for (int u = tid; u < T; u += blockDim.x) {
+        int eu[KMAX];
+        load_row_experts<KMAX>(l, u, eu);
+        uint64_t m = 0;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int e = eu[k];
+            bad |= (e == -2);
+            if (e < 0)
+                continue;
+            atomicAdd(&cnt[e], 1);
+            if (u < t)
+                atomicAdd(&before[e], 1);
+            m |= 1ull << (e / l.L);
+        }
+        mask[u] = m;
+        for (uint64_t mm = m; mm; mm &= mm - 1) {
+            const int r = __builtin_ctzll(mm);
+            atomicAdd(&cnt[E + r], 1);
+            if (u < t)
+                atomicAdd(&before[E + r], 1);
+        }
+    }
+    if (bad && t == 0)
+        flag_error(a.err, EPX_DEV_BAD_ROUTE);
+    __syncthreads();
+    if (t == 0) {
+        write_totals(l, cnt, off);  // scans into off, then the global outputs
+    } else {
+        if (tid < kWave)
+            wave_exclusive_scan(cnt, E, off);
+        else if (tid < 2 * kWave)
+            wave_exclusive_scan(cnt + E, R, off + E + 1);
+    }
+    __syncthreads();
+    if (t == 0 && l.channel_prefix) {
+        for (int i = tid; i < R * l.C; i += blockDim.x) {
+            const int r = i / l.C, c = i - r * l.C;
+            const int end = (int)channel_end(l, c);
+            int n = 0;
+            for (int u = 0; u < end; ++u)
+                n += (int)((mask[u] >> r) & 1ull);
+            l.channel_prefix[i] = n;
+        }
+    }
+
+    // token t: its row of the layout (wave 0) and its destinations (every wave)
+    const uint64_t mt = mask[t];
+    const bool in_r = lane < R && ((mt >> lane) & 1ull);
+    int64_t send_r = -1, recv_r = -1;
+    if (in_r && a.send_x)
+        send_r = (int64_t)off[E + 1 + lane] + before[E + lane];
+    const bool valid = lane < K && ek >= 0 && ek < E;
+    int slot = -1;
+    {
+        int rep = 0;  // earlier entries of this row with the same expert
+        for (int k2 = 0; k2 < K; ++k2)
+            rep += (k2 < lane && readlane64(ek, k2) == ek);
+        if (valid) {
+            slot = before[ek] + rep;
+            recv_r = (int64_t)off[ek] + slot;
+        }
+    }
+    if (w == 0) {
+        if (lane < R) {
+            l.is_token_in_rank[(int64_t)t * R + lane] = in_r ? 1 : 0;
+            l.pos_in_rank[(int64_t)t * R + lane] = in_r ? before[E + lane] : -1;
+        }
+        if (lane < K)
+            l.slot_in_expert[(int64_t)t * K + lane] = slot;
+    }
+    const Dests d = token_dests(a, t, ek, send_r, recv_r, w == 0);
+    for (int sl = w; sl < nslices; sl += kLayoutThreads / kWave) {
+        if (sl != w)
+            row.load(src, sl * per, nitems);
+        scatter_slice<FP8>(row, d, sl * per, a);
+    }
+}
+
 // Blocks of this kernel one compute unit holds at once for a dynamic LDS
 // size (the occupancy query, cached for the last size asked).
 template <int KMAX, bool FP8, int NV>
@@ -189,13 +315,20 @@ hipError_t launch_fused_k(const FusedArgs &f, hipStream_t stream, bool launch, i
 {
     const size_t lds = layout_tok_lds_bytes(f.lay.E, f.lay.R, f.lay.K);
     const int64_t blocks = fused_grid(f);
-    const bool one = f.lay.ntiles == 0 ||
+    const bool small = f.disp.T >= 1 && f.disp.T <= kSmallMaxT;
+    const bool one = small || f.lay.ntiles == 0 ||
                      (blocks >= f.cus &&
                       blocks <= (int64_t)fused_blocks_per_cu<KMAX, FP8, NV>(lds) * f.cus);
     if (launches)
         *launches = one ? 1 : 2;
     if (!launch)
         return hipSuccess;
+    if (small) {
+        hipLaunchKernelGGL((fused_small_kernel<KMAX, FP8>), dim3((unsigned)f.disp.T),
+                           dim3(kLayoutThreads), small_lds_bytes(f.disp.T, f.disp.E, f.disp.R),
+                           stream, f);
+        return hipGetLastError();
+    }
     if (!one) {
         const hipError_t e = launch_layout(f.lay, stream);
         return e != hipSuccess ? e : launch_dispatch(f.disp, FP8, stream);

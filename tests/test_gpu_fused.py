@@ -87,44 +87,49 @@ def test_fused_edge_cases(T, K, E, R, h, fp8, kind):
     _fused_check(x, topk, w, E, R, fp8, C=5 if T else None)
 
 
-def _one_launch_window(h, K, E, R, fp8):
-    """The smallest and the largest T > 0 that epx_dispatch_fused does in
-    one launch (the grid must cover every compute unit and fit at once)."""
+def _one_launch_runs(h, K, E, R, fp8, top=1 << 15):
+    """The runs of T in [1, top) that epx_dispatch_fused does in one launch:
+    small batches (every block computing the whole layout), then the tiled
+    layout with one token per wave while its grid covers every compute unit
+    and fits at once."""
     import combine_get_dispatch_counts_amd as epx
 
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    one = 8 * cus  # one block per unit: covers all, always fits
-    assert epx.fused_launches(one, h, K, E, R, fp8) == 1
-    assert epx.fused_launches(1, h, K, E, R, fp8) == 2
-    assert epx.fused_launches(1 << 22, h, K, E, R, fp8) == 2
-    lo, hi = 1, one  # launches(lo) == 2, launches(hi) == 1
-    while hi - lo > 1:
-        mid = (lo + hi) // 2
-        lo, hi = (lo, mid) if epx.fused_launches(mid, h, K, E, R, fp8) == 1 else (mid, hi)
-    first = hi
-    lo, hi = one, 1 << 22  # launches(lo) == 1, launches(hi) == 2
-    while hi - lo > 1:
-        mid = (lo + hi) // 2
-        lo, hi = (mid, hi) if epx.fused_launches(mid, h, K, E, R, fp8) == 1 else (lo, mid)
-    return first, lo
+    runs, start = [], None
+    for T in range(1, top):
+        one = epx.fused_launches(T, h, K, E, R, fp8) == 1
+        if one and start is None:
+            start = T
+        if not one and start is not None:
+            runs.append((start, T - 1))
+            start = None
+    assert start is None, "one launch up to the end of the scan"
+    return runs
+
+
+def _one_launch_window(h, K, E, R, fp8):
+    """The one-token-per-wave run (the last run of one-launch shapes)."""
+    return _one_launch_runs(h, K, E, R, fp8)[-1]
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("edge", ["below", "first", "last", "above"])
+@pytest.mark.parametrize("edge", ["one", "small_last", "gap", "first", "last", "above"])
 def test_fused_one_and_two_launches(fp8, edge):
-    """One launch for T in a window (the grid covers every compute unit and
-    fits on the device at once), two on either side; both edges of the
-    window and the shapes just outside it against the oracle."""
+    """Where epx_dispatch_fused is one launch and where two: T = 1, the
+    largest small batch, a shape between the two runs, both ends of the
+    one-token-per-wave run and the shape past it, each against the oracle."""
     import combine_get_dispatch_counts_amd as epx
 
     h, K, E, R = 128, 4, 16, 4
-    first, last = _one_launch_window(h, K, E, R, fp8)
-    assert first <= last
+    runs = _one_launch_runs(h, K, E, R, fp8)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert len(runs) == 2 and runs[0][0] == 1, runs
+    assert runs[1][0] <= 8 * cus <= runs[1][1], runs
     assert epx.fused_launches(0, h, K, E, R, fp8) == 1
-    T = {"below": first - 1, "first": first, "last": last, "above": last + 1}[edge]
-    want = 1 if edge in ("first", "last") else 2
+    T, want = {"one": (1, 1), "small_last": (runs[0][1], 1), "gap": (runs[0][1] + 1, 2),
+               "first": (runs[1][0], 1), "last": (runs[1][1], 1),
+               "above": (runs[1][1] + 1, 2)}[edge]
     assert epx.fused_launches(T, h, K, E, R, fp8) == want
-    say(f"fused T={T} h={h} K={K} fp8={fp8} (window {first}..{last}, {want} launch(es))")
+    say(f"fused T={T} h={h} K={K} fp8={fp8} (one-launch runs {runs}, {want} launch(es))")
     rng = np.random.default_rng(T + h)
     x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
     topk = synth.random_routing(T, K, E, seed=T + 1, p_drop=0.1)
@@ -158,28 +163,37 @@ def test_fused_kernel_edge_cases(K, E, R, h, fp8, kind):
 
 
 def test_fused_shares_workspace_with_layout():
-    """One workspace for fused calls and two-launch layout calls in turn."""
+    """One workspace for fused calls (small batches, which do not touch it,
+    and one-launch / two-launch ones, which do) and two-launch layout calls
+    in turn. After every call the counters are ready: no arrival pending,
+    no finished-block count left, the call number never going back."""
     import combine_get_dispatch_counts_amd as epx
 
     E, R, K, h = 64, 8, 6, 512
-    ws = torch.zeros(epx.fused_workspace_size(2048, K, E, R), dtype=torch.uint8, device="cuda")
-    for i, T in enumerate([2048, 700, 2048, 1]):
+    ws = torch.zeros(epx.fused_workspace_size(4096, K, E, R), dtype=torch.uint8, device="cuda")
+    last = 0
+
+    def counters(what):
+        nonlocal last
+        head = ws[:128].cpu().numpy()  # calls << 32 | arrivals at byte 0; finished blocks at 64
+        calls = int(head[:8].view(np.uint64)[0])
+        assert calls & 0xFFFFFFFF == 0, f"arrivals pending after {what}: {calls:#x}"
+        assert int(head[64:68].view(np.uint32)[0]) == 0, f"finished-block count left by {what}"
+        assert calls >> 32 >= last, f"call number went back after {what}"
+        last = calls >> 32
+
+    for i, T in enumerate([2048, 700, 4096, 1, 2048, 3000]):
         rng = np.random.default_rng(40 + i)
         x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
         topk = synth.random_routing(T, K, E, seed=50 + i)
         w = rng.random((T, K)).astype(np.float32)
-        say(f"fused call {i} T={T} on a shared workspace")
+        say(f"fused call {i} T={T} ({epx.fused_launches(T, h, K, E, R)} launch(es)) on a shared "
+            "workspace")
         _fused_check(x, topk, w, E, R, False, ws=ws)
-        # the counters are left ready: one more call completed, no block of
-        # a call pending (head: calls << 32 | arrivals at byte 0, finished
-        # blocks of a fused call at byte 64)
-        head = ws[:128].cpu().numpy()
-        calls = int(head[:8].view(np.uint64)[0])
-        assert calls == (2 * i + 1) << 32, f"call counter {calls:#x} after fused call {i}"
-        assert int(head[64:68].view(np.uint32)[0]) == 0, "finished-block counter not reset"
+        counters(f"fused call {i}")
         lay = epx.get_dispatch_layout(torch.from_numpy(topk).cuda(), E, R, workspace=ws)
         assert epx.get_error() == 0
-        assert int(ws[:8].cpu().numpy().view(np.uint64)[0]) == (2 * i + 2) << 32
+        counters(f"layout call {i}")
         ol = oracle.layout(topk, E, R)
         for k in LAYOUT_KEYS:
             _eq(host_bits(getattr(lay, k)), ol[k], f"layout call {i} {k}")
