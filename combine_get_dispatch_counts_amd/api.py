@@ -292,8 +292,9 @@ def fused_workspace_size(T: int, K: int, E: int, R: int) -> int:
 
 def fused_launches(T: int, h: int, K: int, E: int, R: int, fp8: bool = False,
                    device: torch.device | None = None) -> int:
-    """How many launches dispatch_fused takes for this shape (1 while its
-    grid covers every compute unit and fits on the device at once, else 2)."""
+    """How many launches dispatch_fused takes for this shape: 1 for small
+    batches (T <= 1024) and while the tiled grid covers every compute unit
+    and fits on the device at once, else 2."""
     device = device or torch.device("cuda", torch.cuda.current_device())
     n = ctypes.c_int()
     check(_lib.load().epx_fused_launches(_ctx(device), T, h, K, E, R, int(fp8), ctypes.byref(n)),

@@ -35,10 +35,11 @@
 // h = 7168, half the waves). With fewer blocks than compute units, on the
 // other hand, a token's eight waves share one unit's store path while other
 // units idle. The host therefore launches this kernel when its grid covers
-// every compute unit and, by the occupancy query, fits on the chip at once,
-// and otherwise runs the layout and the dispatch as two launches, whose
-// 64-thread dispatch blocks spread one wave per token over the chip and
-// free their place wave by wave. Layout blocks come first in the grid;
+// every compute unit and, by the occupancy query, fits on the chip at once;
+// small batches go to fused_small_kernel below, and everything else runs
+// the layout and the dispatch as two launches, whose 64-thread dispatch
+// blocks spread one wave per token over the chip and free their place wave
+// by wave. Layout blocks come first in the grid;
 // dispatch-only blocks issue their row loads before waiting, so the loads
 // overlap the layout. Every wait is bounded.
 #include <atomic>

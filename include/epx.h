@@ -205,10 +205,12 @@ int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
  * again); calls that share it must not overlap, and it may be shared with
  * epx_get_dispatch_layout calls of any shape. The
  * capacities must be known up front (no host wait happens): T*min(K,R) send
- * rows and T*K receive rows always suffice. One launch while its grid
+ * rows and T*K receive rows always suffice. One launch for T <= 1024
+ * (every block then computes the whole batch's layout itself and leaves the
+ * workspace untouched), and for larger T while the tiled grid
  * (max(ceil(T/256) + 1, ceil(T/8)) blocks of 512 threads) covers every
  * compute unit and fits on the device at once (at h = 7168 and 256 units:
- * 2048 <= T <= 4096), else the layout and the dispatch are launched one
+ * 2048 <= T <= 4096); else the layout and the dispatch are launched one
  * after the other (epx_fused_launches says which; T = 0 is one launch). */
 /* How many launches epx_dispatch_fused takes for this shape on the
  * context's device (host out: 1 or 2, see above); arguments as there.
