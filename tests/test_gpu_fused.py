@@ -266,3 +266,27 @@ def test_fused_workspace_recovery():
     ws.zero_()
     say("fused call after the workspace was zeroed")
     _fused_check(x, topk, w, E, R, False, ws=ws)
+
+
+@pytest.mark.parametrize("T", [100, 4096, 9000])
+def test_fused_flags_bad_route(T):
+    """A top-k entry outside [-1, E) sets EPX_DEV_BAD_ROUTE in every regime
+    of the fused call (small batch, tiled one launch, two launches); the
+    entry is skipped, so no row lands outside the buffers."""
+    import combine_get_dispatch_counts_amd as epx
+
+    E, R, K, h = 64, 8, 4, 256
+    rng = np.random.default_rng(T)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=T)
+    topk[T // 2, 1] = E + 5
+    topk[T - 1, 0] = -7
+    w = rng.random((T, K)).astype(np.float32)
+    say(f"fused call with bad routes T={T} ({epx.fused_launches(T, h, K, E, R)} launch(es))")
+    d = epx.dispatch_fused(dev_bf16(x), torch.from_numpy(topk).cuda(), torch.from_numpy(w).cuda(),
+                           E, R)
+    flags = epx.get_error()
+    assert flags == epx._lib.DEV_BAD_ROUTE, f"expected EPX_DEV_BAD_ROUTE, got {flags:#x}"
+    pos = host_bits(d.pos_exp)
+    assert pos[T // 2, 1] == -1 and pos[T - 1, 0] == -1
+    assert int(d.layout.totals[1]) == T * K - 2
