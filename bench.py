@@ -82,6 +82,9 @@ def step_bytes(T, h, K, R, n_rank, n_exp):
     return dict(layout=layout, dispatch=dispatch, combine=combine)
 
 
+GRAPH_STEPS = 5  # steps captured per HIP graph for the graph figure
+
+
 def layout_bytes(T, K, E, R):
     """Compulsory bytes of the layout (topk_idx in; is_token_in_rank,
     pos_in_rank, slot_in_expert out; the small count and offset arrays
@@ -653,8 +656,9 @@ def main():
     dispatch_us = back_to_back_us(lambda: epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs))
     assert epx.get_error() == 0
 
-    # the same step captured once in a HIP graph and replayed (no host launch
-    # work per step); checked against the eager result first
+    # the step captured in a HIP graph (GRAPH_STEPS steps per graph, as a
+    # model's graph holds several layers) and replayed, no host launch work
+    # per step; checked against the eager result first
     graph_us = None
     if args.graph:
         ref_out = out.clone()
@@ -665,18 +669,20 @@ def main():
         torch.cuda.current_stream().wait_stream(side)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step()
+            for _ in range(GRAPH_STEPS):
+                step()
         out.zero_()
         g.replay()
         torch.cuda.synchronize()
         if not torch.equal(out.view(torch.int16), ref_out.view(torch.int16)):
             raise RuntimeError("graph replay differs from the eager step")
         torch.cuda.synchronize()
+        reps = max(1, args.steps // GRAPH_STEPS)
         tg0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(reps):
             g.replay()
         torch.cuda.synchronize()
-        graph_us = (time.perf_counter() - tg0) * 1e6 / args.steps
+        graph_us = (time.perf_counter() - tg0) * 1e6 / (reps * GRAPH_STEPS)
         del g, ref_out
 
     # labelled cold-cache figure: flush the 256 MB MALL before each step
