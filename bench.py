@@ -708,7 +708,12 @@ def main():
         b.copy_(a)
         ceil["d2d_copy_gbs"] = round(2 * (1 << 30) / (_loop_us(lambda: b.copy_(a), 10) * 1e3), 1)
         ceil["fill_gbs"] = round((1 << 30) / (_loop_us(lambda: a.fill_(3), 10) * 1e3), 1)
-        del a, b
+        # a plain streaming read+write kernel (elementwise, vectorised loads
+        # and stores) rather than the runtime's copy path
+        ai, bi = a.view(torch.int32), b.view(torch.int32)
+        ceil["rw_kernel_gbs"] = round(
+            2 * (1 << 30) / (_loop_us(lambda: torch.add(ai, 0, out=bi), 10) * 1e3), 1)
+        del a, b, ai, bi
 
     by = step_bytes(T, h, K, R, n_rank, n_exp)
     bmin = survey_bmin(T, h, K, R, n_rank, n_exp)
@@ -764,6 +769,7 @@ def main():
                        "dispatch_traffic": measured_traffic("dispatch_kernel")},
         "ceilings": ceil or None,
         "frac_of_copy_ceiling": round(gbs / ceil["d2d_copy_gbs"], 4) if ceil else None,
+        "frac_of_rw_kernel_ceiling": round(gbs / ceil["rw_kernel_gbs"], 4) if ceil else None,
         "cold_cache_us_per_layer": round(cold_us, 2) if cold_us else None,
         "graph_us_per_layer": round(graph_us, 2) if graph_us else None,
         "fused_kernel_us": round(fused_us, 2),
