@@ -49,6 +49,10 @@ def _edge_cases():
         cases.append(("uniform", 300, K, 64, 8, 7, 0.0))
     for R in (1, 4, 8, 32, 64):
         cases.append(("uniform", 513, 4, 128, R, 33, 0.0))
+    # ranks that are not powers of two: multiples of 4 (12, 24, 48; 48 also a
+    # multiple of 16) and others (2, 3, 6) take the layout's other row paths
+    for R in (2, 3, 6, 12, 24, 48):
+        cases.append(("uniform", 777, 6, 96, R, 9, 0.05))
     cases.append(("dropped", 700, 8, 256, 32, 5, 0.3))
     cases.append(("one_expert", 1000, 1, 64, 8, 10, 0.0))
     cases.append(("max_experts", 600, 8, 512, 64, 3, 0.0))
