@@ -92,7 +92,7 @@ def layout_bytes(T, K, E, R):
     return 8 * T * K + T * R + 4 * T * R + 4 * T * K
 
 
-def survey_bmin(T, h, K, R, n_rank, n_exp):
+def compulsory_step_bytes(T, h, K, R, n_rank, n_exp):
     """The whole-step compulsory byte count used for `value`."""
     row = 2 * h
     disp = T * row + 12 * T * K + n_rank * row + n_exp * row + (
@@ -357,7 +357,7 @@ def other_workloads(n=20):
         "max_tokens_per_expert": int(lay.num_tokens_per_expert.max()),
         "layout_us": round(lay_us, 2), "dispatch": rec(d_us, by["dispatch"]),
         "combine": rec(c_us, by["combine"]), "step_us": round(lay_us + d_us + c_us, 2),
-        "step_gbs": round(survey_bmin(T, h, K, R, n_rank, n_exp) / ((lay_us + d_us + c_us) * 1e-6) / 1e9, 1)}
+        "step_gbs": round(compulsory_step_bytes(T, h, K, R, n_rank, n_exp) / ((lay_us + d_us + c_us) * 1e-6) / 1e9, 1)}
     return out
 
 
@@ -533,8 +533,8 @@ def main():
                     help="MALL flush size for the labelled cold-cache figure (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the one-GPU share of the path; runs on more than one GPU "
-              "are not part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU's share of the path; runs on more than one GPU "
+              "are not supported (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -716,7 +716,7 @@ def main():
         del a, b, ai, bi
 
     by = step_bytes(T, h, K, R, n_rank, n_exp)
-    bmin = survey_bmin(T, h, K, R, n_rank, n_exp)
+    bmin = compulsory_step_bytes(T, h, K, R, n_rank, n_exp)
     gbs = bmin / (ms_per_step * 1e-3) / 1e9
     fused_bytes = by["layout"] + by["dispatch"]
     fused_gbs = fused_bytes / (fused_us * 1e-6) / 1e9
@@ -733,7 +733,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         med, nr, ne, reps = cpu_baseline(inp, wl)
-        cpu = {"value": round(survey_bmin(T, h, K, R, nr, ne) / med / 1e9, 3), "unit": "GB/s",
+        cpu = {"value": round(compulsory_step_bytes(T, h, K, R, nr, ne) / med / 1e9, 3), "unit": "GB/s",
                "cores": 1, "kind": "oracle",
                "sample": f"the full prefill workload (T={T}, one layer: layout+dispatch+combine), "
                          f"median of {reps} single-threaded runs, {med * 1e3:.0f} ms each"}
