@@ -75,6 +75,7 @@ def test_fused_workloads_full_size(cfg):
     (300, 4, 16, 4, 128, False, "repeats"), (0, 4, 16, 4, 128, False, "uniform"),
     (513, 4, 128, 8, 512, False, "uniform"), (400, 6, 96, 12, 256, True, "dropped"),
     (999, 8, 96, 48, 128, False, "uniform"), (77, 3, 96, 6, 128, False, "repeats"),
+    (130, 8, 256, 32, 7168, True, "dropped"),
 ])
 def test_fused_edge_cases(T, K, E, R, h, fp8, kind):
     say(f"fused T={T} K={K} E={E} R={R} h={h} fp8={fp8} {kind}")
