@@ -212,11 +212,6 @@ int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
  * compute unit and fits on the device at once (at h = 7168 and 256 units:
  * 2048 <= T <= 4096); else the layout and the dispatch are launched one
  * after the other (epx_fused_launches says which; T = 0 is one launch). */
-/* How many launches epx_dispatch_fused takes for this shape on the
- * context's device (host out: 1 or 2, see above); arguments as there.
- * Nothing is launched. */
-int epx_fused_launches(epx_ctx *ctx, int T, int h, int K, int E, int R, int fp8, int *launches);
-
 int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
                        const float *topk_w, int T, int K, int E, int R, int C,
                        int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
@@ -227,6 +222,11 @@ int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *to
                        int64_t *send_topk_idx, float *send_topk_w, int64_t send_cap_rows,
                        void *recv_x, float *recv_scales, int32_t *recv_src,
                        int64_t recv_cap_rows, int32_t *pos_exp, hipStream_t stream);
+
+/* How many launches epx_dispatch_fused takes for this shape on the
+ * context's device (host out: 1 or 2, see above); arguments as there.
+ * Nothing is launched. */
+int epx_fused_launches(epx_ctx *ctx, int T, int h, int K, int E, int R, int fp8, int *launches);
 
 /* Combine: reduce expert outputs back to source-token order. [P2] "combine
  * 过程" (route back through the handle, reduce per source token); [P1]
