@@ -41,15 +41,67 @@ def _p(t: torch.Tensor | None) -> ctypes.c_void_p | None:
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int | None = None):
+def _need(t: torch.Tensor | None, dtype: torch.dtype, name: str, ndim: int | None = None,
+          shape: tuple | None = None, device: torch.device | None = None):
+    """Reject what the kernels cannot take: the C ABI sees bare pointers and
+    row counts, so every buffer's dtype, shape and device is checked here."""
+    if t is None:
+        raise ValueError(f"{name} is missing")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _nbytes(ws: torch.Tensor, dev: torch.device) -> int:
+    if not ws.is_cuda or ws.device != dev or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    return ws.numel() * ws.element_size()
+
+
+def _check_layout(lay: "Layout", T: int, K: int, E: int, R: int, C: int | None,
+                  dev: torch.device) -> None:
+    i32 = torch.int32
+    _need(lay.num_tokens_per_expert, i32, "num_tokens_per_expert", shape=(E,), device=dev)
+    _need(lay.num_tokens_per_rank, i32, "num_tokens_per_rank", shape=(R,), device=dev)
+    _need(lay.is_token_in_rank, torch.uint8, "is_token_in_rank", shape=(T, R), device=dev)
+    _need(lay.rank_off, i32, "rank_off", shape=(R + 1,), device=dev)
+    _need(lay.exp_off, i32, "exp_off", shape=(E + 1,), device=dev)
+    _need(lay.pos_in_rank, i32, "pos_in_rank", shape=(T, R), device=dev)
+    _need(lay.slot_in_expert, i32, "slot_in_expert", shape=(T, K), device=dev)
+    _need(lay.totals, i32, "totals", shape=(2,), device=dev)
+    if C:
+        _need(lay.channel_prefix, i32, "channel_prefix", shape=(R, C), device=dev)
+
+
+def _check_dispatch_out(out: dict, T: int, h: int, K: int, fp8: bool,
+                        dev: torch.device) -> None:
+    """``out`` as alloc_dispatch makes it (row slices of those tensors
+    included): the send arrays share send_x's row count, the receive
+    arrays recv_x's."""
+    dt = torch.uint8 if fp8 else torch.bfloat16
+    _need(out.get("send_x"), dt, "send_x", ndim=2, device=dev)
+    _need(out.get("recv_x"), dt, "recv_x", ndim=2, device=dev)
+    ns, nr = out["send_x"].shape[0], out["recv_x"].shape[0]
+    _need(out["send_x"], dt, "send_x", shape=(ns, h))
+    _need(out["recv_x"], dt, "recv_x", shape=(nr, h))
+    _need(out.get("send_src"), torch.int32, "send_src", shape=(ns,), device=dev)
+    _need(out.get("send_topk_idx"), torch.int64, "send_topk_idx", shape=(ns, K), device=dev)
+    _need(out.get("send_topk_w"), torch.float32, "send_topk_w", shape=(ns, K), device=dev)
+    _need(out.get("recv_src"), torch.int32, "recv_src", shape=(nr,), device=dev)
+    _need(out.get("pos_exp"), torch.int32, "pos_exp", shape=(T, K), device=dev)
+    if fp8:
+        st = scale_stride(h)
+        _need(out.get("send_scales"), torch.float32, "send_scales", shape=(ns, st), device=dev)
+        _need(out.get("recv_scales"), torch.float32, "recv_scales", shape=(nr, st), device=dev)
 
 
 _workspaces: dict[tuple[int, int], torch.Tensor] = {}
@@ -134,15 +186,10 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
     T, K = topk_idx.shape
     E, R = num_experts, num_ranks
     lay = out if out is not None else alloc_layout(T, K, E, R, num_channels, dev)
-    if out is not None:
-        if tuple(lay.pos_in_rank.shape) != (T, R) or tuple(lay.slot_in_expert.shape) != (T, K) \
-                or lay.num_tokens_per_expert.numel() != E:
-            raise ValueError("out was allocated for different shapes")
-        if num_channels and (lay.channel_prefix is None
-                             or tuple(lay.channel_prefix.shape) != (R, num_channels)):
-            raise ValueError("out has no channel_prefix of shape (R, num_channels)")
+    _check_layout(lay, T, K, E, R, num_channels, dev)
     if workspace is None:
         workspace = _layout_workspace(dev, workspace_size(T, K, E, R))
+    ws_bytes = _nbytes(workspace, dev)
     if totals_host is not None and not (totals_host.is_pinned() and totals_host.numel() >= 2
                                         and totals_host.dtype == torch.int32):
         raise ValueError("totals_host must be a pinned int32 tensor of >= 2 elements")
@@ -152,7 +199,7 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
         _p(lay.num_tokens_per_expert), _p(lay.num_tokens_per_rank), _p(lay.is_token_in_rank),
         _p(lay.rank_off), _p(lay.exp_off), _p(lay.pos_in_rank), _p(lay.slot_in_expert),
         _p(cp), _p(lay.totals), _p(totals_host), _p(workspace),
-        workspace.numel(), _stream(dev))
+        ws_bytes, _stream(dev))
     check(rc, "epx_get_dispatch_layout")
     return lay
 
@@ -211,21 +258,22 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor
     wait before allocating the receive tensor); otherwise worst-case sizes
     T*min(K,R) and T*K rows are used and no wait happens."""
     _need(x, torch.bfloat16, "x", 2)
-    _need(topk_idx, torch.int64, "topk_idx", 2)
-    _need(topk_weights, torch.float32, "topk_weights", 2)
     dev = x.device
     T, h = x.shape
+    _need(topk_idx, torch.int64, "topk_idx", 2, device=dev)
     K = topk_idx.shape[1]
-    if topk_idx.shape[0] != T or tuple(topk_weights.shape) != (T, K):
-        raise ValueError("x, topk_idx and topk_weights disagree on T or K")
+    _need(topk_idx, torch.int64, "topk_idx", shape=(T, K))
+    _need(topk_weights, torch.float32, "topk_weights", shape=(T, K), device=dev)
     if layout is None:
         layout = get_dispatch_layout(topk_idx, num_experts, num_ranks)
+    _check_layout(layout, T, K, num_experts, num_ranks, None, dev)
     if out is None:
         if exact:
             n_send, n_recv = (int(v) for v in layout.totals.cpu())
         else:
             n_send, n_recv = T * min(K, num_ranks), T * K
         out = alloc_dispatch(T, h, K, n_send, n_recv, fp8, dev)
+    _check_dispatch_out(out, T, h, K, fp8, dev)
     rc = _lib.load().epx_dispatch(
         _ctx(dev), _p(x), h, _p(topk_idx), _p(topk_weights), T, K, num_experts, num_ranks,
         _p(layout.rank_off), _p(layout.exp_off), _p(layout.pos_in_rank),
@@ -257,9 +305,11 @@ def recv_permute(rows: torch.Tensor, local_topk_idx: torch.Tensor, num_local_exp
     ``local_topk_idx`` [N, K] int64 holds each row's local expert indices
     (-1 for entries of other ranks), as dispatch's send_topk_idx does. The
     payload is copied bit for bit by the dispatch kernel's permute."""
-    _need(local_topk_idx, torch.int64, "local_topk_idx", 2)
     dev = rows.device
+    _need(local_topk_idx, torch.int64, "local_topk_idx", 2, device=dev)
     N, K = local_topk_idx.shape
+    if scales is not None and scales.device != dev:
+        raise ValueError(f"scales are on {scales.device}, the rows on {dev}")
     L = num_local_experts
     lay = get_dispatch_layout(local_topk_idx, L, 1)
     cap = N * K
@@ -268,8 +318,9 @@ def recv_permute(rows: torch.Tensor, local_topk_idx: torch.Tensor, num_local_exp
     pos = torch.empty((N, K), dtype=torch.int32, device=dev)
     src_row = torch.empty(cap, dtype=torch.int32, device=dev)
     for pl in payloads:
-        if not pl.is_contiguous() or pl.shape[0] != N:
-            raise ValueError("payload rows must be contiguous with one row per received row")
+        if not pl.is_cuda or not pl.is_contiguous() or pl.dim() != 2 or pl.shape[0] != N:
+            raise ValueError("payload rows must be a contiguous 2-d GPU tensor with one row "
+                             "per received row")
         v = pl.view(torch.uint8).view(N, -1).view(torch.bfloat16)
         hh = v.shape[1]
         out = torch.empty((cap, hh), dtype=torch.bfloat16, device=dev)
@@ -316,19 +367,21 @@ def dispatch_fused(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.
     zero-filled before its first use (without one, a cached workspace per
     device and stream is used)."""
     _need(x, torch.bfloat16, "x", 2)
-    _need(topk_idx, torch.int64, "topk_idx", 2)
-    _need(topk_weights, torch.float32, "topk_weights", 2)
     dev = x.device
     T, h = x.shape
+    _need(topk_idx, torch.int64, "topk_idx", 2, device=dev)
     K = topk_idx.shape[1]
+    _need(topk_idx, torch.int64, "topk_idx", shape=(T, K))
+    _need(topk_weights, torch.float32, "topk_weights", shape=(T, K), device=dev)
     E, R = num_experts, num_ranks
-    if topk_idx.shape[0] != T or tuple(topk_weights.shape) != (T, K):
-        raise ValueError("x, topk_idx and topk_weights disagree on T or K")
     lay = layout if layout is not None else alloc_layout(T, K, E, R, num_channels, dev)
+    _check_layout(lay, T, K, E, R, num_channels, dev)
     if out is None:
         out = alloc_dispatch(T, h, K, T * min(K, R), T * K, fp8, dev)
+    _check_dispatch_out(out, T, h, K, fp8, dev)
     if workspace is None:
         workspace = _layout_workspace(dev, fused_workspace_size(T, K, E, R))
+    ws_bytes = _nbytes(workspace, dev)
     if totals_host is not None and not (totals_host.is_pinned() and totals_host.numel() >= 2
                                         and totals_host.dtype == torch.int32):
         raise ValueError("totals_host must be a pinned int32 tensor of >= 2 elements")
@@ -337,7 +390,7 @@ def dispatch_fused(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.
         _ctx(dev), _p(x), h, _p(topk_idx), _p(topk_weights), T, K, E, R, num_channels or 0,
         _p(lay.num_tokens_per_expert), _p(lay.num_tokens_per_rank), _p(lay.is_token_in_rank),
         _p(lay.rank_off), _p(lay.exp_off), _p(lay.pos_in_rank), _p(lay.slot_in_expert),
-        _p(cp), _p(lay.totals), _p(totals_host), _p(workspace), workspace.numel(), int(fp8),
+        _p(cp), _p(lay.totals), _p(totals_host), _p(workspace), ws_bytes, int(fp8),
         _p(out["send_x"]), _p(out["send_scales"]), _p(out["send_src"]),
         _p(out["send_topk_idx"]), _p(out["send_topk_w"]), out["send_x"].shape[0],
         _p(out["recv_x"]), _p(out["recv_scales"]), _p(out["recv_src"]), out["recv_x"].shape[0],
@@ -350,13 +403,14 @@ def combine(expert_out: torch.Tensor, pos: torch.Tensor, topk_weights: torch.Ten
             out: torch.Tensor | None = None) -> torch.Tensor:
     """out[t] = bf16(sum over valid k, in k order, of w[t,k] * expert_out[pos[t,k]])."""
     _need(expert_out, torch.bfloat16, "expert_out", 2)
-    _need(pos, torch.int32, "pos", 2)
-    _need(topk_weights, torch.float32, "topk_weights", 2)
     dev = expert_out.device
+    _need(pos, torch.int32, "pos", 2, device=dev)
     T, K = pos.shape
     h = expert_out.shape[1]
+    _need(topk_weights, torch.float32, "topk_weights", shape=(T, K), device=dev)
     if out is None:
         out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", shape=(T, h), device=dev)
     rc = _lib.load().epx_combine(_ctx(dev), _p(expert_out), expert_out.shape[0], h,
                                  _p(topk_weights), _p(pos), T, K, _p(out), _stream(dev))
     check(rc, "epx_combine")
@@ -372,13 +426,20 @@ def combine_partial(expert_out: torch.Tensor, dispatched: Dispatched,
     _need(expert_out, torch.bfloat16, "expert_out", 2)
     dev = expert_out.device
     d = dispatched
+    _need(d.send_topk_idx, torch.int64, "send_topk_idx", 2, device=dev)
     cap, K = d.send_topk_idx.shape
+    _need(d.pos_exp, torch.int32, "pos_exp", 2, device=dev)
     T = d.pos_exp.shape[0]
     h = expert_out.shape[1]
+    _need(d.pos_exp, torch.int32, "pos_exp", shape=(T, K))
+    _need(d.send_src, torch.int32, "send_src", shape=(cap,), device=dev)
+    _need(d.send_topk_w, torch.float32, "send_topk_w", shape=(cap, K), device=dev)
     if out is None:
         out = torch.empty((cap, h), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", shape=(cap, h), device=dev)
     if num_rows is None:
         num_rows = d.layout.totals[:1]
+    _need(num_rows, torch.int32, "num_rows", shape=(1,), device=dev)
     rc = _lib.load().epx_combine_partial(
         _ctx(dev), _p(expert_out), expert_out.shape[0], h, _p(d.send_src), _p(d.send_topk_idx),
         _p(d.send_topk_w), _p(d.pos_exp), T, K, cap, _p(num_rows), _p(out), _stream(dev))
@@ -391,10 +452,13 @@ def combine_final(partial: torch.Tensor, layout: Layout,
     """Stage 2: each token's partial rows summed in rank order (fp32) into bf16."""
     _need(partial, torch.bfloat16, "partial", 2)
     dev = partial.device
+    _need(layout.pos_in_rank, torch.int32, "pos_in_rank", 2, device=dev)
     T, R = layout.pos_in_rank.shape
+    _need(layout.rank_off, torch.int32, "rank_off", shape=(R + 1,), device=dev)
     h = partial.shape[1]
     if out is None:
         out = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", shape=(T, h), device=dev)
     rc = _lib.load().epx_combine_final(_ctx(dev), _p(partial), partial.shape[0], h,
                                        _p(layout.rank_off), _p(layout.pos_in_rank), T, R, _p(out),
                                        _stream(dev))
@@ -442,18 +506,29 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
     launch; ``stats`` (int32 [2] on the device) receives the entries routed
     and the fullest region's count."""
     _need(x, torch.bfloat16, "x", 2)
-    _need(topk_idx, torch.int64, "topk_idx", 2)
     dev = x.device
     T, h = x.shape
+    _need(topk_idx, torch.int64, "topk_idx", 2, device=dev)
     K = topk_idx.shape[1]
+    _need(topk_idx, torch.int64, "topk_idx", shape=(T, K))
     R_buf = num_ranks if R_buf is None else R_buf
     if buf is None:
         buf = alloc_ll(num_experts, R_buf, cap, h, T, K, fp8, dev)
+    rows = num_experts * R_buf * cap
+    _need(buf.ll_x, torch.uint8 if fp8 else torch.bfloat16, "ll_x", shape=(rows, h), device=dev)
+    if fp8:
+        _need(buf.ll_scales, torch.float32, "ll_scales", shape=(rows, scale_stride(h)),
+              device=dev)
+    _need(buf.ll_src, torch.int32, "ll_src", shape=(rows,), device=dev)
+    _need(buf.ll_count, torch.int32, "ll_count", shape=(num_experts * R_buf,), device=dev)
+    _need(buf.pos_ll, torch.int32, "pos_ll", shape=(T, K), device=dev)
     if stats is not None:
-        _need(stats, torch.int32, "stats")
+        _need(stats, torch.int32, "stats", device=dev)
         if stats.numel() < 2:
             raise ValueError("stats needs 2 int32 entries")
     nxt = next_buf.ll_count if next_buf is not None else None
+    if nxt is not None:
+        _need(nxt, torch.int32, "next_buf.ll_count", device=dev)
     rc = _lib.load().epx_ll_dispatch(
         _ctx(dev), _p(x), h, _p(topk_idx), T, K, num_experts, num_ranks, src_rank, cap, R_buf,
         int(fp8), _p(buf.ll_x), _p(buf.ll_scales), _p(buf.ll_src), _p(buf.ll_count),

@@ -515,6 +515,86 @@ def test_error_paths():
     assert bool((buf.ll_x[4:].view(torch.uint8) == CANARY).all())
 
 
+def test_binding_rejects_mismatched_buffers():
+    """The C ABI takes bare pointers and row counts, so the binding checks
+    every caller-supplied buffer's dtype, shape and device first: each bad
+    buffer below raises before anything is launched, and the device flags
+    stay clear."""
+    import combine_get_dispatch_counts_amd as epx
+
+    inp = synth.make_inputs(1)
+    wl = inp["workload"]
+    T, h, K, E, R = wl.T, wl.h, wl.K, wl.E, wl.R
+    dev = torch.device("cuda", torch.cuda.current_device())
+    x, tk, w = dev_bf16(inp["x"]), torch.from_numpy(inp["topk_idx"]).cuda(), \
+        torch.from_numpy(inp["topk_w"]).cuda()
+    lay = epx.get_dispatch_layout(tk, E, R)
+    cap_s, cap_r = T * min(K, R), T * K
+
+    def bad_out(fp8=False, **repl):
+        out = epx.alloc_dispatch(T, h, K, cap_s, cap_r, fp8, dev)
+        out.update(repl)
+        return out
+
+    say("binding: mismatched dispatch buffers")
+    cases = [
+        (ValueError, dict(send_src=torch.empty(cap_s - 1, dtype=torch.int32, device=dev))),
+        (ValueError, dict(send_topk_idx=torch.empty((cap_s, K + 1), dtype=torch.int64,
+                                                    device=dev))),
+        (TypeError, dict(recv_src=torch.empty(cap_r, dtype=torch.int64, device=dev))),
+        (ValueError, dict(pos_exp=torch.empty((T - 1, K), dtype=torch.int32, device=dev))),
+        (ValueError, dict(recv_x=torch.empty((cap_r, h), dtype=torch.bfloat16,
+                                             device=dev)[:, :h - 8])),
+        (ValueError, dict(send_topk_w=torch.empty((cap_s, K), dtype=torch.float32))),
+    ]
+    for exc, repl in cases:
+        with pytest.raises(exc):
+            epx.dispatch(x, tk, w, E, R, layout=lay, out=bad_out(**repl))
+        with pytest.raises(exc):
+            epx.dispatch_fused(x, tk, w, E, R, out=bad_out(**repl))
+    with pytest.raises(TypeError):  # bf16 rows where FP8 codes belong
+        epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bad_out(False))
+    with pytest.raises(ValueError):
+        epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay,
+                     out=bad_out(True, recv_scales=torch.empty((cap_r, 1), device=dev)))
+    with pytest.raises(ValueError):
+        epx.dispatch(x, tk, w.cpu(), E, R, layout=lay, out=bad_out())
+    with pytest.raises(ValueError):
+        epx.dispatch(x, tk[:, :K - 1].contiguous(), w, E, R, layout=lay, out=bad_out())
+
+    say("binding: mismatched layout buffers and workspaces")
+    with pytest.raises(ValueError):
+        epx.get_dispatch_layout(tk, E, R, out=epx.alloc_layout(T + 1, K, E, R, None, dev))
+    with pytest.raises(ValueError):
+        epx.get_dispatch_layout(tk, E, R, 4, out=epx.alloc_layout(T, K, E, R, None, dev))
+    with pytest.raises(ValueError):
+        epx.get_dispatch_layout(tk, E, R, workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        epx.dispatch(x, tk, w, E, R, layout=epx.alloc_layout(T, K, 2 * E, R, None, dev),
+                     out=bad_out())
+
+    say("binding: mismatched combine buffers")
+    d = epx.dispatch(x, tk, w, E, R, layout=lay)
+    y = synth.expert_outputs(d.recv_x.shape[0], h, seed=3, device="cuda")
+    with pytest.raises(ValueError):
+        epx.combine(y, d.pos_exp, w, out=torch.empty((T - 1, h), dtype=torch.bfloat16,
+                                                     device=dev))
+    with pytest.raises(ValueError):
+        epx.combine(y, d.pos_exp, w[:, :K - 1].contiguous())
+    with pytest.raises(ValueError):
+        epx.combine_partial(y, d, out=torch.empty((d.send_x.shape[0] - 1, h),
+                                                  dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        epx.combine_final(torch.empty((d.send_x.shape[0], h), dtype=torch.bfloat16, device=dev),
+                          lay, out=torch.empty((T, h + 8), dtype=torch.bfloat16, device=dev))
+
+    say("binding: low-latency buffer of another capacity")
+    buf = epx.alloc_ll(E, 1, T + 1, h, T, K, True, dev)
+    with pytest.raises(ValueError):
+        epx.ll_dispatch(x, tk, E, R, 0, T, 1, True, buf)
+    assert epx.get_error() == 0
+
+
 def test_ll_ping_pong_and_fill_stats():
     """Four decode steps over a ping-pong pair: each step dispatches into one
     buffer and resets the other's counts in the same launch (garbage written
