@@ -211,7 +211,12 @@ int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
  * (max(ceil(T/256) + 1, ceil(T/8)) blocks of 512 threads) covers every
  * compute unit and fits on the device at once (at h = 7168 and 256 units:
  * 2048 <= T <= 4096); else the layout and the dispatch are launched one
- * after the other (epx_fused_launches says which; T = 0 is one launch). */
+ * after the other (epx_fused_launches says which; T = 0 is one launch).
+ * In the tiled one-launch form the first ceil(T/256) + 1 blocks wait for
+ * one another's totals, so they must get compute units together: work on
+ * other streams that holds the device for longer than the bounded wait (a
+ * fraction of a second) makes the call set EPX_DEV_WORKSPACE instead of
+ * hanging, and its outputs are then not valid. */
 int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
                        const float *topk_w, int T, int K, int E, int R, int C,
                        int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,
