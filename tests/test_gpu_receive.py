@@ -110,3 +110,57 @@ def test_low_latency_buffer_filled_by_every_source():
         p = o["pos_ll"]
         full = np.where(p >= 0, ((p // cap) * R + s) * cap + p % cap, -1)
         _eq(pos[s], full, f"source {s} handle")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_two_level_dedup_node_then_rank(fp8):
+    """Two-level dedup on the GPU: the pack at node granularity (R = N
+    logical nodes, one row per (token, node)), then inside every node the
+    pack of the node's received rows over its R/N ranks, using the
+    node-local indices and weights the first pack wrote (FP8 codes move as
+    bit patterns, their scales travel with the source row). Every rank must
+    receive exactly the oracle's one-level rank-major rows, in order."""
+    import combine_get_dispatch_counts_amd as epx
+
+    T, h, E, R, N, K = 512, 1024, 64, 8, 2, 6
+    L_node, per_node = E // N, R // N
+    rng = np.random.default_rng(55)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=56, p_drop=0.05)
+    w = rng.random((T, K)).astype(np.float32)
+    say(f"two-level dedup T={T} h={h} E={E} R={R} nodes={N} K={K} fp8={fp8}")
+
+    tk = torch.from_numpy(topk).cuda()
+    lay1 = epx.get_dispatch_layout(tk, E, N)
+    d1 = epx.dispatch(dev_bf16(x), tk, torch.from_numpy(w).cuda(), E, N, fp8=fp8, layout=lay1)
+    assert epx.get_error() == 0
+    o = oracle.dispatch(x, topk, w, E, R, fp8=fp8)
+    ro = o["layout"]["rank_off"]
+    assert int(lay1.totals[0]) < int(o["layout"]["totals"][0]), "no token shared a node"
+    ro1 = lay1.rank_off.cpu().numpy()
+    ngrp = h // 128
+    for n in range(N):
+        a, b = int(ro1[n]), int(ro1[n + 1])
+        rows = d1.send_x[a:b]
+        if fp8:
+            rows = rows.view(torch.bfloat16)  # codes as bit patterns, h/2 wide
+        idx, wn = d1.send_topk_idx[a:b], d1.send_topk_w[a:b]
+        lay2 = epx.get_dispatch_layout(idx, L_node, per_node)
+        d2 = epx.dispatch(rows, idx, wn, L_node, per_node, layout=lay2)
+        assert epx.get_error() == 0
+        ro2 = lay2.rank_off.cpu().numpy()
+        src1 = host_bits(d1.send_src)[a:b]
+        for g in range(per_node):
+            r = n * per_node + g
+            a2, b2 = int(ro2[g]), int(ro2[g + 1])
+            fa, fb = int(ro[r]), int(ro[r + 1])
+            sel = host_bits(d2.send_src)[a2:b2]
+            _eq(src1[sel], o["send_src"][fa:fb], f"rank {r} sources")
+            got = host_bits(d2.send_x)[a2:b2]
+            if fp8:
+                got = np.ascontiguousarray(got).view(np.uint8)
+                _eq(host_bits(d1.send_scales)[a:b][sel, :ngrp], o["send_scales"][fa:fb],
+                    f"rank {r} scales")
+            _eq(got, o["send_x"][fa:fb], f"rank {r} rows")
+            _eq(host_bits(d2.send_topk_idx)[a2:b2], o["send_topk_idx"][fa:fb], f"rank {r} indices")
+            _eq(host_bits(d2.send_topk_w)[a2:b2], o["send_topk_w"][fa:fb], f"rank {r} weights")

@@ -104,3 +104,65 @@ def test_capacity_and_shape_errors(orc):
     with pytest.raises(orc.OracleError) as ei:
         orc.dispatch(x_odd, inp["topk_idx"], inp["topk_w"], wl.E, wl.R, fp8=True)
     assert ei.value.code == orc.EUNSUPPORTED
+
+
+def _two_level(orc, x, topk, w, E, R, N, fp8):
+    """Node-level pack (R = N: one row per (token, node)), then inside each
+    node the pack of that node's received rows over its R/N ranks, with the
+    node-local expert indices the first level wrote. Returns, per rank, the
+    rows, source tokens, rank-local indices, weights (and FP8 scales)."""
+    L_node = E // N
+    d1 = orc.dispatch(x, topk, w, E, N, fp8=fp8)
+    ro1 = d1["layout"]["rank_off"]
+    per_rank = {}
+    for n in range(N):
+        a, b = int(ro1[n]), int(ro1[n + 1])
+        rows = d1["send_x"][a:b]
+        if fp8:  # codes travel as bit patterns, two per 16-bit element
+            rows = np.ascontiguousarray(rows).view(np.uint16)
+        d2 = orc.dispatch(rows, d1["send_topk_idx"][a:b], d1["send_topk_w"][a:b], L_node,
+                          R // N)
+        ro2 = d2["layout"]["rank_off"]
+        for g in range(R // N):
+            a2, b2 = int(ro2[g]), int(ro2[g + 1])
+            sel = d2["send_src"][a2:b2]
+            out = dict(x=d2["send_x"][a2:b2], src=d1["send_src"][a:b][sel],
+                       idx=d2["send_topk_idx"][a2:b2], w=d2["send_topk_w"][a2:b2])
+            if fp8:
+                out["x"] = np.ascontiguousarray(out["x"]).view(np.uint8)
+                out["scales"] = d1["send_scales"][a:b][sel]
+            per_rank[n * (R // N) + g] = out
+    return per_rank
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_two_level_pack_equals_rank_level_pack(orc, fp8):
+    """Two-level dedup (the DeepEP study notes' hybrid section: one copy per
+    node, then one per GPU inside the node) delivers to every rank exactly
+    the rows of the one-level rank-deduplicated pack, in the same order, with
+    the same rank-local top-k indices and weights: node n's rank g is rank
+    n*(R/N) + g, and a node-local index minus g*L is the rank-local one."""
+    T, h, E, R, N, K = 200, 256, 32, 8, 2, 4
+    rng = np.random.default_rng(11)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=12, p_drop=0.1)
+    w = rng.random((T, K)).astype(np.float32)
+    flat = orc.dispatch(x, topk, w, E, R, fp8=fp8)
+    ro = flat["layout"]["rank_off"]
+    two = _two_level(orc, x, topk, w, E, R, N, fp8)
+    for r in range(R):
+        a, b = int(ro[r]), int(ro[r + 1])
+        got = two[r]
+        np.testing.assert_array_equal(got["src"], flat["send_src"][a:b], err_msg=f"rank {r} src")
+        np.testing.assert_array_equal(got["x"], flat["send_x"][a:b], err_msg=f"rank {r} rows")
+        np.testing.assert_array_equal(got["idx"], flat["send_topk_idx"][a:b],
+                                      err_msg=f"rank {r} indices")
+        np.testing.assert_array_equal(got["w"], flat["send_topk_w"][a:b],
+                                      err_msg=f"rank {r} weights")
+        if fp8:
+            np.testing.assert_array_equal(got["scales"], flat["send_scales"][a:b],
+                                          err_msg=f"rank {r} scales")
+    # the node level moves fewer rows than the rank level whenever a token
+    # has two ranks in one node
+    n1 = int(orc.layout(topk, E, N)["totals"][0])
+    assert n1 < int(flat["layout"]["totals"][0])
