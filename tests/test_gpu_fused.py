@@ -202,14 +202,21 @@ def test_fused_shares_workspace_with_layout():
             _eq(host_bits(getattr(lay, k)), ol[k], f"layout call {i} {k}")
 
 
-def test_fused_step_in_graph():
+@pytest.mark.parametrize("T", [256, 1536, 2048])
+def test_fused_step_in_graph(T):
+    """A captured fused step (layout + dispatch, then combine) replayed three
+    times equals the eager step bit for bit: the small-batch kernel (T =
+    256), the two launches (T = 1536 at h = 4096: the tiled grid would not
+    cover the device) and the tiled kernel (T = 2048)."""
     import combine_get_dispatch_counts_amd as epx
 
-    inp = synth.make_inputs(4, T=2048)
+    inp = synth.make_inputs(4, T=T)
     wl = inp["workload"]
-    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
-    assert epx.fused_launches(T, h, K, E, R) == 1
-    say(f"fused step in a graph T={T}")
+    h, E, R, K = wl.h, wl.E, wl.R, wl.K
+    launches = epx.fused_launches(T, h, K, E, R)
+    if T != 1536:
+        assert launches == 1
+    say(f"fused step in a graph T={T} ({launches} launch(es))")
     dev = torch.device("cuda")
     x, tk, w = dev_bf16(inp["x"]), torch.from_numpy(inp["topk_idx"]).cuda(), \
         torch.from_numpy(inp["topk_w"]).cuda()
@@ -226,6 +233,13 @@ def test_fused_step_in_graph():
     step()
     torch.cuda.synchronize()
     ref = [out.clone(), bufs["recv_x"].clone(), lay.pos_in_rank.clone()]
+    if T == 256:  # the eager step itself against the oracle (larger T: other tests)
+        o = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], E, R)
+        n_recv = int(o["layout"]["totals"][1])
+        _eq(host_bits(ref[1])[:n_recv], o["recv_x"], "eager recv_x")
+        _eq(host_bits(ref[2]), o["layout"]["pos_in_rank"], "eager pos_in_rank")
+        _eq(host_bits(ref[0]), oracle.combine(host_bits(y), inp["topk_w"],
+                                              o["pos_exp"]), "eager combine")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
