@@ -137,6 +137,7 @@ def _check_dispatch(x, topk, w, E, R, fp8, worst_case=False, guard=0):
     (1, 8, 256, 32, 7168, False, 0.0), (63, 2, 8, 4, 128, False, 0.0),
     (65, 6, 64, 8, 4096, True, 0.0), (257, 8, 256, 64, 256, True, 0.2),
     (200, 4, 16, 1, 1024, False, 0.1), (130, 8, 128, 32, 7168, True, 0.0),
+    (300, 32, 512, 64, 256, True, 0.1), (600, 32, 512, 64, 1024, False, 0.0),
     (96, 3, 24, 4, 136, False, 0.0), (0, 4, 16, 4, 128, True, 0.0),
 ])
 def test_dispatch_edge_cases(T, K, E, R, h, fp8, p_drop):
