@@ -391,6 +391,26 @@ def test_ll_dispatch_row_slices(h, fp8, K):
         _check_ll_scales(host_bits(buf.ll_scales), o["ll_scales"], o["ll_src"], "ll_scales")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_ll_dispatch_largest_shapes(fp8):
+    """The low-latency kernel at the largest supported routing shape: E =
+    512 experts, R = 64 ranks (the last source rank), K = 32 entries per
+    token, every region's count and row against the oracle."""
+    T, h, E, R, K, src, cap = 100, 256, 512, 64, 32, 63, 100
+    rng = np.random.default_rng(64)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=65, p_drop=0.1)
+    say(f"ll_dispatch T={T} h={h} E={E} R={R} K={K} src={src} fp8={fp8}")
+    buf = _ll_gpu(x, topk, E, R, src, cap, 1, fp8)
+    o = oracle.ll_dispatch(x, topk, E, R, src, cap, 1, fp8=fp8)
+    _eq(host_bits(buf.pos_ll), o["pos_ll"], "pos_ll")
+    _eq(host_bits(buf.ll_count), o["ll_count"], "ll_count")
+    _eq(host_bits(buf.ll_src), o["ll_src"], "ll_src")
+    _eq(host_bits(buf.ll_x), o["ll_x"], "ll_x")
+    if fp8:
+        _check_ll_scales(host_bits(buf.ll_scales), o["ll_scales"], o["ll_src"], "ll_scales")
+
+
 def test_ll_dispatch_decode_full_buffer():
     """Decode workload at full size: T=128, E=256, R=32, cap=128, FP8, the
     full logical buffer of all 32 destinations (1,048,576 rows, 7.75 GB).
