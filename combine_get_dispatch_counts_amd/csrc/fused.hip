@@ -31,8 +31,8 @@
 // chip together; and the dispatch work is all in flight at once only while
 // the whole grid is: a block keeps its place until its slowest wave ends,
 // so later rounds of blocks would each start behind a tail (a loop over
-// several tokens per wave instead costs registers: 175 rather than 124 at
-// h = 7168, half the waves). With fewer blocks than compute units, on the
+// several tokens per wave instead raised the register count at h = 7168 far
+// enough to halve the resident waves). With fewer blocks than compute units, on the
 // other hand, a token's eight waves share one unit's store path while other
 // units idle. The host therefore launches this kernel when its grid covers
 // every compute unit and, by the occupancy query, fits on the chip at once;
