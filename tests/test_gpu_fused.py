@@ -56,6 +56,9 @@ def _fused_check(x, topk, w, E, R, fp8, C=None, ws=None):
         ngrp = h // 128
         _eq(host_bits(d.send_scales)[:n_send, :ngrp], o["send_scales"], "send_scales")
         _eq(host_bits(d.recv_scales)[:n_recv, :ngrp], o["recv_scales"], "recv_scales")
+        for k, n in (("send_scales", n_send), ("recv_scales", n_recv)):
+            pad = host_bits(getattr(d, k))[:n, ngrp:]
+            assert (pad.view(np.uint32) == 0).all(), f"{k} padding is not +0"
     return d
 
 
@@ -76,7 +79,8 @@ def test_fused_workloads_full_size(cfg):
     (513, 4, 128, 8, 512, False, "uniform"), (400, 6, 96, 12, 256, True, "dropped"),
     (999, 8, 96, 48, 128, False, "uniform"), (77, 3, 96, 6, 128, False, "repeats"),
     (130, 8, 256, 32, 7168, True, "dropped"), (600, 32, 512, 64, 256, True, "dropped"),
-    (1500, 32, 512, 64, 128, False, "uniform"),
+    (1500, 32, 512, 64, 128, False, "uniform"), (70, 8, 64, 8, 16384, True, "uniform"),
+    (2100, 8, 64, 8, 9216, False, "dropped"), (90, 6, 64, 8, 8200, False, "uniform"),
 ])
 def test_fused_edge_cases(T, K, E, R, h, fp8, kind):
     say(f"fused T={T} K={K} E={E} R={R} h={h} fp8={fp8} {kind}")
@@ -145,7 +149,8 @@ def test_fused_one_and_two_launches(fp8, edge):
     (4, 16, 4, 128, False, "repeats"), (6, 64, 8, 4096, True, "uniform"),
     (8, 128, 32, 512, False, "uniform"), (2, 8, 1, 128, True, "dropped"),
     (6, 96, 12, 256, False, "dropped"), (8, 96, 48, 128, True, "uniform"),
-    (32, 512, 64, 128, False, "uniform"),
+    (32, 512, 64, 128, False, "uniform"), (8, 64, 8, 9216, True, "dropped"),
+    (8, 64, 8, 16384, False, "uniform"),
 ])
 def test_fused_kernel_edge_cases(K, E, R, h, fp8, kind):
     """The one-launch kernel itself on edge shapes: T inside its window,

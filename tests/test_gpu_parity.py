@@ -138,6 +138,10 @@ def _check_dispatch(x, topk, w, E, R, fp8, worst_case=False, guard=0):
     (65, 6, 64, 8, 4096, True, 0.0), (257, 8, 256, 64, 256, True, 0.2),
     (200, 4, 16, 1, 1024, False, 0.1), (130, 8, 128, 32, 7168, True, 0.0),
     (300, 32, 512, 64, 256, True, 0.1), (600, 32, 512, 64, 1024, False, 0.0),
+    # rows longer than one register pass: two full passes, partial second passes
+    (40, 8, 64, 8, 16384, True, 0.1), (40, 8, 64, 8, 16384, False, 0.1),
+    (33, 6, 64, 8, 9216, False, 0.0), (45, 8, 64, 8, 9216, True, 0.0),
+    (50, 4, 32, 4, 8200, False, 0.0),
     (96, 3, 24, 4, 136, False, 0.0), (0, 4, 16, 4, 128, True, 0.0),
 ])
 def test_dispatch_edge_cases(T, K, E, R, h, fp8, p_drop):
@@ -280,7 +284,8 @@ def test_combine_workloads(cfg):
 
 def test_combine_edge_cases():
     rng = np.random.default_rng(12)
-    for T, K, h, n in [(1, 1, 8, 1), (37, 8, 7168, 300), (64, 32, 256, 2000), (5, 3, 64, 0)]:
+    for T, K, h, n in [(1, 1, 8, 1), (37, 8, 7168, 300), (64, 32, 256, 2000), (5, 3, 64, 0),
+                       (21, 8, 16384, 100), (9, 4, 8200, 30)]:
         say(f"combine T={T} K={K} h={h} rows={n}")
         y = synth.expert_outputs(max(n, 1), h, seed=T, device="cuda")[:n]
         pos = rng.integers(-1, max(n, 1), (T, K)).astype(np.int32) if n else np.full((T, K), -1, np.int32)
