@@ -333,14 +333,8 @@ int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *to
                        pos_exp, f.disp);
     if (rc != EPX_OK)
         return rc;
-    const size_t need = epx::fused_workspace_bytes(T, K, E, R);
-    if (ws_bytes < need)
+    if (ws_bytes < epx::fused_workspace_bytes(T, K, E, R))
         return EPX_ECAPACITY;
-    if (need > 0) {
-        char *base = static_cast<char *>(ws) + epx::layout_workspace_bytes(T, E, R);
-        f.tot = reinterpret_cast<uint64_t *>(base);
-        f.tok = f.tot + (E + R);
-    }
     f.cus = ctx->cus;
     return launched(epx::launch_fused(f, fp8 != 0, stream));
 }

@@ -91,14 +91,11 @@ struct LLArgs {
 hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream);
 
 // Layout and dispatch in one launch: the layout's arguments (workspace head
-// and tile words included), the dispatch's (its layout pointers unused),
-// and the two extra parts of the workspace the dispatch blocks read.
+// and tile words included) and the dispatch's (its layout pointers unused).
 struct FusedArgs {
     LayoutArgs lay;
     DispatchArgs disp;
-    uint64_t *tot;   // [E + R] tagged totals
-    uint64_t *tok;   // [T, R + K] tagged final positions, then slots
-    int cus;         // compute units of the device
+    int cus;  // compute units of the device
 };
 
 size_t fused_workspace_bytes(int T, int K, int E, int R);

@@ -3,20 +3,24 @@
 //
 // [P2] "DeepEP v2": the v2 dispatch kernel computes the layout itself (its
 // notify warps take the place of get_dispatch_layout) while its dispatch
-// warps move the data, in one launch. Here the first blocks of the grid are
-// the layout's blocks (layout_device.h: one per 256-token tile, then the
-// totals block), and every block of kLayoutThreads threads then dispatches
-// one token per wave (dispatch_device.h), so the grid is no larger than
-// the dispatch alone needs.
+// warps move the data, in one launch. Here every block of kLayoutThreads
+// threads owns kFusedTokens consecutive tokens (one per wave) and works out
+// their layout rows itself, so the grid is the size the dispatch alone needs.
 //
-// Hand-over. The layout blocks publish, beside their usual outputs, the
-// totals and each token's final in-rank positions and in-expert slots as
-// self-contained words (tag << 32 | value, the scheme of the tiles'
-// look-back), so no ordering between different addresses is relied on, and
-// words left in the workspace by earlier calls, of any shape, carry older
-// tags. A block, once the totals are out, scans them into the rank and
-// expert offsets in LDS; each of its waves then waits for its token's
-// R + K words and moves the row.
+// One hand-over. A token's in-rank position (in-expert slot) is the count of
+// earlier tokens (entries) of the same rank (expert): the sum over the
+// 256-token tiles before its own, plus the count inside its tile before it.
+// The first ntiles blocks each count one whole tile in LDS and publish its
+// E + R counts as self-contained words (tag << 32 | value), before they wait
+// for anything; every block then reads all tiles' words -- their sum is the
+// totals, from which it scans the offsets, and the tiles before its own give
+// its prefix -- while it counts its own tile's tokens before its first token
+// in LDS, and the entries of its earlier tokens from the rows its waves
+// hold. No ordering between different addresses is relied on, and words
+// left in the workspace by earlier calls, of any shape, carry older tags.
+// Blocks write their own tokens' rows of is_token_in_rank, pos_in_rank and
+// slot_in_expert, and the channel_prefix columns whose channel ends in their
+// tokens; block 0 writes the counts, offsets and totals.
 //
 // The call's tag. No block takes an arrival on the call counter (one
 // word: every block of the grid hitting it at once would serialise for
@@ -26,22 +30,21 @@
 // block reads it with one plain load, checking on the way that no layout
 // call was left unfinished (arrivals 0).
 //
-// When it is used. The layout blocks, once their layout part is done, wait
-// for the totals block like the others, so all layout blocks must be on the
-// chip together; and the dispatch work is all in flight at once only while
-// the whole grid is: a block keeps its place until its slowest wave ends,
-// so later rounds of blocks would each start behind a tail (a loop over
-// several tokens per wave instead raised the register count at h = 7168 far
-// enough to halve the resident waves). With fewer blocks than compute units, on the
-// other hand, a token's eight waves share one unit's store path while other
-// units idle. The host therefore launches this kernel when its grid covers
-// every compute unit and, by the occupancy query, fits on the chip at once;
-// small batches go to fused_small_kernel below, and everything else runs
-// the layout and the dispatch as two launches, whose 64-thread dispatch
-// blocks spread one wave per token over the chip and free their place wave
-// by wave. Layout blocks come first in the grid;
-// dispatch-only blocks issue their row loads before waiting, so the loads
-// overlap the layout. Every wait is bounded.
+// When it is used. Every block waits for the first ntiles blocks, which
+// wait for nothing before they publish; and the dispatch work is all in
+// flight at once only while the whole grid is: a block keeps its place until
+// its slowest wave ends, so later rounds of blocks would each start behind a
+// tail (a loop over several tokens per wave instead raised the register
+// count at h = 7168 far enough to halve the resident waves). With fewer
+// blocks than compute units, on the other hand, a token's eight waves share
+// one unit's store path while other units idle. The host therefore launches
+// this kernel when its grid covers every compute unit and, by the occupancy
+// query, fits on the chip at once; small batches go to fused_small_kernel
+// below, and everything else runs the layout and the dispatch as two
+// launches, whose 64-thread dispatch blocks spread one wave per token over
+// the chip and free their place wave by wave. Every block issues its
+// counting loads, then its rows' loads, before it waits, so the loads
+// overlap the hand-over. Every wait is bounded.
 #include <atomic>
 
 #include "dispatch_device.h"
@@ -52,107 +55,219 @@ namespace {
 
 constexpr int kFusedTokens = kLayoutThreads / kWave;  // tokens per block
 
-// Wait until the word each needing lane reads carries the call's tag
-// (bounded; false on time-out). Wave-uniform loop.
-__device__ bool wait_tagged(const uint64_t *p, bool need, uint32_t tag, uint64_t &w)
+// LDS of fused_kernel: the rank bits and entries of the block's tokens,
+// then per expert and rank (E + R ints each): the counts over the block's
+// tile before its first token, the tile it publishes, the totals, the counts
+// over the earlier tiles, and the offsets (E + R + 2).
+__host__ __device__ inline size_t fused_lds_bytes(int E, int R, int kmax)
 {
-    int polls = 0;
-    w = need ? pub_load(p) : 0;
-    while (__any(need && (uint32_t)(w >> 32) != tag)) {
-        if (++polls > kSpinLimit)
-            return false;
-        __builtin_amdgcn_s_sleep(2);
-        if (need && (uint32_t)(w >> 32) != tag)
-            w = pub_load(p);
-    }
-    return true;
+    return sizeof(uint64_t) * kFusedTokens + sizeof(int) * (size_t)kFusedTokens * kmax +
+           sizeof(int) * (5 * (size_t)(E + R) + 2);
 }
 
 template <int KMAX, bool FP8, int NV>
 __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    const LayoutArgs &l = f.lay;
     const DispatchArgs &a = f.disp;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
-    const int t = blockIdx.x * kFusedTokens + w;
-    const bool have = t < a.T;
-    const int ER = a.E + a.R;
-    int *tot = reinterpret_cast<int *>(lds + count_lds_bytes(a.E, a.R));
-    int *off = tot + ER;  // [E+1] expert offsets, then [R+1] rank offsets
+    const int E = a.E, R = a.R, K = a.K, T = a.T, ER = E + R;
+    uint64_t *tmask = reinterpret_cast<uint64_t *>(lds);                // [kFusedTokens]
+    int *tent = reinterpret_cast<int *>(tmask + kFusedTokens);          // [kFusedTokens][KMAX]
+    int *bef = tent + kFusedTokens * KMAX;  // [E + R] the tile's tokens before t0
+    int *agg = bef + ER;                    // [E + R] the tile this block publishes
+    int *tot = agg + ER;                    // [E + R] all tiles
+    int *pre = tot + ER;                    // [E + R] the tiles before this block's
+    int *off = pre + ER;                    // [E + 1] expert offsets, [R + 1] rank offsets
+    __shared__ int s_go;
+    __shared__ uint32_t s_tag;
 
-    bool go = true;  // block-uniform: false once the layout part was refused
-    uint32_t tag;
+    if (l.ntiles == 0) {  // T = 0: one block, zero counts and offsets, no counters
+        for (int i = tid; i < ER; i += blockDim.x)
+            tot[i] = 0;
+        __syncthreads();
+        write_totals(l, tot, off);
+        if (l.channel_prefix)
+            for (int i = tid; i < R * l.C; i += blockDim.x)
+                l.channel_prefix[i] = 0;
+        return;
+    }
+
+    const int t0 = blockIdx.x * kFusedTokens;
+    const int tile = t0 / kLayoutTile, tile_base = tile * kLayoutTile;
+    const int t = t0 + w;
+    const bool have = t < T;
+    const bool publisher = (int)blockIdx.x < l.ntiles;
+
+    // Loads first, the counting entries ahead of the row: the call number;
+    // threads below kLayoutTile take the tokens of the block's own tile
+    // before t0, the others (publishers only) the tokens of tile blockIdx;
+    // lane k < K the token's entry k; then the token's row.
+    if (tid == 0) {
+        const unsigned long long v =
+            __hip_atomic_load(&l.hdr->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_tag = (uint32_t)(v >> 32) + 1u;
+        s_go = (uint32_t)v == 0u;  // no layout call was left unfinished
+    }
+    const bool pub_thread = tid >= kLayoutTile;
+    const int u = pub_thread ? (int)blockIdx.x * kLayoutTile + (tid - kLayoutTile)
+                             : tile_base + tid;
+    const bool counting = pub_thread ? (publisher && u < T) : u < t0;
+    int eu[KMAX];
+    if (counting) {
+        load_row_experts<KMAX>(l, u, eu);
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            eu[k] = -1;
+    }
+    const int64_t e = (have && lane < K) ? a.topk_idx[(int64_t)t * K + lane] : -1;
     typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
     const uint16_t *xrow = a.x + (size_t)(have ? t : 0) * a.h;
-    if ((int)blockIdx.x <= f.lay.ntiles) {  // a layout block (or T = 0)
-        go = layout_block<KMAX>(f.lay, lds, f.tok, f.tot, false, tag);  // flags if refused
-        if (f.lay.ntiles == 0)  // T = 0: one block, no counters involved
-            return;
-        __syncthreads();  // the layout's LDS is reused below
-        if (go && have)
-            row.load(reinterpret_cast<const u32x4 *>(xrow), 0, FP8 ? a.h >> 4 : a.h >> 3);
-    } else {
-        if (have)
-            row.load(reinterpret_cast<const u32x4 *>(xrow), 0, FP8 ? a.h >> 4 : a.h >> 3);
-        __shared__ int s_go;
-        const unsigned long long v =
-            __hip_atomic_load(&f.lay.hdr->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        tag = (uint32_t)(v >> 32) + 1u;
-        if (tid == 0) {
-            s_go = (uint32_t)v == 0u;
-            if (!s_go)
-                flag_error(a.err, EPX_DEV_WORKSPACE);
-        }
-        __syncthreads();
-        go = s_go;
-    }
-    const int64_t e = (have && lane < a.K) ? a.topk_idx[(int64_t)t * a.K + lane] : -1;
+    if (have)
+        row.load(reinterpret_cast<const u32x4 *>(xrow), 0, FP8 ? a.h >> 4 : a.h >> 3);
 
-    if (go) {
-        // the totals, 64 words per wave, then the offsets scanned into LDS
-        for (int c0 = w * kWave; c0 < ER; c0 += kFusedTokens * kWave) {
-            const int c = c0 + lane;
-            uint64_t word;
-            if (!wait_tagged(f.tot + min(c, ER - 1), c < ER, tag, word) && lane == 0)
-                flag_error(a.err, EPX_DEV_WORKSPACE);
-            if (c < ER)
-                tot[c] = (int)((uint32_t)word & 0x7FFFFFFFu);
+    // the token's rank bits and entries, for the tokens after it in the block
+    const bool valid = lane < K && e >= 0 && e < E;
+    const uint64_t mt = uniform64(wave_or(valid ? 1ull << ((int)e / l.L) : 0ull));
+    if (lane == 0)
+        tmask[w] = have ? mt : 0ull;
+    if (lane < K)
+        tent[w * KMAX + lane] = valid ? (int)e : -1;
+    for (int i = tid; i < 2 * ER; i += blockDim.x)
+        bef[i] = 0;  // bef and agg
+    __syncthreads();
+
+    // counts: per expert every valid entry, per rank every token once
+    {
+        int *cnt = pub_thread ? agg : bef;
+        uint64_t m = 0;
+        int bad = 0;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int ek = eu[k];
+            bad |= (ek == -2);
+            if (ek < 0)
+                continue;
+            atomicAdd(&cnt[ek], 1);
+            m |= 1ull << (ek / l.L);
         }
-        __syncthreads();
-        if (tid < kWave)
-            wave_exclusive_scan(tot, a.E, off);
-        else if (tid < 2 * kWave)
-            wave_exclusive_scan(tot + a.E, a.R, off + a.E + 1);
-        __syncthreads();
+        for (; m; m &= m - 1)
+            atomicAdd(&cnt[E + __builtin_ctzll(m)], 1);
+        if (bad && pub_thread)
+            flag_error(a.err, EPX_DEV_BAD_ROUTE);
     }
-    if (go && have) {
-        // the token's final positions (lane r < R) and slots (lane k < K)
-        const uint64_t *tw = f.tok + (int64_t)t * (a.R + a.K);
-        uint64_t pw, sw;
-        const bool ok_p = wait_tagged(tw + min(lane, a.R - 1), lane < a.R, tag, pw);
-        const bool ok_s = wait_tagged(tw + a.R + min(lane, a.K - 1), lane < a.K, tag, sw);
-        if (!(ok_p && ok_s) && lane == 0)
+    __syncthreads();
+    const uint32_t tag = s_tag;
+    bool go = s_go;
+    if (!go) {
+        if (tid == 0)
             flag_error(a.err, EPX_DEV_WORKSPACE);
-        int64_t send_r = -1, recv_r = -1;
-        if (ok_p && lane < a.R) {
-            const int p = (int)(uint32_t)pw;
-            if (p >= 0)
-                send_r = (int64_t)off[a.E + 1 + lane] + p;
+    } else if (publisher) {
+        uint64_t *prow = l.pub + (int64_t)blockIdx.x * ER;
+        for (int c = tid; c < ER; c += blockDim.x)
+            pub_store(prow + c, ((uint64_t)tag << 32) | (uint32_t)agg[c]);
+    }
+
+    // every tile's counts: the totals and this tile's prefix (bounded waits)
+    bool ok = true;
+    if (go) {
+        for (int c = tid; c < ER; c += blockDim.x) {
+            int all = 0, before = 0;
+            for (int j0 = 0; j0 < l.ntiles; j0 += 16) {
+                // 16 tiles' words in flight together, then each polled on
+                // its own until it carries the call's tag
+                const int nq = min(16, l.ntiles - j0);
+                const uint64_t *col = l.pub + (int64_t)j0 * ER + c;
+                uint64_t wv[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    wv[q] = q < nq ? pub_load(col + (int64_t)q * ER) : 0;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    if (q >= nq)
+                        break;
+                    for (int polls = 0; (uint32_t)(wv[q] >> 32) != tag && ok;) {
+                        if (++polls > kSpinLimit)
+                            ok = false;
+                        __builtin_amdgcn_s_sleep(2);
+                        wv[q] = pub_load(col + (int64_t)q * ER);
+                    }
+                    const int v = (int)(uint32_t)wv[q];
+                    all += v;
+                    before += j0 + q < tile ? v : 0;
+                }
+            }
+            tot[c] = all;
+            pre[c] = before;
         }
-        if (ok_s && e >= 0 && e < a.E) {
-            const int sl = (int)(uint32_t)sw;
-            recv_r = sl >= 0 ? (int64_t)off[(int)e] + sl : -1;
+    }
+    if (__syncthreads_or(!ok)) {
+        if (tid == 0)
+            flag_error(a.err, EPX_DEV_WORKSPACE);
+        go = false;
+    }
+    if (go) {
+        if (blockIdx.x == 0) {
+            write_totals(l, tot, off);  // scans into off, then the global outputs
+        } else {
+            if (tid < kWave)
+                wave_exclusive_scan(tot, E, off);
+            else if (tid < 2 * kWave)
+                wave_exclusive_scan(tot + E, R, off + E + 1);
         }
+    }
+    __syncthreads();
+
+    // channel_prefix columns whose last token is one of this block's
+    if (go && l.channel_prefix) {
+        const int tlast = min(t0 + kFusedTokens, T) - 1;
+        for (int c = tid; c < l.C; c += blockDim.x) {
+            const int end = (int)channel_end(l, c);
+            if (end - 1 < t0 || end - 1 > tlast)
+                continue;
+            for (int r = 0; r < R; ++r) {
+                int n = pre[E + r] + bef[E + r];
+                for (int w2 = 0; w2 < end - t0; ++w2)
+                    n += (int)((tmask[w2] >> r) & 1ull);
+                l.channel_prefix[(int64_t)r * l.C + c] = n;
+            }
+        }
+    }
+
+    if (go && have) {
+        // earlier tokens of the block: per rank lane, the tokens going to
+        // it; per entry lane, the entries with the same expert
+        int cr = 0, ce = 0, rep = 0;
+        for (int w2 = 0; w2 < w; ++w2) {
+            cr += (int)((tmask[w2] >> lane) & 1ull);
+            for (int k2 = 0; k2 < K; ++k2)
+                ce += (valid && tent[w2 * KMAX + k2] == (int)e);
+        }
+        for (int k2 = 0; k2 < K; ++k2)  // earlier entries of the token's own row
+            rep += (valid && k2 < lane && tent[w * KMAX + k2] == (int)e);
+        const bool in_r = lane < R && ((mt >> lane) & 1ull);
+        const int p = in_r ? pre[E + lane] + bef[E + lane] + cr : -1;
+        const int slot = valid ? pre[(int)e] + bef[(int)e] + ce + rep : -1;
+        const int64_t send_r = in_r ? (int64_t)off[E + 1 + lane] + p : -1;
+        const int64_t recv_r = valid ? (int64_t)off[(int)e] + slot : -1;
+        if (lane < R) {
+            l.is_token_in_rank[(int64_t)t * R + lane] = in_r ? 1 : 0;
+            l.pos_in_rank[(int64_t)t * R + lane] = p;
+        }
+        if (lane < K)
+            l.slot_in_expert[(int64_t)t * K + lane] = slot;
         dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r);
     }
 
     // this block is done: the last block of the grid opens the next call
     __syncthreads();
     if (tid == 0) {
-        const unsigned int n = atomicAdd(&f.lay.hdr->done, 1u);
+        const unsigned int n = atomicAdd(&l.hdr->done, 1u);
         if (n == gridDim.x - 1) {
-            __hip_atomic_store(&f.lay.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            atomicAdd(&f.lay.hdr->calls, 1ull << 32);
+            __hip_atomic_store(&l.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            atomicAdd(&l.hdr->calls, 1ull << 32);
         }
     }
 }
@@ -301,20 +416,18 @@ int fused_blocks_per_cu(size_t lds)
     return n;
 }
 
-// The grid: the layout's blocks, or the dispatch's one block per
-// kFusedTokens tokens if more (one block for T = 0).
+// The grid: one block per kFusedTokens tokens (one block for T = 0).
 int64_t fused_grid(const FusedArgs &f)
 {
     const int64_t disp_blocks = (f.disp.T + kFusedTokens - 1) / kFusedTokens;
-    const int64_t nlay = f.lay.ntiles + 1;
-    return f.lay.ntiles == 0 ? 1 : (disp_blocks > nlay ? disp_blocks : nlay);
+    return disp_blocks > 0 ? disp_blocks : 1;
 }
 
 // With launch false, only say how many launches the call takes (1 or 2).
 template <int KMAX, bool FP8, int NV>
 hipError_t launch_fused_k(const FusedArgs &f, hipStream_t stream, bool launch, int *launches)
 {
-    const size_t lds = layout_tok_lds_bytes(f.lay.E, f.lay.R, f.lay.K);
+    const size_t lds = fused_lds_bytes(f.lay.E, f.lay.R, KMAX);
     const int64_t blocks = fused_grid(f);
     const bool small = f.disp.T >= 1 && f.disp.T <= kSmallMaxT;
     const bool one = small || f.lay.ntiles == 0 ||
@@ -357,11 +470,8 @@ hipError_t launch_fused_kmax(const FusedArgs &f, bool fp8, hipStream_t stream, b
 
 size_t fused_workspace_bytes(int T, int K, int E, int R)
 {
-    const size_t base = layout_workspace_bytes(T, E, R);
-    if (base == 0)
-        return 0;
-    // the layout's, then the totals row, then the tokens' words
-    return base + (size_t)(E + R) * sizeof(uint64_t) + (size_t)T * (R + K) * sizeof(uint64_t);
+    (void)K;
+    return layout_workspace_bytes(T, E, R);  // the head and the tiles' words
 }
 
 hipError_t launch_fused(const FusedArgs &f, bool fp8, hipStream_t stream)

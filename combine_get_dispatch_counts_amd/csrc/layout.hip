@@ -9,8 +9,7 @@ template <int KMAX>
 __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    uint32_t tag;
-    layout_block<KMAX>(a, lds, nullptr, nullptr, true, tag);
+    layout_block<KMAX>(a, lds);
 }
 
 }  // namespace

@@ -81,13 +81,6 @@ __host__ __device__ inline size_t layout_lds_bytes(int E, int R)
     return count_lds_bytes(E, R) + sizeof(int) * (3 * (size_t)(E + R) + 2);
 }
 
-// With the per-token words published (the fused launch): the tile's slot
-// values staged after that.
-__host__ __device__ inline size_t layout_tok_lds_bytes(int E, int R, int K)
-{
-    return layout_lds_bytes(E, R) + sizeof(int) * (size_t)kLayoutTile * K;
-}
-
 // Published words: (tag << 32) | inclusive bit 31 | value (< 2^31). A word
 // from an earlier call carries an older tag and reads as "not yet".
 constexpr uint64_t kInclusive = 0x80000000ull;
@@ -313,28 +306,14 @@ __device__ void write_totals(const LayoutArgs &a, const int *tot, int *off)
 
 // The work of one layout block: the totals for T = 0, the totals block
 // (blockIdx == ntiles), or tile blockIdx. Every layout block of the launch
-// takes one arrival on the workspace counter (see the kernel's header
-// comment). tot_row, if not null, also receives the totals as tagged words
-// [E + R] (tag << 32 | inclusive bit | value), and tok each token's final
-// pos_in_rank and slot_in_expert values as tagged words [T][R + K]
-// (tag << 32 | value): published so blocks of the same launch can read them
-// without waiting for the launch to end. With tok, the block's LDS must
-// hold layout_tok_lds_bytes.
-// With arrive, the block takes an arrival on the call counter and the last
-// layout block to arrive opens the next call. Without (the fused kernel,
-// whose last block to finish opens it), the block reads the call number,
-// which stays fixed for the whole launch, and checks that no call was left
-// unfinished. Returns false when the workspace was not left ready
-// (flagged), else true with the call's tag in tag_out (T = 0 touches no
-// counter: tag_out is 0).
+// takes one arrival on the workspace counter and the last to arrive opens
+// the next call (see the header comment). A block that finds the workspace
+// not left ready flags EPX_DEV_WORKSPACE and stops.
 template <int KMAX>
-__device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uint64_t *tok,
-                                             uint64_t *tot_row, bool arrive, uint32_t &tag_out)
+__device__ __forceinline__ void layout_block(const LayoutArgs &a, char *lds)
 {
     const CountLds s = carve_count(lds, a.E, a.R);
     const int ER = a.E + a.R;
-    // the tile's slot values, staged for the word run (with tok only)
-    int *slot_lds = tok ? reinterpret_cast<int *>(lds + layout_lds_bytes(a.E, a.R)) : nullptr;
     int *agg = reinterpret_cast<int *>(lds + count_lds_bytes(a.E, a.R));
     int *pre = agg + ER, *off = pre + ER;
     __shared__ int s_ok;
@@ -349,8 +328,7 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
         if (a.channel_prefix)
             for (int i = tid; i < a.R * a.C; i += blockDim.x)
                 a.channel_prefix[i] = 0;
-        tag_out = 0;
-        return true;
+        return;
     }
 
     // Threads tid and tid + 256 both hold token tid of the tile: the first
@@ -367,19 +345,12 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
         load_row_experts<KMAX>(a, t, ek);
     if (tid == 0) {
         const uint32_t nblk = (uint32_t)a.ntiles + 1u;  // the layout blocks
-        if (arrive) {
-            const unsigned long long v = atomicAdd(&a.hdr->calls, 1ull);
-            const uint32_t arrived = (uint32_t)v;
-            s_ok = arrived < nblk;
-            s_tag = (uint32_t)(v >> 32) + 1u;
-            if (arrived == nblk - 1)  // all layout blocks are in: open the next call
-                atomicAdd(&a.hdr->calls, (1ull << 32) - (unsigned long long)nblk);
-        } else {
-            const unsigned long long v =
-                __hip_atomic_load(&a.hdr->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_ok = (uint32_t)v == 0u;
-            s_tag = (uint32_t)(v >> 32) + 1u;
-        }
+        const unsigned long long v = atomicAdd(&a.hdr->calls, 1ull);
+        const uint32_t arrived = (uint32_t)v;
+        s_ok = arrived < nblk;
+        s_tag = (uint32_t)(v >> 32) + 1u;
+        if (arrived == nblk - 1)  // all layout blocks are in: open the next call
+            atomicAdd(&a.hdr->calls, (1ull << 32) - (unsigned long long)nblk);
     }
 
     // The block after the last tile: the totals are the inclusive prefix
@@ -389,20 +360,17 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
         if (!s_ok) {
             if (tid == 0)
                 flag_error(a.err, EPX_DEV_WORKSPACE);
-            return false;
+            return;
         }
-        tag_out = s_tag;
         for (int c = tid; c < ER; c += blockDim.x) {
             int p = 0;
             if (!look_back(a.pub, ER, a.ntiles, a.ntiles - 1, c, s_tag, &p))
                 flag_error(a.err, EPX_DEV_WORKSPACE);
             agg[c] = p;
-            if (tot_row)
-                pub_store(tot_row + c, ((uint64_t)s_tag << 32) | kInclusive | (uint32_t)p);
         }
         __syncthreads();
         write_totals(a, agg, off);
-        return true;
+        return;
     }
     for (int i = tid; i < W * a.E; i += blockDim.x) {
         s.emask[i] = 0;
@@ -441,11 +409,10 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
         s.dupwave[w] = 1;
     __syncthreads();
     const uint32_t tag = s_tag;
-    tag_out = tag;
     if (!s_ok) {  // the counter was not left by a previous call: give up
         if (tid == 0)
             flag_error(a.err, EPX_DEV_WORKSPACE);
-        return false;
+        return;
     }
 
     // wave prefixes inside the tile and the tile's counts, published at
@@ -497,12 +464,6 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
                        ? pre[e] + s.wpre_e[wt * a.E + e] + wave_rank(a, s, tile_base, tt0, k, e)
                        : -1;
         }
-        if (slot_lds) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (k >= k_lo && k < k_hi)
-                    slot_lds[tt0 * a.K + k] = v[k];
-        }
         if ((a.K & 3) == 0) {
 #pragma unroll
             for (int k0 = 0; k0 < KMAX; k0 += 4)
@@ -515,30 +476,6 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
             for (int k = 0; k < KMAX; ++k)
                 if (k >= k_lo && k < k_hi)
                     sie[k] = v[k];
-        }
-    }
-
-    // the tile's tokens' words, one contiguous run (consecutive lanes,
-    // consecutive words): positions recomputed from the bitmaps, then slots;
-    // published before the tile's own output rows, which only the caller reads
-    if (tok) {
-        __syncthreads();
-        const int RK = a.R + a.K;
-        uint64_t *dst = tok + (int64_t)tile_base * RK;
-        const uint64_t tagw = (uint64_t)tag << 32;
-        for (int i = tid; i < ntok * RK; i += blockDim.x) {
-            const int tt = i / RK, j = i - tt * RK;
-            int v;
-            if (j < a.R) {
-                const int ww = tt >> 6;
-                v = ((s.rb[tt] >> j) & 1ull) ? pre[a.E + j] + s.wpre_r[ww * a.R + j] +
-                                                   __popcll(s.rmask[ww * a.R + j] &
-                                                            lanes_below(tt & 63))
-                                             : -1;
-            } else {
-                v = slot_lds[tt * a.K + (j - a.R)];
-            }
-            pub_store(dst + i, tagw | (uint32_t)v);
         }
     }
 
@@ -630,7 +567,6 @@ __device__ __forceinline__ bool layout_block(const LayoutArgs &a, char *lds, uin
             a.channel_prefix[i] = v;
         }
     }
-    return true;
 }
 
 }  // namespace

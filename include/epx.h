@@ -186,9 +186,8 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
                  hipStream_t stream);
 
 /* Workspace bytes epx_dispatch_fused needs for (T, K, E, R) (host out): the
- * layout's workspace, then 8 bytes per expert and per rank and per (token,
- * rank or top-k entry). Zero-filled before its first use, like the
- * layout's. */
+ * same as the layout's (epx_workspace_size), whose head and per-tile words
+ * it uses. Zero-filled before its first use, like the layout's. */
 int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
 
 /* get_dispatch_layout and the high-throughput dispatch in one launch. [P2]
@@ -207,16 +206,15 @@ int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes);
  * capacities must be known up front (no host wait happens): T*min(K,R) send
  * rows and T*K receive rows always suffice. One launch for T <= 1024
  * (every block then computes the whole batch's layout itself and leaves the
- * workspace untouched), and for larger T while the tiled grid
- * (max(ceil(T/256) + 1, ceil(T/8)) blocks of 512 threads) covers every
- * compute unit and fits on the device at once (at h = 7168 and 256 units:
- * 2048 <= T <= 4096); else the layout and the dispatch are launched one
- * after the other (epx_fused_launches says which; T = 0 is one launch).
- * In the tiled one-launch form the first ceil(T/256) + 1 blocks wait for
- * one another's totals, so they must get compute units together: work on
- * other streams that holds the device for longer than the bounded wait (a
- * fraction of a second) makes the call set EPX_DEV_WORKSPACE instead of
- * hanging, and its outputs are then not valid. */
+ * workspace untouched), and for larger T while the tiled grid (ceil(T/8)
+ * blocks of 512 threads) covers every compute unit and fits on the device
+ * at once (at h = 7168 and 256 units: 2048 <= T <= 4096); else the layout
+ * and the dispatch are launched one after the other (epx_fused_launches says
+ * which; T = 0 is one launch). In the tiled one-launch form every block
+ * waits for the per-tile counts that the first ceil(T/256) blocks publish:
+ * work on other streams that holds the device for longer than the bounded
+ * wait (a fraction of a second) makes the call set EPX_DEV_WORKSPACE
+ * instead of hanging, and its outputs are then not valid. */
 int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx,
                        const float *topk_w, int T, int K, int E, int R, int C,
                        int32_t *num_tokens_per_expert, int32_t *num_tokens_per_rank,

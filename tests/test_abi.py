@@ -117,8 +117,11 @@ def test_fused_launches_rejects(lib):
 def test_fused_workspace_size(lib):
     n = ctypes.c_size_t()
     assert lib.epx_fused_workspace_size(4096, 8, 256, 32, ctypes.byref(n)) == 0
-    # the layout's workspace, the totals row, the tokens' words
-    assert n.value == (128 + 16 * 288 * 8) + 288 * 8 + 4096 * (32 + 8) * 8
+    # the layout's workspace: a 128-byte head and one 8-byte word per (tile, expert or rank)
+    assert n.value == 128 + 16 * 288 * 8
+    m = ctypes.c_size_t()
+    assert lib.epx_workspace_size(4096, 8, 256, 32, ctypes.byref(m)) == 0
+    assert m.value == n.value
     assert lib.epx_fused_workspace_size(0, 8, 256, 32, ctypes.byref(n)) == 0
     assert n.value == 0
     assert lib.epx_fused_workspace_size(10, 8, 256, 30, ctypes.byref(n)) == -1
