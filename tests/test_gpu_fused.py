@@ -172,6 +172,27 @@ def test_fused_kernel_edge_cases(K, E, R, h, fp8, kind):
     _fused_check(x, topk, w, E, R, fp8, C=5)
 
 
+@pytest.mark.parametrize("C_kind", ["dense", "past_T"])
+def test_fused_kernel_many_channels(C_kind):
+    """channel_prefix from the one-launch kernel when channels are shorter
+    than a block's 8 tokens (several columns end in one block) and when
+    there are more channels than tokens (every column past the last token
+    ends at T), against the oracle."""
+    import combine_get_dispatch_counts_amd as epx
+
+    K, E, R, h, fp8 = 8, 64, 8, 256, False
+    first, last = _one_launch_window(h, K, E, R, fp8)
+    T = min(first + 101, last)
+    assert epx.fused_launches(T, h, K, E, R, fp8) == 1
+    C = 1000 if C_kind == "dense" else T + 7
+    say(f"fused kernel T={T} C={C}")
+    rng = np.random.default_rng(T + C)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=T + 5, p_drop=0.1)
+    w = rng.random((T, K)).astype(np.float32)
+    _fused_check(x, topk, w, E, R, fp8, C=C)
+
+
 def test_fused_shares_workspace_with_layout():
     """One workspace for fused calls (small batches, which do not touch it,
     and one-launch / two-launch ones, which do) and two-launch layout calls
