@@ -141,6 +141,12 @@ def _loop_us(fn, n):
     return a.elapsed_time(b) * 1e3 / n
 
 
+def _eager_us(fn, n, reps=3):
+    """Median over reps of _loop_us: launches from Python are timed with the
+    host in the loop, so one host stall must not decide the figure."""
+    return statistics.median(_loop_us(fn, n) for _ in range(reps))
+
+
 def _graph_us(fn, n):
     """Average microseconds per call of fn, n calls captured in one HIP graph
     and replayed (no host launch work per call: for kernels shorter than a
@@ -165,8 +171,8 @@ def _graph_us(fn, n):
 
 
 def other_workloads(n=20):
-    """The FP8, low-latency, skewed, two-stage-combine and receive rows on
-    their own workloads: per-kernel time, compulsory GB/s and fraction of the
+    """The FP8, low-latency, tiny, skewed, two-stage-combine and receive rows
+    on their own workloads: per-kernel time, compulsory GB/s and fraction of the
     8 TB/s HBM peak. Not the headline figure (that is the prefill step
     above); reported beside it."""
     import numpy as np
@@ -320,15 +326,43 @@ def other_workloads(n=20):
 
     out["decode_steps"] = {
         "workload": f"T={T} h={h} E={E} R={R} topk={K}: dispatch + combine per step",
-        "ll_fp8_step_us": {"eager": round(_loop_us(ll_pair, n) / 2, 2),
+        "ll_fp8_step_us": {"eager": round(_eager_us(ll_pair, n) / 2, 2),
                            "graph": round(_graph_us(ll_pair, n) / 2, 2)},
-        "ht_bf16_two_launch_step_us": {"eager": round(_loop_us(ht_two, n), 2),
+        "ht_bf16_two_launch_step_us": {"eager": round(_eager_us(ht_two, n), 2),
                                        "graph": round(_graph_us(ht_two, n), 2)},
-        "ht_bf16_fused_step_us": {"eager": round(_loop_us(ht_fused, n), 2),
+        "ht_bf16_fused_step_us": {"eager": round(_eager_us(ht_fused, n), 2),
                                   "graph": round(_graph_us(ht_fused, n), 2)},
     }
     assert epx.get_error() == 0
     del ll_bufs, y, comb, ws_d, fws_d, lay_d, bufs_d, y2
+    torch.cuda.empty_cache()
+
+    # the tiny worked-example size: T=64, h=128, E=8, R=4, topk=2 (latency-bound:
+    # the whole step, layout + dispatch in one launch, then combine)
+    inp = synth.make_inputs(1)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    tk = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    fws_t = torch.zeros(max(epx.fused_workspace_size(T, K, E, R), 1), dtype=torch.uint8,
+                        device=dev)
+    lay_t = epx.alloc_layout(T, K, E, R, None, dev)
+    bufs_t = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, False, dev)
+    y_t = synth.expert_outputs(T * K, h, seed=31, device="cuda")
+    comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+
+    def tiny_step():
+        d = epx.dispatch_fused(x, tk, w, E, R, layout=lay_t, out=bufs_t, workspace=fws_t)
+        epx.combine(y_t, d.pos_exp, w, out=comb)
+
+    out["tiny"] = {
+        "workload": f"T={T} h={h} E={E} R={R} topk={K}, bf16: layout + dispatch (one launch) "
+                    "+ combine per step",
+        "step_us": {"eager": round(_eager_us(tiny_step, n), 2),
+                    "graph": round(_graph_us(tiny_step, n), 2)}}
+    assert epx.get_error() == 0
+    del fws_t, lay_t, bufs_t, y_t, comb
     torch.cuda.empty_cache()
 
     # skewed routing, bf16: T=8192, h=4096, E=64, R=8, topk=6
