@@ -33,6 +33,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# rates of the dispatch's paced store sweep, bf16 and FP8 rows (the library's defaults)
+SWEEP_GBPS = (6200, 6000)
 METRIC = "dispatch+combine µs/layer and HBM GB/s (% peak) at T=4096,h=7168,topk=8"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T4096_traffic.json")
 # each kernel's sources: its measured traffic is reported only while these match
@@ -579,6 +581,7 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    epx.set_sweep_rate(*SWEEP_GBPS)
     inp = synth.make_inputs(3)
     wl = inp["workload"]
     T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
@@ -807,6 +810,7 @@ def main():
         "cold_cache_us_per_layer": round(cold_us, 2) if cold_us else None,
         "graph_us_per_layer": round(graph_us, 2) if graph_us else None,
         "fused_kernel_us": round(fused_us, 2),
+        "sweep_gbps": {"bf16": SWEEP_GBPS[0], "fp8": SWEEP_GBPS[1]},
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("fused_kernel"),

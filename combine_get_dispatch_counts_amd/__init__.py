@@ -31,6 +31,7 @@ from .api import (  # noqa: E402
     Received,
     recv_permute,
     scale_stride,
+    set_sweep_rate,
     workspace_size,
 )
 
@@ -38,4 +39,4 @@ __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
            "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
-           "fused_launches", "dispatch_fused"]
+           "fused_launches", "dispatch_fused", "set_sweep_rate"]

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libepx.so")
 
 EPX_OK, EPX_EINVAL, EPX_ECAPACITY, EPX_EUNSUPPORTED, EPX_EHIP, EPX_EDEVICE = 0, -1, -2, -3, -4, -5
 DEV_BAD_ROUTE, DEV_OVERFLOW, DEV_BAD_HANDLE, DEV_WORKSPACE = 1, 2, 4, 8
-MAX_TOPK, MAX_EXPERTS, MAX_RANKS = 32, 512, 64
+MAX_TOPK, MAX_EXPERTS, MAX_RANKS, MAX_SWEEP_GBPS = 32, 512, 64, 100000
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -24,6 +24,7 @@ SIGNATURES = {
     "epx_create": (_I, [ctypes.POINTER(_P), _I]),
     "epx_destroy": (_I, [_P]),
     "epx_strerror": (ctypes.c_char_p, [_I]),
+    "epx_set_sweep_rate": (_I, [_P, _I, _I]),
     "epx_workspace_size": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "epx_ll_size_hint": (_SZ, [_I, _I, _I, _I, _I]),
     "epx_scale_stride": (_I, [_I]),

@@ -129,6 +129,15 @@ def ll_size_hint(max_tokens_per_rank: int, h: int, R: int, E: int, fp8: bool) ->
     return int(_lib.load().epx_ll_size_hint(max_tokens_per_rank, h, R, E, int(fp8)))
 
 
+def set_sweep_rate(bf16_gbps: int, fp8_gbps: int, device: torch.device | None = None) -> None:
+    """Rate (GB/s of destination rows) of the high-throughput dispatch's
+    paced store sweep for bf16 and FP8 rows; 0 turns pacing off. Outputs do
+    not depend on it (see epx_set_sweep_rate in include/epx.h)."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    check(_lib.load().epx_set_sweep_rate(_ctx(device), int(bf16_gbps), int(fp8_gbps)),
+          "epx_set_sweep_rate")
+
+
 def get_error(device: torch.device | None = None) -> int:
     """Synchronise the current stream, return and clear the device error bits."""
     device = device or torch.device("cuda", torch.cuda.current_device())
@@ -541,4 +550,4 @@ __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
            "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
-           "fused_launches", "dispatch_fused"]
+           "fused_launches", "dispatch_fused", "set_sweep_rate"]

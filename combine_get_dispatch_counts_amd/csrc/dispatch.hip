@@ -20,6 +20,8 @@
 // (source, expert) regions, FP8 payload. [P3] "DeepSeek DeepEP探索：低延迟分发",
 // 3.2: the local path is an unrolled 16-byte vector copy with non-caching
 // loads -- kept here as streaming 16-byte loads.
+#include <atomic>
+
 #include "dispatch_device.h"
 
 namespace epx {
@@ -48,7 +50,8 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
     }
     if (valid)
         recv_r = (int64_t)a.exp_off[(int)e] + a.slot_in_expert[tk + lane];
-    dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r);
+    const int64_t nsend = (a.sweep_bpt && a.send_x) ? a.rank_off[a.R] : 0;
+    dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r, nsend);
 }
 
 // Low-latency dispatch, one launch. Block t handles token t with kLLWaves
@@ -183,23 +186,46 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
 }  // namespace
 
 
+// One-wave blocks of dispatch_kernel<FP8, NV> a compute unit holds at once
+// (the occupancy query, asked once per instantiation; 0 if it fails).
 template <bool FP8, int NV>
-static void launch_dispatch_nv(const DispatchArgs &a, hipStream_t stream)
+static int dispatch_blocks_per_cu()
 {
-    hipLaunchKernelGGL((dispatch_kernel<FP8, NV>), dim3(a.T), dim3(kWave), 0, stream, a);
+    static std::atomic<int> cache{-1};
+    int n = cache.load(std::memory_order_relaxed);
+    if (n >= 0)
+        return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dispatch_kernel<FP8, NV>, kWave, 0) !=
+        hipSuccess)
+        n = 0;
+    n = n < 0 ? 0 : n;
+    cache.store(n, std::memory_order_relaxed);
+    return n;
 }
 
-hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, hipStream_t stream)
+// The sweep is paced only when every token's wave is resident at once: a
+// wave held back for a late row keeps its place, so with later rounds of
+// waves the pacing would stall them.
+template <bool FP8, int NV>
+static void launch_dispatch_nv(const DispatchArgs &a, int cus, hipStream_t stream)
+{
+    DispatchArgs b = a;
+    if ((int64_t)a.T > (int64_t)dispatch_blocks_per_cu<FP8, NV>() * cus)
+        b.sweep_bpt = 0;
+    hipLaunchKernelGGL((dispatch_kernel<FP8, NV>), dim3(a.T), dim3(kWave), 0, stream, b);
+}
+
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, hipStream_t stream)
 {
     if (a.T == 0)
         return hipSuccess;
     switch (pick_nv(a.h, fp8) + (fp8 ? 100 : 0)) {
-    case 8: launch_dispatch_nv<false, 8>(a, stream); break;
-    case 14: launch_dispatch_nv<false, 14>(a, stream); break;
-    case 16: launch_dispatch_nv<false, 16>(a, stream); break;
-    case 104: launch_dispatch_nv<true, 4>(a, stream); break;
-    case 107: launch_dispatch_nv<true, 7>(a, stream); break;
-    default: launch_dispatch_nv<true, 8>(a, stream); break;
+    case 8: launch_dispatch_nv<false, 8>(a, cus, stream); break;
+    case 14: launch_dispatch_nv<false, 14>(a, cus, stream); break;
+    case 16: launch_dispatch_nv<false, 16>(a, cus, stream); break;
+    case 104: launch_dispatch_nv<true, 4>(a, cus, stream); break;
+    case 107: launch_dispatch_nv<true, 7>(a, cus, stream); break;
+    default: launch_dispatch_nv<true, 8>(a, cus, stream); break;
     }
     return hipGetLastError();
 }

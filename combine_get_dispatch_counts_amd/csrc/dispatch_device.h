@@ -228,37 +228,84 @@ struct Dests {
     int send_row, recv_row;
 };
 
+// Smallest value over the wave.
+__device__ __forceinline__ int wave_min(int v)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1)
+        v = min(v, __shfl_xor(v, d, kWave));
+    return v;
+}
+
+// The paced sweep. Scattered row stores from many waves reach HBM as
+// random writes (a fill in random order tops out at 5.0-5.3 TB/s on MI355X
+// whatever the chunk size), while writes that the running waves make to
+// adjacent addresses go at sequential-fill speed (6.5 TB/s). When every
+// token's wave is on the chip at once, the scatter can be made sequential
+// in time: each wave stores its rows in ascending order of their place in
+// the output -- all send rows, then all receive rows -- and holds each row
+// back until the wall clock has run (row's byte offset in that order) /
+// sweep_bpt ticks since the wave became ready. All waves then write near
+// one front that moves through the output at the set rate. Only the time of
+// each store changes, never what is stored; every wait is bounded by the
+// clock.
+struct Sweep {
+    uint64_t t0;        // wall clock when the wave became ready
+    uint32_t bpt;       // bytes per tick (0: no pacing)
+    int64_t nsend;      // send rows ahead of the receive rows in the sweep
+    int64_t row_bytes;  // bytes of one destination row (FP8: codes and scale row)
+    __device__ __forceinline__ void wait(int64_t g) const
+    {
+        if (bpt == 0)
+            return;
+        const uint64_t due = t0 + (uint64_t)(g * row_bytes) / bpt;
+        while (wall_clock64() < due)
+            __builtin_amdgcn_s_sleep(1);
+    }
+};
+
 // Write the token's row (the pass held in `row`, plus any further passes
-// loaded here) to every destination: send rows in buffer a, recv rows in b.
+// loaded here) to every destination, send rows (buffer a, rank order) then
+// receive rows (buffer b, ascending row), each when the sweep reaches it.
 // FP8 rows go out with the nontemporal policy, bf16 rows write-through.
 template <bool FP8, typename Row>
 __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t *xrow, int h,
-                                        void *a_x, float *a_s, void *b_x, float *b_s)
+                                        void *a_x, float *a_s, void *b_x, float *b_s,
+                                        const Sweep &sw)
 {
     const int nvec = h >> 3, nseg = h >> 4, ld_s = scale_stride(h);
     const int per_pass = Row::kPerPass;
     const int nitems = FP8 ? nseg : nvec;
     const size_t row_bytes = FP8 ? (size_t)h : (size_t)h * 2;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
+    const int lane = lane_id();
     for (int i0 = 0; i0 < nitems; i0 += per_pass) {
         if (i0 > 0) {
             row.load(src, i0, nitems);
             row.quantise(i0, nitems);
         }
-        for (uint64_t m = d.rbits; m; m &= m - 1) {
+        for (uint64_t m = d.rbits; m; m &= m - 1) {  // rank order is row order
             const int r = readlane(d.send_row, __builtin_ctzll(m));
             if (r < 0)
                 continue;
+            sw.wait(r);
             if constexpr (FP8)
                 row.template store<StorePolicy::NT>(static_cast<uint8_t *>(a_x) + (size_t)r * row_bytes,
                                                     a_s + (size_t)r * ld_s, i0, nseg);
             else
                 row.store(static_cast<char *>(a_x) + (size_t)r * row_bytes, i0, nvec);
         }
-        for (uint64_t m = d.vbits; m; m &= m - 1) {
-            const int r = readlane(d.recv_row, __builtin_ctzll(m));
+        // receive rows, smallest first (skipped rows, -1, sort last)
+        const int key = ((d.vbits >> lane) & 1ull) ? (d.recv_row < 0 ? INT32_MAX - 1 : d.recv_row)
+                                                   : INT32_MAX;
+        for (uint64_t m = d.vbits; m;) {
+            const int kmin = wave_min(((m >> lane) & 1ull) ? key : INT32_MAX);
+            const int k = __builtin_ctzll(m & uniform64(__ballot(key == kmin)));
+            m &= ~(1ull << k);
+            const int r = readlane(d.recv_row, k);
             if (r < 0)
                 continue;
+            sw.wait(sw.nsend + r);
             if constexpr (FP8)
                 row.template store<StorePolicy::NT>(static_cast<uint8_t *>(b_x) + (size_t)r * row_bytes,
                                                     b_s + (size_t)r * ld_s, i0, nseg);
@@ -323,15 +370,21 @@ __device__ __forceinline__ Dests token_dests(const DispatchArgs &a, int t, int64
 // The per-token part of the high-throughput dispatch, for a wave holding
 // token t's row (first pass loaded, not yet quantised) and its lanes as in
 // token_dests: checks, handle and metadata, then the row to every
-// destination.
+// destination. nsend: the number of send rows (the receive rows' place in
+// the sweep; 0 without a send buffer). The wave's sweep starts now.
 template <bool FP8, typename Row>
 __device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row &row,
                                                const uint16_t *xrow, int64_t e, int64_t send_r,
-                                               int64_t recv_r)
+                                               int64_t recv_r, int64_t nsend)
 {
+    Sweep sw;
+    sw.t0 = wall_clock64();
+    sw.bpt = a.sweep_bpt;
+    sw.nsend = nsend;
+    sw.row_bytes = FP8 ? (int64_t)a.h + 4 * (int64_t)scale_stride(a.h) : 2 * (int64_t)a.h;
     const Dests d = token_dests(a, t, e, send_r, recv_r, true);
     row.quantise(0, FP8 ? a.h >> 4 : a.h >> 3);
-    scatter<FP8>(row, d, xrow, a.h, a.send_x, a.send_scales, a.recv_x, a.recv_scales);
+    scatter<FP8>(row, d, xrow, a.h, a.send_x, a.send_scales, a.recv_x, a.recv_scales, sw);
 }
 
 // One slice of a token's row (items s0 .. s0 + Row::kPerPass - 1, loaded in

@@ -69,7 +69,11 @@ int epx_create(epx_ctx **out, int device)
         rc = EPX_EHIP;
     } else {
         c->device = device;
+        c->sweep_gbps[0] = epx::kSweepGBpsBf16;
+        c->sweep_gbps[1] = epx::kSweepGBpsFp8;
         if (hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, device) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&c->wclk_khz, hipDeviceAttributeWallClockRate, device) !=
                 hipSuccess ||
             hipMalloc(reinterpret_cast<void **>(&c->d_err), sizeof(int)) != hipSuccess ||
             hipMemset(c->d_err, 0, sizeof(int)) != hipSuccess) {
@@ -255,6 +259,11 @@ static int dispatch_args(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *
     a.recv_x = recv_x; a.recv_scales = recv_scales; a.recv_src = recv_src;
     a.recv_cap = recv_cap_rows; a.pos_exp = pos_exp;
     a.err = ctx->d_err;
+    // the paced sweep's rate in bytes per wall-clock tick (GB/s = 1e6 B per ms)
+    const int64_t gbps = ctx->sweep_gbps[fp8 ? 1 : 0];
+    a.sweep_bpt = ctx->wclk_khz > 0 ? (uint32_t)(gbps * 1000000 / ctx->wclk_khz) : 0u;
+    if (gbps > 0 && a.sweep_bpt == 0)
+        a.sweep_bpt = 1;
     return EPX_OK;
 }
 
@@ -273,7 +282,17 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
                                  recv_src, recv_cap_rows, pos_exp, a);
     if (rc != EPX_OK)
         return rc;
-    return launched(epx::launch_dispatch(a, fp8 != 0, stream));
+    return launched(epx::launch_dispatch(a, fp8 != 0, ctx->cus, stream));
+}
+
+int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps)
+{
+    if (!ctx || bf16_gbps < 0 || fp8_gbps < 0 || bf16_gbps > EPX_MAX_SWEEP_GBPS ||
+        fp8_gbps > EPX_MAX_SWEEP_GBPS)
+        return EPX_EINVAL;
+    ctx->sweep_gbps[0] = bf16_gbps;
+    ctx->sweep_gbps[1] = fp8_gbps;
+    return EPX_OK;
 }
 
 int epx_fused_workspace_size(int T, int K, int E, int R, size_t *bytes)

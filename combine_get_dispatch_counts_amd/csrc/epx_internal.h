@@ -8,11 +8,19 @@
 
 struct epx_ctx {
     int device;
-    int cus;     // compute units of the device
-    int *d_err;  // device error word (EPX_DEV_* bits)
+    int cus;            // compute units of the device
+    int *d_err;         // device error word (EPX_DEV_* bits)
+    int wclk_khz;       // rate of the device's constant wall clock (wall_clock64)
+    int sweep_gbps[2];  // paced row-store sweep rate for bf16 and FP8 rows (0: off)
 };
 
 namespace epx {
+
+// Default rates of the paced sweep of the high-throughput dispatch's row
+// stores (GB/s of destination rows), measured on MI355X at the prefill shape:
+// just below the rate at which the paced front outruns the memory system.
+constexpr int kSweepGBpsBf16 = 6200;
+constexpr int kSweepGBpsFp8 = 6000;
 
 // fp32 entries per row of an FP8 scale array for hidden size h: the h/128
 // group scales rounded up to a multiple of 32, so every row is a whole
@@ -71,9 +79,16 @@ struct DispatchArgs {
     int64_t recv_cap;
     int32_t *pos_exp;
     int *err;
+    // The paced sweep (0: off): each wave stores its token's rows in
+    // ascending order of their place in the sweep -- the send rows, then the
+    // receive rows -- and none before its own start plus that row's byte
+    // offset in the sweep divided by sweep_bpt (bytes per wall-clock tick).
+    uint32_t sweep_bpt;
 };
 
-hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, hipStream_t stream);
+// Launch the dispatch; the sweep is paced only when every token's wave is on
+// the chip at once (cus: compute units of the device).
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, hipStream_t stream);
 
 struct LLArgs {
     const uint16_t *x;

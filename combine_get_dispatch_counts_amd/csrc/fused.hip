@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
         }
         if (lane < K)
             l.slot_in_expert[(int64_t)t * K + lane] = slot;
-        dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r);
+        dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r, off[E + 1 + R]);
     }
 
     // this block is done: the last block of the grid opens the next call
@@ -445,7 +445,7 @@ hipError_t launch_fused_k(const FusedArgs &f, hipStream_t stream, bool launch, i
     }
     if (!one) {
         const hipError_t e = launch_layout(f.lay, stream);
-        return e != hipSuccess ? e : launch_dispatch(f.disp, FP8, stream);
+        return e != hipSuccess ? e : launch_dispatch(f.disp, FP8, f.cus, stream);
     }
     hipLaunchKernelGGL((fused_kernel<KMAX, FP8, NV>), dim3((unsigned)blocks),
                        dim3(kLayoutThreads), lds, stream, f);

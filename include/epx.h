@@ -64,6 +64,7 @@ extern "C" {
 #define EPX_MAX_TOPK 32
 #define EPX_MAX_EXPERTS 512
 #define EPX_MAX_RANKS 64
+#define EPX_MAX_SWEEP_GBPS 100000
 
 typedef struct epx_ctx epx_ctx;
 
@@ -76,6 +77,25 @@ typedef struct epx_ctx epx_ctx;
 int epx_create(epx_ctx **out, int device);
 int epx_destroy(epx_ctx *ctx);
 const char *epx_strerror(int code);
+
+/* Rate of the paced store sweep of the high-throughput dispatch
+ * (epx_dispatch, epx_dispatch_fused), in GB/s of destination rows, for bf16
+ * rows and for FP8 rows (codes plus scale row); 0 turns pacing off. Pacing
+ * changes when each row is stored, never what is stored: outputs are
+ * identical at every rate. When every token's wave is on the device at once
+ * (the fused call's one-launch shapes; epx_dispatch while T fits the
+ * device), each wave stores its token's rows in ascending order of their
+ * place in the output -- send rows, then receive rows -- and holds a row
+ * back until its byte offset in that order, at this rate, has elapsed since
+ * the wave became ready. The waves' stores then move through the output as
+ * one front, which HBM absorbs at sequential-write speed, where the same
+ * rows in routing order arrive as random writes. A rate above what the
+ * memory sustains lets the front spread back toward random order (no worse
+ * than unpaced); a lower one leaves bandwidth idle. Defaults, measured on
+ * MI355X: 6200 (bf16) and 6000 (FP8). The setting is per context and read at
+ * each call. EPX_EINVAL for a NULL context or a rate outside
+ * [0, EPX_MAX_SWEEP_GBPS]. */
+int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps);
 
 /* Workspace bytes epx_get_dispatch_layout needs for (T, K, E, R) (host out):
  * a 128-byte head plus 8 bytes per (256-token tile, expert or rank).

@@ -125,3 +125,9 @@ def test_fused_workspace_size(lib):
     assert lib.epx_fused_workspace_size(0, 8, 256, 32, ctypes.byref(n)) == 0
     assert n.value == 0
     assert lib.epx_fused_workspace_size(10, 8, 256, 30, ctypes.byref(n)) == -1
+
+
+def test_set_sweep_rate_needs_a_context(lib):
+    """Argument checks come first: no context, no setting."""
+    assert lib.epx_set_sweep_rate(None, 6200, 6000) == -1
+    assert lib.epx_set_sweep_rate(None, 0, 0) == -1

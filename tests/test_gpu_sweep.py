@@ -1,0 +1,90 @@
+"""The paced store sweep changes when the dispatch stores its rows, never what
+it stores: at the prefill size (T=4096, h=7168, E=256, R=32, topk=8) the
+dispatch and the fused call give the same bytes with pacing off, at the
+default rates, far below what the memory sustains and far above it, and the
+default run matches the oracle. Also the setter's argument checks."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu import host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+DEFAULTS = (6200, 6000)
+
+
+def _run(epx, inp, fused, fp8, bufs, lay_buf, ws):
+    wl = inp["workload"]
+    x = torch.from_numpy(inp["x"].view(np.int16)).cuda().view(torch.bfloat16)
+    tk = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    for v in bufs.values():
+        if v is not None:
+            v.view(torch.uint8).fill_(0xA5)
+    if fused:
+        d = epx.dispatch_fused(x, tk, w, wl.E, wl.R, fp8=fp8, layout=lay_buf, out=bufs,
+                               workspace=ws)
+    else:
+        lay = epx.get_dispatch_layout(tk, wl.E, wl.R, out=lay_buf)
+        d = epx.dispatch(x, tk, w, wl.E, wl.R, fp8=fp8, layout=lay, out=bufs)
+    flags = epx.get_error()
+    assert flags == 0, f"device flags {flags:#x}"
+    out = {k: host_bits(v) for k, v in bufs.items() if v is not None}
+    out["totals"] = host_bits(d.layout.totals)
+    return out
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("fused", [False, True])
+def test_sweep_rate_does_not_change_outputs(fused, fp8):
+    import combine_get_dispatch_counts_amd as epx
+
+    inp = synth.make_inputs(3)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    if fused:
+        assert epx.fused_launches(T, h, K, E, R, fp8) == 1
+    dev = torch.device("cuda")
+    bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, fp8, dev)
+    lay_buf = epx.alloc_layout(T, K, E, R, None, dev)
+    ws = torch.zeros(epx.fused_workspace_size(T, K, E, R), dtype=torch.uint8, device=dev)
+    runs = {}
+    try:
+        for rate in (DEFAULTS, (0, 0), (1500, 1500), (60000, 60000)):
+            say(f"{'fused' if fused else 'dispatch'} fp8={fp8} sweep rate {rate}")
+            epx.set_sweep_rate(*rate)
+            runs[rate] = _run(epx, inp, fused, fp8, bufs, lay_buf, ws)
+    finally:
+        epx.set_sweep_rate(*DEFAULTS)
+    ref = runs[(0, 0)]
+    for rate, got in runs.items():
+        for k in ref:
+            assert np.array_equal(got[k].view(np.uint8), ref[k].view(np.uint8)), \
+                f"{k} differs at sweep rate {rate}"
+    # the default run against the oracle (rows up to the totals)
+    o = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], E, R, fp8=fp8)
+    n_send, n_recv = (int(v) for v in ref["totals"])
+    got = runs[DEFAULTS]
+    for k in ["send_x", "send_src", "send_topk_idx", "send_topk_w", "recv_x", "recv_src",
+              "pos_exp"]:
+        g = got[k] if k == "pos_exp" else got[k][:n_send if k.startswith("send") else n_recv]
+        assert np.array_equal(g.view(np.uint8), np.asarray(o[k]).view(np.uint8)), k
+    if fp8:
+        ngrp = h // 128
+        for k, n in (("send_scales", n_send), ("recv_scales", n_recv)):
+            assert np.array_equal(got[k][:n, :ngrp].view(np.uint32),
+                                  np.asarray(o[k]).view(np.uint32)), k
+
+
+def test_sweep_rate_argument_checks():
+    import combine_get_dispatch_counts_amd as epx
+
+    with pytest.raises(epx.EpxError):
+        epx.set_sweep_rate(-1, 6000)
+    with pytest.raises(epx.EpxError):
+        epx.set_sweep_rate(6200, 100001)
+    epx.set_sweep_rate(100000, 0)
+    epx.set_sweep_rate(*DEFAULTS)
