@@ -1,8 +1,10 @@
 """The paced store sweep changes when the dispatch stores its rows, never what
-it stores: at the prefill size (T=4096, h=7168, E=256, R=32, topk=8) the
-dispatch and the fused call give the same bytes with pacing off, at the
-default rates, far below what the memory sustains and far above it, and the
-default run matches the oracle. Also the setter's argument checks."""
+it stores: on the prefill (T=4096, h=7168, E=256, R=32, topk=8), the skewed
+workload (T=8192: every wave slot of the device) and the FP8 prefill at
+T=16384 (more tokens than one round of waves, so left unpaced) the dispatch
+and the fused call give the same bytes with pacing off, at the default
+rates, far below what the memory sustains and far above it, and the default
+run matches the oracle. Also the setter's argument checks."""
 import numpy as np
 import pytest
 import torch
@@ -37,12 +39,15 @@ def _run(epx, inp, fused, fp8, bufs, lay_buf, ws):
     return out
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("fused", [False, True])
-def test_sweep_rate_does_not_change_outputs(fused, fp8):
+@pytest.mark.parametrize("cfg,fused,fp8", [
+    (3, False, False), (3, False, True), (3, True, False), (3, True, True),
+    (4, False, False),   # skewed routing
+    (5, False, True),    # T = 16384: more tokens than one round of waves (left unpaced)
+])
+def test_sweep_rate_does_not_change_outputs(cfg, fused, fp8):
     import combine_get_dispatch_counts_amd as epx
 
-    inp = synth.make_inputs(3)
+    inp = synth.make_inputs(cfg)
     wl = inp["workload"]
     T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
     if fused:
@@ -54,7 +59,7 @@ def test_sweep_rate_does_not_change_outputs(fused, fp8):
     runs = {}
     try:
         for rate in (DEFAULTS, (0, 0), (1500, 1500), (60000, 60000)):
-            say(f"{'fused' if fused else 'dispatch'} fp8={fp8} sweep rate {rate}")
+            say(f"config {cfg} {'fused' if fused else 'dispatch'} fp8={fp8} sweep rate {rate}")
             epx.set_sweep_rate(*rate)
             runs[rate] = _run(epx, inp, fused, fp8, bufs, lay_buf, ws)
     finally:
@@ -77,6 +82,34 @@ def test_sweep_rate_does_not_change_outputs(fused, fp8):
         for k, n in (("send_scales", n_send), ("recv_scales", n_recv)):
             assert np.array_equal(got[k][:n, :ngrp].view(np.uint32),
                                   np.asarray(o[k]).view(np.uint32)), k
+
+
+def test_sweep_rate_receive_permute():
+    """The receiver's permute of the prefill's 29 811 rank-major rows into 8
+    local experts (more rows than one round of waves) stores the same bytes
+    whatever the sweep rate."""
+    import combine_get_dispatch_counts_amd as epx
+
+    inp = synth.make_inputs(3)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    d = epx.dispatch(torch.from_numpy(inp["x"].view(np.int16)).cuda().view(torch.bfloat16),
+                     torch.from_numpy(inp["topk_idx"]).cuda(),
+                     torch.from_numpy(inp["topk_w"]).cuda(), E, R)
+    rows, idx = d.send_x, d.send_topk_idx
+    got = {}
+    try:
+        for rate in (DEFAULTS, (0, 0)):
+            say(f"receive permute of {rows.shape[0]} rows, sweep rate {rate}")
+            epx.set_sweep_rate(*rate)
+            rec = epx.recv_permute(rows, idx, E // R)
+            assert epx.get_error() == 0
+            n = int(rec.layout.totals[1].item())  # rows past the total are not written
+            got[rate] = (host_bits(rec.x)[:n], host_bits(rec.src_row)[:n], host_bits(rec.pos))
+    finally:
+        epx.set_sweep_rate(*DEFAULTS)
+    for a, b in zip(got[DEFAULTS], got[(0, 0)]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 def test_sweep_rate_argument_checks():
