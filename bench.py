@@ -415,7 +415,7 @@ PROFILE_RUNS = {
 }
 # the prefill launches the traffic record covers: (kernel, grid in threads)
 PREFILL_KERNELS = {
-    "dispatch_kernel": ("dispatch_kernel<false, 14>", 4096 * 64),
+    "dispatch_kernel": ("dispatch_kernel<false, 14, false>", 4096 * 64),
     "fused_kernel": ("fused_kernel<8, false, 14>", (4096 // 8) * 512),
 }
 _KERNEL_PREFIXES = ("dispatch", "combine", "layout", "ll_", "fill", "fused")

@@ -27,10 +27,11 @@
 namespace epx {
 namespace {
 
-template <bool FP8, int NV>
+template <bool FP8, int NV, bool CHUNKED>
 __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
 {
-    const int t = blockIdx.x, lane = threadIdx.x;
+    const int t = CHUNKED ? a.t_begin + (int)blockIdx.x : (int)blockIdx.x;
+    const int lane = threadIdx.x;
     const int64_t tk = (int64_t)t * a.K;
     const uint16_t *xrow = a.x + (size_t)t * a.h;
 
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
     if (valid)
         recv_r = (int64_t)a.exp_off[(int)e] + a.slot_in_expert[tk + lane];
     const int64_t nsend = (a.sweep_bpt && a.send_x) ? a.rank_off[a.R] : 0;
-    dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r, nsend);
+    dispatch_token<FP8, CHUNKED>(a, t, row, xrow, e, send_r, recv_r, nsend);
 }
 
 // Low-latency dispatch, one launch. Block t handles token t with kLLWaves
@@ -186,33 +187,59 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
 }  // namespace
 
 
-// One-wave blocks of dispatch_kernel<FP8, NV> a compute unit holds at once
-// (the occupancy query, asked once per instantiation; 0 if it fails).
-template <bool FP8, int NV>
+// One-wave blocks of dispatch_kernel<FP8, NV, CHUNKED> a compute unit holds
+// at once (the occupancy query, asked once per instantiation; 0 if it fails).
+template <bool FP8, int NV, bool CHUNKED>
 static int dispatch_blocks_per_cu()
 {
     static std::atomic<int> cache{-1};
     int n = cache.load(std::memory_order_relaxed);
     if (n >= 0)
         return n;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dispatch_kernel<FP8, NV>, kWave, 0) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dispatch_kernel<FP8, NV, CHUNKED>, kWave,
+                                                     0) != hipSuccess)
         n = 0;
     n = n < 0 ? 0 : n;
     cache.store(n, std::memory_order_relaxed);
     return n;
 }
 
-// The sweep is paced only when every token's wave is resident at once: a
-// wave held back for a late row keeps its place, so with later rounds of
-// waves the pacing would stall them.
+// A paced sweep needs every wave of a launch on the chip at once: a wave
+// held back for a late row keeps its place, so a wave that found no place
+// would wait behind it. Up to one round of waves, one launch paces the
+// whole sweep; beyond, the tokens go in chunks of consecutive tokens, each
+// its own launch sweeping its own rows, sized to 7/8 of the round the
+// occupancy query reports for the chunked kernel (the query has been seen to
+// promise a wave per SIMD more than a kernel got), at 9/10 of the set rate
+// (each chunk's sweep shares HBM with the loads of its own rows; measured
+// on the FP8 prefill, T = 16384 in five chunks: best at 5400 GB/s, slower
+// than unpaced at 6000). Unpaced, or when the query fails, one launch takes
+// all tokens.
 template <bool FP8, int NV>
 static void launch_dispatch_nv(const DispatchArgs &a, int cus, hipStream_t stream)
 {
     DispatchArgs b = a;
-    if ((int64_t)a.T > (int64_t)dispatch_blocks_per_cu<FP8, NV>() * cus)
+    b.t_begin = 0;
+    b.t_count = 0;
+    if (a.sweep_bpt == 0 || (int64_t)a.T <= (int64_t)dispatch_blocks_per_cu<FP8, NV, false>() * cus) {
+        hipLaunchKernelGGL((dispatch_kernel<FP8, NV, false>), dim3(a.T), dim3(kWave), 0, stream, b);
+        return;
+    }
+    const int64_t round = (int64_t)dispatch_blocks_per_cu<FP8, NV, true>() * cus * 7 / 8;
+    if (round <= 0) {
         b.sweep_bpt = 0;
-    hipLaunchKernelGGL((dispatch_kernel<FP8, NV>), dim3(a.T), dim3(kWave), 0, stream, b);
+        hipLaunchKernelGGL((dispatch_kernel<FP8, NV, false>), dim3(a.T), dim3(kWave), 0, stream, b);
+        return;
+    }
+    const int64_t nchunk = (a.T + round - 1) / round;
+    const int64_t size = (a.T + nchunk - 1) / nchunk;
+    b.sweep_bpt = a.sweep_bpt * 9 / 10 > 0 ? a.sweep_bpt * 9 / 10 : 1;
+    for (int64_t t0 = 0; t0 < a.T; t0 += size) {
+        b.t_begin = (int)t0;
+        b.t_count = (int)(a.T - t0 < size ? a.T - t0 : size);
+        hipLaunchKernelGGL((dispatch_kernel<FP8, NV, true>), dim3((unsigned)b.t_count), dim3(kWave),
+                           0, stream, b);
+    }
 }
 
 hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, hipStream_t stream)

@@ -226,6 +226,9 @@ struct RowFp8 {
 struct Dests {
     uint64_t rbits, vbits;
     int send_row, recv_row;
+    // a chunked sweep only: the destination's segment (lane r: rank r's
+    // rows; lane k: entry k's expert's rows) as first row and row count
+    int send_seg, send_n, recv_seg, recv_n;
 };
 
 // Smallest value over the wave.
@@ -250,17 +253,37 @@ __device__ __forceinline__ int wave_min(int v)
 // each store changes, never what is stored; every wait is bounded by the
 // clock.
 struct Sweep {
+    static constexpr bool kChunked = false;
     uint64_t t0;        // wall clock when the wave became ready
     uint32_t bpt;       // bytes per tick (0: no pacing)
     int64_t nsend;      // send rows ahead of the receive rows in the sweep
     int64_t row_bytes;  // bytes of one destination row (FP8: codes and scale row)
-    __device__ __forceinline__ void wait(int64_t g) const
+    // wait for the row whose place in the sweep is o
+    __device__ __forceinline__ void wait(int64_t o) const
     {
         if (bpt == 0)
             return;
-        const uint64_t due = t0 + (uint64_t)(g * row_bytes) / bpt;
+        const uint64_t due = t0 + (uint64_t)(o * row_bytes) / bpt;
         while (wall_clock64() < due)
             __builtin_amdgcn_s_sleep(1);
+    }
+};
+
+// The sweep of one chunk of a dispatch launched in chunks of consecutive
+// tokens (too many tokens for one round of waves). Rows sit in token order
+// inside every segment (a rank's rows, an expert's rows), so a chunk's rows
+// are one run per segment; a row's place among the chunk's rows is
+// estimated from its place g in the whole sweep and its segment's first row
+// a and size n as (g - a) + (a * cnt - n * tb) / T, for the chunk's tokens
+// [tb, tb + cnt) -- exact when routing is spread evenly over the tokens,
+// and only a timing estimate otherwise.
+struct SweepChunk : Sweep {
+    static constexpr bool kChunked = true;
+    int64_t tb, cnt, T;
+    __device__ __forceinline__ void wait(int64_t g, int64_t a, int64_t n) const
+    {
+        const int64_t o = g - a + (a * cnt - n * tb) / T;
+        Sweep::wait(o < 0 ? 0 : o);
     }
 };
 
@@ -268,10 +291,10 @@ struct Sweep {
 // loaded here) to every destination, send rows (buffer a, rank order) then
 // receive rows (buffer b, ascending row), each when the sweep reaches it.
 // FP8 rows go out with the nontemporal policy, bf16 rows write-through.
-template <bool FP8, typename Row>
+template <bool FP8, typename Row, typename SW>
 __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t *xrow, int h,
                                         void *a_x, float *a_s, void *b_x, float *b_s,
-                                        const Sweep &sw)
+                                        const SW &sw)
 {
     const int nvec = h >> 3, nseg = h >> 4, ld_s = scale_stride(h);
     const int per_pass = Row::kPerPass;
@@ -285,10 +308,14 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
             row.quantise(i0, nitems);
         }
         for (uint64_t m = d.rbits; m; m &= m - 1) {  // rank order is row order
-            const int r = readlane(d.send_row, __builtin_ctzll(m));
+            const int lr = __builtin_ctzll(m);
+            const int r = readlane(d.send_row, lr);
             if (r < 0)
                 continue;
-            sw.wait(r);
+            if constexpr (SW::kChunked)
+                sw.wait(r, readlane(d.send_seg, lr), readlane(d.send_n, lr));
+            else
+                sw.wait(r);
             if constexpr (FP8)
                 row.template store<StorePolicy::NT>(static_cast<uint8_t *>(a_x) + (size_t)r * row_bytes,
                                                     a_s + (size_t)r * ld_s, i0, nseg);
@@ -305,7 +332,10 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
             const int r = readlane(d.recv_row, k);
             if (r < 0)
                 continue;
-            sw.wait(sw.nsend + r);
+            if constexpr (SW::kChunked)
+                sw.wait(sw.nsend + r, sw.nsend + readlane(d.recv_seg, k), readlane(d.recv_n, k));
+            else
+                sw.wait(sw.nsend + r);
             if constexpr (FP8)
                 row.template store<StorePolicy::NT>(static_cast<uint8_t *>(b_x) + (size_t)r * row_bytes,
                                                     b_s + (size_t)r * ld_s, i0, nseg);
@@ -371,18 +401,35 @@ __device__ __forceinline__ Dests token_dests(const DispatchArgs &a, int t, int64
 // token t's row (first pass loaded, not yet quantised) and its lanes as in
 // token_dests: checks, handle and metadata, then the row to every
 // destination. nsend: the number of send rows (the receive rows' place in
-// the sweep; 0 without a send buffer). The wave's sweep starts now.
-template <bool FP8, typename Row>
+// the sweep; 0 without a send buffer). The wave's sweep starts now. CHUNKED:
+// the launch is one chunk [a.t_begin, a.t_begin + a.t_count) of the tokens,
+// and the lanes' segments are read from the layout offsets.
+template <bool FP8, bool CHUNKED = false, typename Row>
 __device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row &row,
                                                const uint16_t *xrow, int64_t e, int64_t send_r,
                                                int64_t recv_r, int64_t nsend)
 {
-    Sweep sw;
+    typename std::conditional<CHUNKED, SweepChunk, Sweep>::type sw;
     sw.t0 = wall_clock64();
     sw.bpt = a.sweep_bpt;
     sw.nsend = nsend;
     sw.row_bytes = FP8 ? (int64_t)a.h + 4 * (int64_t)scale_stride(a.h) : 2 * (int64_t)a.h;
-    const Dests d = token_dests(a, t, e, send_r, recv_r, true);
+    Dests d = token_dests(a, t, e, send_r, recv_r, true);
+    if constexpr (CHUNKED) {
+        sw.tb = a.t_begin;
+        sw.cnt = a.t_count;
+        sw.T = a.T;
+        const int lane = lane_id();
+        d.send_seg = d.send_n = d.recv_seg = d.recv_n = 0;
+        if (send_r >= 0 && lane < a.R) {
+            d.send_seg = a.rank_off[lane];
+            d.send_n = a.rank_off[lane + 1] - d.send_seg;
+        }
+        if (recv_r >= 0 && e >= 0 && e < a.E) {
+            d.recv_seg = a.exp_off[(int)e];
+            d.recv_n = a.exp_off[(int)e + 1] - d.recv_seg;
+        }
+    }
     row.quantise(0, FP8 ? a.h >> 4 : a.h >> 3);
     scatter<FP8>(row, d, xrow, a.h, a.send_x, a.send_scales, a.recv_x, a.recv_scales, sw);
 }

@@ -259,8 +259,10 @@ static int dispatch_args(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *
     a.recv_x = recv_x; a.recv_scales = recv_scales; a.recv_src = recv_src;
     a.recv_cap = recv_cap_rows; a.pos_exp = pos_exp;
     a.err = ctx->d_err;
-    // the paced sweep's rate in bytes per wall-clock tick (GB/s = 1e6 B per ms)
-    const int64_t gbps = ctx->sweep_gbps[fp8 ? 1 : 0];
+    // the paced sweep's rate in bytes per wall-clock tick (GB/s = 1e6 B per ms);
+    // the permute alone reads a row for every row it writes, so the write
+    // rate alone does not describe its traffic: it is left unpaced
+    const int64_t gbps = pack ? ctx->sweep_gbps[fp8 ? 1 : 0] : 0;
     a.sweep_bpt = ctx->wclk_khz > 0 ? (uint32_t)(gbps * 1000000 / ctx->wclk_khz) : 0u;
     if (gbps > 0 && a.sweep_bpt == 0)
         a.sweep_bpt = 1;

@@ -84,10 +84,16 @@ struct DispatchArgs {
     // receive rows -- and none before its own start plus that row's byte
     // offset in the sweep divided by sweep_bpt (bytes per wall-clock tick).
     uint32_t sweep_bpt;
+    // This launch's tokens [t_begin, t_begin + t_count) when a dispatch too
+    // large for one round of waves is launched in chunks (t_count 0: one
+    // launch takes all T); each chunk sweeps its own rows.
+    int t_begin, t_count;
 };
 
-// Launch the dispatch; the sweep is paced only when every token's wave is on
-// the chip at once (cus: compute units of the device).
+// Launch the dispatch (cus: compute units of the device). The sweep is paced
+// when every token's wave is on the chip at once; with more tokens than that,
+// the dispatch is launched in chunks of consecutive tokens that each fit one
+// round, each chunk pacing its own rows.
 hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, hipStream_t stream);
 
 struct LLArgs {

@@ -83,17 +83,20 @@ const char *epx_strerror(int code);
  * rows and for FP8 rows (codes plus scale row); 0 turns pacing off. Pacing
  * changes when each row is stored, never what is stored: outputs are
  * identical at every rate. When every token's wave is on the device at once
- * (the fused call's one-launch shapes; epx_dispatch while T fits the
- * device), each wave stores its token's rows in ascending order of their
- * place in the output -- send rows, then receive rows -- and holds a row
- * back until its byte offset in that order, at this rate, has elapsed since
- * the wave became ready. The waves' stores then move through the output as
- * one front, which HBM absorbs at sequential-write speed, where the same
- * rows in routing order arrive as random writes. A rate above what the
- * memory sustains lets the front spread back toward random order (no worse
- * than unpaced); a lower one leaves bandwidth idle. Defaults, measured on
- * MI355X: 6200 (bf16) and 6000 (FP8). The setting is per context and read at
- * each call. EPX_EINVAL for a NULL context or a rate outside
+ * (the fused call's one-launch shapes; epx_dispatch while T fits the device),
+ * each wave stores its token's rows in ascending order of their place in
+ * the output -- send rows, then receive rows -- and holds a row back until
+ * its byte offset in that order, at this rate, has elapsed since the wave
+ * became ready. The waves' stores then move through the output as one
+ * front, which HBM absorbs at sequential-write speed, where the same rows in
+ * routing order arrive as random writes. A larger epx_dispatch is launched
+ * as chunks of consecutive tokens that each fit, each sweeping its own rows
+ * at 9/10 of the rate. The permute alone (epx_dispatch with send_x = NULL),
+ * which reads as many rows as it writes, is not paced. A rate above what the memory sustains lets the front
+ * spread back toward random order (in one launch measured no slower than
+ * unpaced); a lower one leaves bandwidth idle. Defaults, measured on MI355X:
+ * 6200 (bf16) and 6000 (FP8). The setting is per context and read at each
+ * call. EPX_EINVAL for a NULL context or a rate outside
  * [0, EPX_MAX_SWEEP_GBPS]. */
 int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps);
 

@@ -1,8 +1,8 @@
 """The paced store sweep changes when the dispatch stores its rows, never what
 it stores: on the prefill (T=4096, h=7168, E=256, R=32, topk=8), the skewed
 workload (T=8192: every wave slot of the device) and the FP8 prefill at
-T=16384 (more tokens than one round of waves, so left unpaced) the dispatch
-and the fused call give the same bytes with pacing off, at the default
+T=16384 (more tokens than one round of waves: launched in paced chunks) the
+dispatch and the fused call give the same bytes with pacing off, at the default
 rates, far below what the memory sustains and far above it, and the default
 run matches the oracle. Also the setter's argument checks."""
 import numpy as np
@@ -42,7 +42,7 @@ def _run(epx, inp, fused, fp8, bufs, lay_buf, ws):
 @pytest.mark.parametrize("cfg,fused,fp8", [
     (3, False, False), (3, False, True), (3, True, False), (3, True, True),
     (4, False, False),   # skewed routing
-    (5, False, True),    # T = 16384: more tokens than one round of waves (left unpaced)
+    (5, False, True),    # T = 16384: more tokens than one round, launched in paced chunks
 ])
 def test_sweep_rate_does_not_change_outputs(cfg, fused, fp8):
     import combine_get_dispatch_counts_amd as epx
@@ -86,8 +86,8 @@ def test_sweep_rate_does_not_change_outputs(cfg, fused, fp8):
 
 def test_sweep_rate_receive_permute():
     """The receiver's permute of the prefill's 29 811 rank-major rows into 8
-    local experts (more rows than one round of waves) stores the same bytes
-    whatever the sweep rate."""
+    local experts (the permute alone, which is left unpaced) stores the same
+    bytes whatever the sweep rate."""
     import combine_get_dispatch_counts_amd as epx
 
     inp = synth.make_inputs(3)
