@@ -94,10 +94,13 @@ const char *epx_strerror(int code);
  * at 9/10 of the rate. The permute alone (epx_dispatch with send_x = NULL),
  * which reads as many rows as it writes, is not paced. A rate above what the memory sustains lets the front
  * spread back toward random order (in one launch measured no slower than
- * unpaced); a lower one leaves bandwidth idle. Defaults, measured on MI355X:
- * 6200 (bf16) and 6000 (FP8). The setting is per context and read at each
- * call. EPX_EINVAL for a NULL context or a rate outside
- * [0, EPX_MAX_SWEEP_GBPS]. */
+ * unpaced); a lower one leaves bandwidth idle. Pacing assumes the launch has
+ * the device's compute units to itself: with kernels of other streams
+ * running alongside, some waves may find no place until paced waves end,
+ * and the call can take up to about twice as long (set the rates to 0 for
+ * such use). Defaults, measured on MI355X: 6200 (bf16) and 6000 (FP8). The
+ * setting is per context and read at each call. EPX_EINVAL for a NULL
+ * context or a rate outside [0, EPX_MAX_SWEEP_GBPS]. */
 int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps);
 
 /* Workspace bytes epx_get_dispatch_layout needs for (T, K, E, R) (host out):
