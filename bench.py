@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 # rates of the dispatch's paced store sweep, bf16 and FP8 rows (the library's defaults)
-SWEEP_GBPS = (6200, 6000)
+SWEEP_GBPS = (6300, 6000)
 METRIC = "dispatch+combine µs/layer and HBM GB/s (% peak) at T=4096,h=7168,topk=8"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T4096_traffic.json")
 # each kernel's sources: its measured traffic is reported only while these match

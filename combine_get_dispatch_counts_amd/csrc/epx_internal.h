@@ -19,7 +19,7 @@ namespace epx {
 // Default rates of the paced sweep of the high-throughput dispatch's row
 // stores (GB/s of destination rows), measured on MI355X at the prefill shape:
 // just below the rate at which the paced front outruns the memory system.
-constexpr int kSweepGBpsBf16 = 6200;
+constexpr int kSweepGBpsBf16 = 6300;
 constexpr int kSweepGBpsFp8 = 6000;
 
 // fp32 entries per row of an FP8 scale array for hidden size h: the h/128

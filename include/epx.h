@@ -98,7 +98,7 @@ const char *epx_strerror(int code);
  * the device's compute units to itself: with kernels of other streams
  * running alongside, some waves may find no place until paced waves end,
  * and the call can take up to about twice as long (set the rates to 0 for
- * such use). Defaults, measured on MI355X: 6200 (bf16) and 6000 (FP8). The
+ * such use). Defaults, measured on MI355X: 6300 (bf16) and 6000 (FP8). The
  * setting is per context and read at each call. EPX_EINVAL for a NULL
  * context or a rate outside [0, EPX_MAX_SWEEP_GBPS]. */
 int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps);

@@ -15,7 +15,7 @@ from _gpu import host_bits, say
 
 pytestmark = pytest.mark.gpu
 
-DEFAULTS = (6200, 6000)
+DEFAULTS = (6300, 6000)
 
 
 def _run(epx, inp, fused, fp8, bufs, lay_buf, ws):
