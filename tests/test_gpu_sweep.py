@@ -112,6 +112,53 @@ def test_sweep_rate_receive_permute():
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def test_chunked_dispatch_in_graph():
+    """The FP8 prefill dispatch (T = 16384: several paced chunk launches)
+    captured in a HIP graph and replayed three times, with the outputs
+    scribbled over and unrelated work run between replays: every replay
+    stores what the eager call stored."""
+    import combine_get_dispatch_counts_amd as epx
+
+    inp = synth.make_inputs(5)
+    wl = inp["workload"]
+    T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
+    dev = torch.device("cuda")
+    x = torch.from_numpy(inp["x"].view(np.int16)).cuda().view(torch.bfloat16)
+    tk = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    ws = torch.zeros(epx.workspace_size(T, K, E, R), dtype=torch.uint8, device=dev)
+    lay = epx.get_dispatch_layout(tk, E, R, workspace=ws, out=epx.alloc_layout(T, K, E, R, None, dev))
+    bufs = epx.alloc_dispatch(T, h, K, T * min(K, R), T * K, True, dev)
+    say(f"chunked FP8 dispatch T={T} in a graph")
+    epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs)
+    torch.cuda.synchronize()
+    n_send, n_recv = (int(v) for v in lay.totals.cpu())
+    keys = ["send_x", "send_scales", "recv_x", "recv_scales", "recv_src", "pos_exp"]
+    def used(k):
+        v = bufs[k]
+        return v[:n_send] if k.startswith("send") else v[:n_recv] if k.startswith("recv") else v
+    ref = {k: used(k).clone() for k in keys}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs)
+    for replay in range(3):
+        for k in keys:
+            used(k).view(torch.uint8).fill_(0x5A)
+        torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert epx.get_error() == 0
+        for k in keys:
+            assert torch.equal(used(k).view(torch.uint8), ref[k].view(torch.uint8)), \
+                f"replay {replay}: {k} differs"
+
+
 def test_sweep_rate_argument_checks():
     import combine_get_dispatch_counts_amd as epx
 
