@@ -567,7 +567,12 @@ def main():
                     help="also time a 1 GiB device copy and fill (the same run's ceilings)")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="MALL flush size for the labelled cold-cache figure (0: skip)")
+    ap.add_argument("--sweep-gbps", default=f"{SWEEP_GBPS[0]},{SWEEP_GBPS[1]}",
+                    help="paced store sweep rates 'bf16,fp8' in GB/s (0,0: unpaced)")
     args = ap.parse_args()
+    sweep = tuple(int(v) for v in args.sweep_gbps.split(","))
+    if len(sweep) != 2:
+        raise SystemExit("--sweep-gbps takes two rates: bf16,fp8")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the path; runs on more than one GPU "
               "are not supported (use --gpus 1)", file=sys.stderr)
@@ -581,7 +586,7 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    epx.set_sweep_rate(*SWEEP_GBPS)
+    epx.set_sweep_rate(*sweep)
     inp = synth.make_inputs(3)
     wl = inp["workload"]
     T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
@@ -810,7 +815,7 @@ def main():
         "cold_cache_us_per_layer": round(cold_us, 2) if cold_us else None,
         "graph_us_per_layer": round(graph_us, 2) if graph_us else None,
         "fused_kernel_us": round(fused_us, 2),
-        "sweep_gbps": {"bf16": SWEEP_GBPS[0], "fp8": SWEEP_GBPS[1]},
+        "sweep_gbps": {"bf16": sweep[0], "fp8": sweep[1]},
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("fused_kernel"),
