@@ -7,7 +7,10 @@
 // those loads are in flight, then writes the row to every destination with
 // 16-byte stores: x is read from HBM once and each destination costs exactly
 // one row write. Destination rows live in lanes and are broadcast with
-// readlane, so the kernel needs no LDS and no barrier.
+// readlane, so the kernel needs no LDS and no barrier. The stores follow the
+// paced sweep (dispatch_device.h): in ascending output order, each held until
+// the wall clock reaches its place, so that the many waves' rows reach HBM
+// as one sequential front rather than as random writes.
 //
 // [P2] "DeepEP 学习笔记" (DeepEP study notes), "dispatch 过程": a token goes,
 // in token order, to every rank is_token_in_rank marks, together with its

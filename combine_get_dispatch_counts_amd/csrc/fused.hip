@@ -44,7 +44,10 @@
 // launches, whose 64-thread dispatch blocks spread one wave per token over
 // the chip and free their place wave by wave. Every block issues its
 // counting loads, then its rows' loads, before it waits, so the loads
-// overlap the hand-over. Every wait is bounded.
+// overlap the hand-over. Every wait is bounded. Each wave then stores its
+// token's rows on the paced sweep (dispatch_device.h), its schedule starting
+// when its block's hand-over is complete (a shared start time was measured:
+// the rows due before most blocks are ready go out as one random burst).
 #include <atomic>
 
 #include "dispatch_device.h"
