@@ -322,12 +322,18 @@ __device__ __forceinline__ void scatter(Row &row, const Dests &d, const uint16_t
             else
                 row.store(static_cast<char *>(a_x) + (size_t)r * row_bytes, i0, nvec);
         }
-        // receive rows, smallest first (skipped rows, -1, sort last)
+        // receive rows, smallest first when paced (skipped rows, -1, sort
+        // last), else in top-k order
         const int key = ((d.vbits >> lane) & 1ull) ? (d.recv_row < 0 ? INT32_MAX - 1 : d.recv_row)
                                                    : INT32_MAX;
         for (uint64_t m = d.vbits; m;) {
-            const int kmin = wave_min(((m >> lane) & 1ull) ? key : INT32_MAX);
-            const int k = __builtin_ctzll(m & uniform64(__ballot(key == kmin)));
+            int k;
+            if (sw.bpt) {
+                const int kmin = wave_min(((m >> lane) & 1ull) ? key : INT32_MAX);
+                k = __builtin_ctzll(m & uniform64(__ballot(key == kmin)));
+            } else {
+                k = __builtin_ctzll(m);
+            }
             m &= ~(1ull << k);
             const int r = readlane(d.recv_row, k);
             if (r < 0)

@@ -266,6 +266,11 @@ static int dispatch_args(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *
     a.sweep_bpt = ctx->wclk_khz > 0 ? (uint32_t)(gbps * 1000000 / ctx->wclk_khz) : 0u;
     if (gbps > 0 && a.sweep_bpt == 0)
         a.sweep_bpt = 1;
+    // at most T*min(K,R) send rows and T*K receive rows
+    const int64_t row_bytes = fp8 ? (int64_t)h + 4 * (int64_t)epx::scale_stride(h) : 2 * (int64_t)h;
+    if ((int64_t)T * (K + (K < R ? K : R)) * row_bytes <=
+        (fp8 ? epx::kSweepMinBytesFp8 : epx::kSweepMinBytesBf16))
+        a.sweep_bpt = 0;
     return EPX_OK;
 }
 

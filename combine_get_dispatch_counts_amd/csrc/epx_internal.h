@@ -21,6 +21,17 @@ namespace epx {
 // just below the rate at which the paced front outruns the memory system.
 constexpr int kSweepGBpsBf16 = 6300;
 constexpr int kSweepGBpsFp8 = 6000;
+// Pacing delays every wave from its own start, which costs a few
+// microseconds; it repays that only once the rows no longer fit in the
+// memory-side cache (256 MiB on MI355X) and must reach HBM within the launch.
+// Calls whose row bound (T*(K + min(K,R)) rows) is at most this many bytes are
+// left unpaced. Measured at h = 7168, E = 256, R = 32, top-8: bf16 loses with
+// pacing up to T = 1024 (235 MB bound: 39.3 us against 36.7) and gains from
+// T = 1536 (352 MB: 57.7 against 61.7); FP8, whose quantisation keeps its
+// unpaced store rate lower, is level at T = 1024 (122 MB) and gains from
+// T = 1536 (182 MB: 42.3 against 43.4; 243 MB: 50.6 against 55.4).
+constexpr int64_t kSweepMinBytesBf16 = 256ll << 20;
+constexpr int64_t kSweepMinBytesFp8 = 128ll << 20;
 
 // fp32 entries per row of an FP8 scale array for hidden size h: the h/128
 // group scales rounded up to a multiple of 32, so every row is a whole

@@ -92,7 +92,10 @@ const char *epx_strerror(int code);
  * routing order arrive as random writes. A larger epx_dispatch is launched
  * as chunks of consecutive tokens that each fit, each sweeping its own rows
  * at 9/10 of the rate. The permute alone (epx_dispatch with send_x = NULL),
- * which reads as many rows as it writes, is not paced. A rate above what the memory sustains lets the front
+ * which reads as many rows as it writes, is not paced, nor is a call whose
+ * row bound (T*(K + min(K,R)) rows) is at most 256 MiB for bf16 or 128 MiB
+ * for FP8: such rows mostly stay in the memory-side cache during the launch,
+ * and the pacing delay would cost more than the ordering saves. A rate above what the memory sustains lets the front
  * spread back toward random order (in one launch measured no slower than
  * unpaced); a lower one leaves bandwidth idle. Pacing assumes the launch has
  * the device's compute units to itself: with kernels of other streams
