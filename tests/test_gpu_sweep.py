@@ -4,7 +4,8 @@ workload (T=8192: every wave slot of the device) and the FP8 prefill at
 T=16384 (more tokens than one round of waves: launched in paced chunks) the
 dispatch and the fused call give the same bytes with pacing off, at the default
 rates, far below what the memory sustains and far above it, and the default
-run matches the oracle. Also the setter's argument checks."""
+run matches the oracle; so do dispatches just below and just above the size
+under which pacing is skipped. Also the setter's argument checks."""
 import numpy as np
 import pytest
 import torch
@@ -45,9 +46,24 @@ def _run(epx, inp, fused, fp8, bufs, lay_buf, ws):
     (5, False, True),    # T = 16384: more tokens than one round, launched in paced chunks
 ])
 def test_sweep_rate_does_not_change_outputs(cfg, fused, fp8):
+    _check_rates(cfg, fused, fp8)
+
+
+@pytest.mark.parametrize("T,fp8", [
+    (1024, False), (1280, False),   # row bound 235 MB (left unpaced) / 294 MB (paced)
+    (1024, True), (1152, True),     # FP8: 122 MB (left unpaced) / 137 MB (paced)
+])
+def test_sweep_size_threshold_edges(T, fp8):
+    """Dispatches on either side of the size below which pacing is skipped
+    (prefill shapes with fewer tokens): the same bytes at every rate, and the
+    oracle's."""
+    _check_rates(3, False, fp8, T)
+
+
+def _check_rates(cfg, fused, fp8, T_override=None):
     import combine_get_dispatch_counts_amd as epx
 
-    inp = synth.make_inputs(cfg)
+    inp = synth.make_inputs(cfg, T=T_override)
     wl = inp["workload"]
     T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
     if fused:
@@ -59,7 +75,7 @@ def test_sweep_rate_does_not_change_outputs(cfg, fused, fp8):
     runs = {}
     try:
         for rate in (DEFAULTS, (0, 0), (1500, 1500), (60000, 60000)):
-            say(f"config {cfg} {'fused' if fused else 'dispatch'} fp8={fp8} sweep rate {rate}")
+            say(f"config {cfg} T={T} {'fused' if fused else 'dispatch'} fp8={fp8} sweep rate {rate}")
             epx.set_sweep_rate(*rate)
             runs[rate] = _run(epx, inp, fused, fp8, bufs, lay_buf, ws)
     finally:
