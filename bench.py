@@ -11,10 +11,18 @@ worst-case capacity, so the timed region holds no host wait and no
 allocation. Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. ``value`` is HBM GB/s over the compulsory bytes of the
-step (each required input read once, each required output written once);
-``ms_per_step`` is the wall time per step. ``roofline`` covers the dominant
-kernel (the fused layout + dispatch) timed with HIP events on its stream; ``cpu_baseline``
-times the CPU oracle (single thread) on the same workload.
+step (each required input read once, each required output written once) in
+the step's median time: each of the K timed steps runs right after a 512 MB
+read that flushes the memory-side cache (outside its HIP events), and the
+median of the K event-timed steps is ``ms_per_step`` / ``us_per_layer``; the
+same K steps launched back to back with no flush are reported as
+``warm_us_per_layer``. The sweep rates of the paced dispatch come from a
+calibration against this GPU's own fill rate (``--sweep-gbps`` sets them
+instead), and the step at the library's hand-tuned defaults is reported
+beside it. ``roofline`` covers the dominant kernel (the fused layout +
+dispatch) timed with HIP events on its stream; ``cpu_baseline`` times the
+CPU oracle on the same workload, single-threaded and with its token-parallel
+phases on the host's cores.
 
 ``python bench.py --summarize-profiles <folder>`` instead writes the
 profiles/ summaries from the rocprofv3 runs listed in PROFILE_RUNS.
@@ -33,8 +41,6 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# rates of the dispatch's paced store sweep, bf16 and FP8 rows (the library's defaults)
-SWEEP_GBPS = (6300, 6000)
 METRIC = "dispatch+combine µs/layer and HBM GB/s (% peak) at T=4096,h=7168,topk=8"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T4096_traffic.json")
 # each kernel's sources: its measured traffic is reported only while these match
@@ -103,9 +109,11 @@ def compulsory_step_bytes(T, h, K, R, n_rank, n_exp):
     return disp + comb
 
 
-def cpu_baseline(inp, wl, target_s=12.0, max_reps=5):
-    """Time the oracle (single-threaded C) on the same workload: layout,
-    dispatch and combine, repeated until about `target_s` seconds of work."""
+def cpu_baseline(inp, wl, target_s=12.0, max_reps=5, threads=1):
+    """Time the oracle on the same workload: layout, dispatch and combine,
+    repeated until about `target_s` seconds of work. threads > 1 runs the
+    dispatch's and the combine's token ranges side by side (the counting and
+    the scans of the layout stay sequential)."""
     import numpy as np
 
     import oracle
@@ -117,14 +125,34 @@ def cpu_baseline(inp, wl, target_s=12.0, max_reps=5):
     while len(times) < max_reps:
         t0 = time.perf_counter()
         lay = oracle.layout(inp["topk_idx"], wl.E, wl.R)
-        d = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, lay=lay)
-        oracle.combine(y[: int(lay["totals"][1])], inp["topk_w"], d["pos_exp"])
+        d = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, lay=lay,
+                            threads=threads)
+        oracle.combine(y[: int(lay["totals"][1])], inp["topk_w"], d["pos_exp"], threads=threads)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > target_s:
             break
     n_rank, n_exp = (int(v) for v in lay["totals"])
     med = statistics.median(times)
     return med, n_rank, n_exp, len(times)
+
+
+def cpu_baseline_record(inp, wl):
+    """The oracle timed on the host beside the GPU run: single-threaded (the
+    sequential definition the parity tests use), and with its token-parallel
+    phases split over the host cores this process may use (at most 16)."""
+    T, h, K, R = wl.T, wl.h, wl.K, wl.R
+    med, nr, ne, reps = cpu_baseline(inp, wl)
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    med_t, _, _, reps_t = cpu_baseline(inp, wl, target_s=6.0, threads=cores)
+    b = compulsory_step_bytes(T, h, K, R, nr, ne)
+    return {"value": round(b / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full prefill workload (T={T}, one layer: layout+dispatch+combine), "
+                      f"median of {reps} single-threaded runs, {med * 1e3:.0f} ms each",
+            "threaded": {"value": round(b / med_t / 1e9, 3), "unit": "GB/s", "cores": cores,
+                         "kind": "oracle, token ranges of the dispatch and combine on "
+                                 f"{cores} threads, layout sequential",
+                         "sample": f"the same workload, median of {reps_t} runs, "
+                                   f"{med_t * 1e3:.0f} ms each"}}
 
 
 def _loop_us(fn, n):
@@ -281,6 +309,15 @@ def other_workloads(n=20):
         n_rows = T * K
         ll_bytes = T * 2 * h + 8 * T * K + n_rows * (row8 + 4) + 4 * T * K + 4 * E
         entry = {"ll_dispatch_fp8": rec(ll_us, ll_bytes)}
+        # buffer fill of this source's regions, from the kernel's own counts
+        # (entries routed over E*cap slots, and the fullest region over cap)
+        stats = torch.zeros(2, dtype=torch.int32, device=dev)
+        epx.ll_dispatch(x, tk, E, R, 0, cap, R_buf, True, buf, stats=stats)
+        routed, fullest = (int(v) for v in stats.cpu())
+        entry["buffer_fill"] = {"entries_routed": routed, "slots": E * cap,
+                                "utilisation": round(routed / (E * cap), 4),
+                                "fullest_region": fullest,
+                                "peak_region_fill": round(fullest / cap, 4)}
         if R_buf == 1:
             y = synth.expert_outputs(E * cap, h, seed=19, device="cuda")
             comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
@@ -549,6 +586,26 @@ def summarize_profiles(folder: str, calib_mb: int = 1024) -> None:
         f"{k} traffic {v['bytes_per_launch'] / 1e6:.1f} MB" for k, v in recs.items()))
 
 
+def _flushed_steps(fn, n, flush, nev):
+    """Per-step GPU time (us) of fn over n steps, each preceded by `flush`
+    (outside the timed events); fn(ev) records its own events ev[0..nev-1]
+    around the kernel groups. Returns the list of per-step event lists."""
+    import torch
+
+    evs = []
+    for i in range(n):
+        flush(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+        fn(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    return evs
+
+
+def _median_us(evs, a=0, b=-1):
+    return statistics.median(e[a].elapsed_time(e[b]) * 1e3 for e in evs)
+
+
 def main():
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
         summarize_profiles(sys.argv[2])
@@ -566,13 +623,15 @@ def main():
     ap.add_argument("--ceilings", type=int, default=1,
                     help="also time a 1 GiB device copy and fill (the same run's ceilings)")
     ap.add_argument("--flush-mb", type=int, default=512,
-                    help="MALL flush size for the labelled cold-cache figure (0: skip)")
-    ap.add_argument("--sweep-gbps", default=f"{SWEEP_GBPS[0]},{SWEEP_GBPS[1]}",
-                    help="paced store sweep rates 'bf16,fp8' in GB/s (0,0: unpaced)")
+                    help="MALL flush: a read of this many MB before every timed step (0: none)")
+    ap.add_argument("--sweep-gbps", default="calibrate",
+                    help="paced store sweep rates: 'calibrate' (from a fill of this GPU), "
+                         "'bf16,fp8' in GB/s, or 0,0 (unpaced)")
     args = ap.parse_args()
-    sweep = tuple(int(v) for v in args.sweep_gbps.split(","))
-    if len(sweep) != 2:
-        raise SystemExit("--sweep-gbps takes two rates: bf16,fp8")
+    if args.sweep_gbps != "calibrate":
+        sweep = tuple(int(v) for v in args.sweep_gbps.split(","))
+        if len(sweep) != 2:
+            raise SystemExit("--sweep-gbps takes 'calibrate' or two rates: bf16,fp8")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the path; runs on more than one GPU "
               "are not supported (use --gpus 1)", file=sys.stderr)
@@ -586,7 +645,15 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    epx.set_sweep_rate(*sweep)
+    default_rates = epx.get_sweep_rate()
+    fill_gbps = None
+    if args.sweep_gbps == "calibrate":
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        fill_gbps = epx.calibrate_sweep_rate(scratch)
+        del scratch
+        sweep = epx.get_sweep_rate()
+    else:
+        epx.set_sweep_rate(*sweep)
     inp = synth.make_inputs(3)
     wl = inp["workload"]
     T, h, E, R, K = wl.T, wl.h, wl.E, wl.R, wl.K
@@ -646,38 +713,46 @@ def main():
     assert epx.get_error() == 0
     n_rank, n_exp = (int(v) for v in lay.totals.cpu())
 
-    # timed region: K back-to-back steps, nothing else on the stream
+    # The MALL flush: a read of flush_mb MB (a reduction over a scratch
+    # buffer) before each timed step, outside its events; a read leaves the
+    # cache holding clean lines only, so nothing is written back inside the
+    # step.
+    if args.flush_mb > 0:
+        flush_buf = torch.ones(args.flush_mb << 20, dtype=torch.uint8, device=dev).view(torch.int32)
+
+        def flush(i):
+            flush_buf.sum()
+    else:
+        def flush(i):
+            pass
+
+    # timed region: K steps bracketed by synchronisations, each step timed
+    # with HIP events on its stream after a flush; the headline is the median
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    evs = _flushed_steps(step, args.steps, flush, 3)
+    wall_s = time.perf_counter() - t0
+    us_step = _median_us(evs)
+    phase = {"layout+dispatch": _median_us(evs, 0, 1), "combine": _median_us(evs, 1, 2)}
+    assert epx.get_error() == 0
+    evs2 = _flushed_steps(step_two, args.steps, flush, 4)
+    two_us = _median_us(evs2)
+    phase_two = {"layout": _median_us(evs2, 0, 1), "dispatch": _median_us(evs2, 1, 2),
+                 "combine": _median_us(evs2, 2, 3)}
     assert epx.get_error() == 0
 
-    # the two-launch form of the same step, timed the same way
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step_two()
-    torch.cuda.synchronize()
-    two_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    assert epx.get_error() == 0
+    # the warm figure: K steps back to back, nothing else on the stream
+    # (no flush: the MALL keeps what the previous step left), wall time / K
+    def warm(fn):
+        torch.cuda.synchronize()
+        tw = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - tw) * 1e6 / args.steps
 
-    # per-phase split, from separate steps with events between the kernel groups
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    phase = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3
-             for j, name in enumerate(["layout+dispatch", "combine"])}
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step_two(evs[i])
-    torch.cuda.synchronize()
-    phase_two = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3
-                 for j, name in enumerate(["layout", "dispatch", "combine"])}
+    warm_us, warm_two_us = warm(step), warm(step_two)
+    assert epx.get_error() == 0
 
     # the dominant kernels on their own, launched back to back on the step's
     # stream (both are idempotent), one event pair around them all
@@ -696,7 +771,18 @@ def main():
         lambda: epx.dispatch_fused(x, tk, w, E, R, layout=lay_buf, out=bufs, workspace=fws))
     lay = epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay_buf)
     dispatch_us = back_to_back_us(lambda: epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs))
+    layout_us = back_to_back_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws,
+                                                                out=lay_buf))
     assert epx.get_error() == 0
+
+    # the same step at the hand-tuned default rates, for comparison with the
+    # calibrated ones (flushed median, as the headline)
+    hand = None
+    if args.sweep_gbps == "calibrate":
+        epx.set_sweep_rate(*default_rates)
+        hand = {"bf16": default_rates[0], "fp8": default_rates[1],
+                "us_per_layer": round(_median_us(_flushed_steps(step, args.steps, flush, 3)), 2)}
+        epx.set_sweep_rate(*sweep)
 
     # the step captured in a HIP graph (GRAPH_STEPS steps per graph, as a
     # model's graph holds several layers) and replayed, no host launch work
@@ -726,20 +812,8 @@ def main():
         torch.cuda.synchronize()
         graph_us = (time.perf_counter() - tg0) * 1e6 / (reps * GRAPH_STEPS)
         del g, ref_out
-
-    # labelled cold-cache figure: flush the 256 MB MALL before each step
-    cold_us = None
     if args.flush_mb > 0:
-        scratch = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
-        cold = []
-        for i in range(min(args.steps, 20)):
-            scratch.fill_(i & 0xFF)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            step(e)
-            torch.cuda.synchronize()
-            cold.append(e[0].elapsed_time(e[-1]) * 1e3)
-        cold_us = statistics.median(cold)
-        del scratch
+        del flush_buf
 
     # copy and fill ceilings of this GPU in the same run (1 GiB each)
     ceil = {}
@@ -755,11 +829,12 @@ def main():
         ai, bi = a.view(torch.int32), b.view(torch.int32)
         ceil["rw_kernel_gbs"] = round(
             2 * (1 << 30) / (_loop_us(lambda: torch.add(ai, 0, out=bi), 10) * 1e3), 1)
+        ceil["read_gbs"] = round((1 << 30) / (_loop_us(lambda: ai.sum(), 10) * 1e3), 1)
         del a, b, ai, bi
 
     by = step_bytes(T, h, K, R, n_rank, n_exp)
     bmin = compulsory_step_bytes(T, h, K, R, n_rank, n_exp)
-    gbs = bmin / (ms_per_step * 1e-3) / 1e9
+    gbs = bmin / (us_step * 1e-6) / 1e9
     fused_bytes = by["layout"] + by["dispatch"]
     fused_gbs = fused_bytes / (fused_us * 1e-6) / 1e9
     disp_gbs = by["dispatch"] / (dispatch_us * 1e-6) / 1e9
@@ -774,11 +849,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        med, nr, ne, reps = cpu_baseline(inp, wl)
-        cpu = {"value": round(compulsory_step_bytes(T, h, K, R, nr, ne) / med / 1e9, 3), "unit": "GB/s",
-               "cores": 1, "kind": "oracle",
-               "sample": f"the full prefill workload (T={T}, one layer: layout+dispatch+combine), "
-                         f"median of {reps} single-threaded runs, {med * 1e3:.0f} ms each"}
+        cpu = cpu_baseline_record(inp, wl)
 
     rec = {
         "metric": METRIC,
@@ -787,7 +858,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(us_step * 1e-3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -797,25 +868,34 @@ def main():
                                "high-throughput layout+dispatch (one launch) + combine",
                    "T": T, "hidden": h, "num_experts": E, "num_ranks": R, "topk": K,
                    "n_rank_rows": n_rank, "n_expert_rows": n_exp},
-        "us_per_layer": round(ms_per_step * 1e3, 2),
+        "timing": f"median over {args.steps} steps of HIP-event step time, the "
+                  f"{args.flush_mb} MB memory-side cache flushed by a read before each step "
+                  "(outside the events); timed loop wall time "
+                  f"{wall_s * 1e3:.1f} ms including the flushes",
+        "us_per_layer": round(us_step, 2),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "warm_us_per_layer": round(warm_us, 2),
+        "warm_frac_of_hbm_peak": round(bmin / (warm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "b_min_bytes": bmin,
-        "b_flow_gbs": round(b_flow / (ms_per_step * 1e-3) / 1e9, 1),
+        "b_flow_gbs": round(b_flow / (us_step * 1e-6) / 1e9, 1),
         "phase_us": {k: round(v, 2) for k, v in phase.items()},
         "phase_gbs": {"layout+dispatch": round(fused_gbs, 1), "combine": round(comb_gbs, 1)},
-        "two_launch": {"us_per_layer": round(two_ms * 1e3, 2),
-                       "value": round(bmin / (two_ms * 1e-3) / 1e9, 1),
+        "two_launch": {"us_per_layer": round(two_us, 2),
+                       "value": round(bmin / (two_us * 1e-6) / 1e9, 1),
+                       "warm_us_per_layer": round(warm_two_us, 2),
                        "phase_us": {k: round(v, 2) for k, v in phase_two.items()},
+                       "layout_kernel_us": round(layout_us, 2),
                        "dispatch_kernel_us": round(dispatch_us, 2),
                        "dispatch_gbs": round(disp_gbs, 1),
                        "dispatch_traffic": measured_traffic("dispatch_kernel")},
         "ceilings": ceil or None,
         "frac_of_copy_ceiling": round(gbs / ceil["d2d_copy_gbs"], 4) if ceil else None,
         "frac_of_rw_kernel_ceiling": round(gbs / ceil["rw_kernel_gbs"], 4) if ceil else None,
-        "cold_cache_us_per_layer": round(cold_us, 2) if cold_us else None,
         "graph_us_per_layer": round(graph_us, 2) if graph_us else None,
         "fused_kernel_us": round(fused_us, 2),
-        "sweep_gbps": {"bf16": sweep[0], "fp8": sweep[1]},
+        "sweep_gbps": {"mode": "calibrated" if fill_gbps else "set", "bf16": sweep[0],
+                       "fp8": sweep[1], "calibration_fill_gbps": fill_gbps},
+        "hand_tuned_rates": hand,
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("fused_kernel"),

@@ -16,6 +16,7 @@ from .api import (  # noqa: E402
     alloc_dispatch,
     alloc_layout,
     alloc_ll,
+    calibrate_sweep_rate,
     combine,
     combine_final,
     combine_partial,
@@ -25,6 +26,7 @@ from .api import (  # noqa: E402
     fused_workspace_size,
     get_dispatch_layout,
     get_error,
+    get_sweep_rate,
     ll_dispatch,
     ll_reset,
     ll_size_hint,
@@ -39,4 +41,5 @@ __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
            "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
-           "fused_launches", "dispatch_fused", "set_sweep_rate"]
+           "fused_launches", "dispatch_fused", "set_sweep_rate", "get_sweep_rate",
+           "calibrate_sweep_rate"]

@@ -25,6 +25,8 @@ SIGNATURES = {
     "epx_destroy": (_I, [_P]),
     "epx_strerror": (ctypes.c_char_p, [_I]),
     "epx_set_sweep_rate": (_I, [_P, _I, _I]),
+    "epx_get_sweep_rate": (_I, [_P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "epx_calibrate_sweep_rate": (_I, [_P, _P, _SZ, ctypes.POINTER(_I), _P]),
     "epx_workspace_size": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "epx_ll_size_hint": (_SZ, [_I, _I, _I, _I, _I]),
     "epx_scale_stride": (_I, [_I]),

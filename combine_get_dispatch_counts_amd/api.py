@@ -138,6 +138,30 @@ def set_sweep_rate(bf16_gbps: int, fp8_gbps: int, device: torch.device | None = 
           "epx_set_sweep_rate")
 
 
+def get_sweep_rate(device: torch.device | None = None) -> tuple[int, int]:
+    """The context's current sweep rates (bf16, FP8) in GB/s."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    b, f = ctypes.c_int(), ctypes.c_int()
+    check(_lib.load().epx_get_sweep_rate(_ctx(device), ctypes.byref(b), ctypes.byref(f)),
+          "epx_get_sweep_rate")
+    return b.value, f.value
+
+
+def calibrate_sweep_rate(scratch: torch.Tensor) -> int:
+    """Set the sweep rates from a fill of ``scratch`` (a contiguous GPU tensor
+    of at least 512 MiB, overwritten) timed on the current stream; waits for
+    the stream. Returns the measured fill rate in GB/s."""
+    if not scratch.is_cuda or not scratch.is_contiguous():
+        raise ValueError("scratch must be a contiguous GPU tensor")
+    dev = scratch.device
+    fill = ctypes.c_int()
+    check(_lib.load().epx_calibrate_sweep_rate(_ctx(dev), _p(scratch),
+                                               scratch.numel() * scratch.element_size(),
+                                               ctypes.byref(fill), _stream(dev)),
+          "epx_calibrate_sweep_rate")
+    return fill.value
+
+
 def get_error(device: torch.device | None = None) -> int:
     """Synchronise the current stream, return and clear the device error bits."""
     device = device or torch.device("cuda", torch.cuda.current_device())
@@ -548,6 +572,8 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
-           "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
+           "dispatch", "combine", "combine_partial",
+           "combine_final", "ll_reset", "alloc_ll",
            "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
-           "fused_launches", "dispatch_fused", "set_sweep_rate"]
+           "fused_launches", "dispatch_fused", "set_sweep_rate", "get_sweep_rate",
+           "calibrate_sweep_rate"]

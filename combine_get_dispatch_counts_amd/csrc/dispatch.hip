@@ -33,8 +33,11 @@ namespace {
 template <bool FP8, int NV, bool CHUNKED>
 __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
 {
+    const uint64_t t_entry = wall_clock64();
     const int t = CHUNKED ? a.t_begin + (int)blockIdx.x : (int)blockIdx.x;
     const int lane = threadIdx.x;
+    if (blockIdx.x == 0 && lane == 0)
+        stamp_launch(a, t_entry);
     const int64_t tk = (int64_t)t * a.K;
     const uint16_t *xrow = a.x + (size_t)t * a.h;
 
@@ -55,27 +58,43 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
     if (valid)
         recv_r = (int64_t)a.exp_off[(int)e] + a.slot_in_expert[tk + lane];
     const int64_t nsend = (a.sweep_bpt && a.send_x) ? a.rank_off[a.R] : 0;
-    dispatch_token<FP8, CHUNKED>(a, t, row, xrow, e, send_r, recv_r, nsend);
+    dispatch_token<FP8, CHUNKED>(a, t, row, xrow, e, send_r, recv_r, nsend, t_entry);
 }
 
-// Low-latency dispatch, one launch. Block t handles token t with kLLWaves
-// waves: together they histogram all T*K entries in LDS (decode batches are
-// small) -- the full histogram gives the count slots, the part before token
-// t gives t's slots; LDS atomics only add, so the result does not depend on
-// their order. The row is cut into 1024-channel slices (eight 128-channel
-// scale groups): wave w loads, quantises and stores slices w, w + kLLWaves,
-// .. to every destination of the token, so the row is read once, each
-// element is quantised once, and a decode batch's few tokens still spread
-// their work over many waves.
+// Low-latency dispatch, one launch. Block b handles G consecutive tokens
+// (G = 1 for decode batches up to 256 tokens, doubling with T up to 8, so
+// the grid stays near one block per compute unit) with kLLWaves waves, 8/G
+// per token. Every block histograms all T*K entries in LDS -- the full
+// histogram gives the count slots, the part before the block's first token
+// gives its slots, and the block's own earlier tokens (their entries kept
+// in LDS) the rest; LDS atomics only add, so the result does not depend on
+// their order, and the total counting work is (blocks) x T*K, linear in T
+// up to T = 8 x 256. The row is cut into 1024-channel slices (eight
+// 128-channel scale groups): a token's waves load, quantise and store its
+// slices in turn to every destination of the token, so the row is read
+// once, each element is quantised once, and a decode batch's few tokens
+// still spread their work over many waves.
 constexpr int kLLWaves = 8;
 
-template <bool FP8>
-__global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
+// Tokens per block of the low-latency kernel for a batch of T tokens.
+inline int ll_tokens_per_block(int T)
 {
-    extern __shared__ int hist[];  // [E] all entries, [E] entries before token t
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+    int g = 1;
+    while (g < kLLWaves && (int64_t)g * 256 < T)
+        g <<= 1;
+    return g;
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a, int G)
+{
+    extern __shared__ int hist[];  // [E] all entries, [E] entries before the block's tokens,
+                                   // [G][K] the experts of the block's tokens
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
     const int nthreads = kLLWaves * kWave;
-    int *hist_all = hist, *hist_before = hist + a.E;
+    const int wpt = kLLWaves / G, j = w / wpt, wj = w - j * wpt;  // waves per token, token, wave of it
+    const int t0 = blockIdx.x * G, t = t0 + j;
+    int *hist_all = hist, *hist_before = hist + a.E, *blk_e = hist + 2 * a.E;
     const bool have_token = t < a.T;
     const int64_t tk = (int64_t)t * a.K;
     const uint16_t *xrow = a.x + (size_t)(have_token ? t : 0) * a.h;
@@ -88,24 +107,26 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
     constexpr int per = decltype(row)::kPerPass;  // 1024 channels
     const int nitems = FP8 ? a.h >> 4 : a.h >> 3;
     const int nslices = (nitems + per - 1) / per;
-    if (have_token && w < nslices)
-        row.load(src, w * per, nitems);
+    if (have_token && wj < nslices)
+        row.load(src, wj * per, nitems);
 
     for (int i = tid; i < 2 * a.E; i += nthreads)
         hist[i] = 0;
+    if (wj == 0 && lane < a.K)
+        blk_e[j * a.K + lane] = (int)ek;  // -1 past the last token
     __syncthreads();
-    const int64_t n_ent = (int64_t)a.T * a.K;
+    const int64_t n_ent = (int64_t)a.T * a.K, before = (int64_t)t0 * a.K;
     for (int64_t i = tid; i < n_ent; i += nthreads) {
         const int64_t e = a.topk_idx[i];
         if (e == -1)
             continue;
         if (e < 0 || e >= a.E) {
-            if (t == 0)
+            if (blockIdx.x == 0)
                 flag_error(a.err, EPX_DEV_BAD_ROUTE);
             continue;
         }
         atomicAdd(&hist_all[e], 1);
-        if (i < tk)
+        if (i < before)
             atomicAdd(&hist_before[e], 1);
     }
     __syncthreads();
@@ -140,23 +161,27 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
     if (!have_token)
         return;
 
-    // the token's rows, lane k < K holding entry k's (the same in every
-    // wave); wave 0 writes the handle and the source index
+    // the token's rows, lane k < K holding entry k's (the same in the
+    // token's every wave); its first wave writes the handle and the source
+    // index. Slot = entries before the block + entries of the block's
+    // earlier tokens + earlier entries of this row, with the same expert.
     const bool valid = lane < a.K && ek >= 0 && ek < a.E;
-    int rep = 0;  // earlier entries of this row with the same expert
+    int rep = 0;
     for (int k2 = 0; k2 < a.K; ++k2)
         rep += (k2 < lane && readlane64(ek, k2) == ek);
+    for (int i = 0; i < j * a.K; ++i)
+        rep += (blk_e[i] == (int)ek);
     int dst = -1;
     if (valid) {
         const int slot = hist_before[ek] + rep;
         if (slot < a.cap) {
             const int64_t region = a.R_buf == 1 ? ek : ek * a.R + a.src_rank;
             dst = (int)(region * a.cap + slot);
-        } else if (w == 0) {
+        } else if (wj == 0) {
             flag_error(a.err, EPX_DEV_OVERFLOW);
         }
     }
-    if (w == 0 && lane < a.K) {
+    if (wj == 0 && lane < a.K) {
         a.pos_ll[tk + lane] = dst;
         if (dst >= 0)
             a.ll_src[dst] = t;
@@ -164,8 +189,8 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
     const uint64_t dbits = uniform64(__ballot(dst >= 0));
     const size_t row_bytes = FP8 ? (size_t)a.h : (size_t)a.h * 2;
     const int ld_s = scale_stride(a.h);
-    for (int sl = w; sl < nslices; sl += kLLWaves) {
-        if (sl != w)
+    for (int sl = wj; sl < nslices; sl += wpt) {
+        if (sl != wj)
             row.load(src, sl * per, nitems);
         row.quantise(sl * per, nitems);
         for (uint64_t m = dbits; m; m &= m - 1) {
@@ -178,6 +203,15 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a)
                           nitems);
         }
     }
+}
+
+__global__ __launch_bounds__(256) void fill_lines_kernel(u32x4 *p, uint32_t v)
+{
+    u32x4 *blk = p + (size_t)blockIdx.x * (kFillBlockBytes / 16);
+    const u32x4 val = u32x4{v, v, v, v};
+#pragma unroll
+    for (int j = 0; j < (int)(kFillBlockBytes / 16 / 256); ++j)
+        blk[j * 256 + threadIdx.x] = val;
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
@@ -209,26 +243,41 @@ static int dispatch_blocks_per_cu()
 
 // A paced sweep needs every wave of a launch on the chip at once: a wave
 // held back for a late row keeps its place, so a wave that found no place
-// would wait behind it. Up to one round of waves, one launch paces the
-// whole sweep; beyond, the tokens go in chunks of consecutive tokens, each
-// its own launch sweeping its own rows, sized to 7/8 of the round the
-// occupancy query reports for the chunked kernel (the query has been seen to
-// promise a wave per SIMD more than a kernel got), at 9/10 of the set rate
-// (each chunk's sweep shares HBM with the loads of its own rows; measured
-// on the FP8 prefill, T = 16384 in five chunks: best at 5400 GB/s, slower
-// than unpaced at 6000). Unpaced, or when the query fails, one launch takes
-// all tokens.
+// would wait behind it (such a wave stores unpaced: the late-wave check).
+// Up to one round of waves, one launch paces the whole sweep; beyond, the
+// tokens go in chunks of consecutive tokens, each its own launch sweeping
+// its own rows, sized to the round the occupancy query reports for the
+// chunked kernel, at 9/10 of the set rate (each chunk's sweep shares HBM
+// with the loads of its own rows). Unpaced, or when the query fails, one
+// launch takes all tokens. (One launch of all chunks' waves, each later
+// round's rows due after the estimated rows of the rounds before it on one
+// clock, was measured on the FP8 prefill at 429-450 us, no better than
+// unpaced: a round's waves find places only as the previous round's last
+// rows go out, and the rows due before their loads return go out as one
+// burst that turns the front back into random writes.)
+// Chunk size as a fraction of the round the occupancy query reports (the
+// whole round: a wave that still finds no place is caught by the late-wave
+// check and stores unpaced), and the chunks' sweep rate as a fraction of
+// the set rate. Measured on the FP8 prefill (T = 16384, h = 7168, E = 256,
+// R = 64): four chunks of a full round 402-405 us against 413-414 us for
+// five of 7/8 of it; the best effective chunk rate ~5500 GB/s either way.
+constexpr int64_t kChunkRoundPermille = 1000;
+constexpr int64_t kChunkRatePermille = 900;
+
 template <bool FP8, int NV>
-static void launch_dispatch_nv(const DispatchArgs &a, int cus, hipStream_t stream)
+static void launch_dispatch_nv(const DispatchArgs &a, int cus, std::atomic<unsigned> *seq,
+                               hipStream_t stream)
 {
     DispatchArgs b = a;
     b.t_begin = 0;
     b.t_count = 0;
+    b.stamp_slot = next_stamp_slot(seq);
     if (a.sweep_bpt == 0 || (int64_t)a.T <= (int64_t)dispatch_blocks_per_cu<FP8, NV, false>() * cus) {
         hipLaunchKernelGGL((dispatch_kernel<FP8, NV, false>), dim3(a.T), dim3(kWave), 0, stream, b);
         return;
     }
-    const int64_t round = (int64_t)dispatch_blocks_per_cu<FP8, NV, true>() * cus * 7 / 8;
+    const int64_t round =
+        (int64_t)dispatch_blocks_per_cu<FP8, NV, true>() * cus * kChunkRoundPermille / 1000;
     if (round <= 0) {
         b.sweep_bpt = 0;
         hipLaunchKernelGGL((dispatch_kernel<FP8, NV, false>), dim3(a.T), dim3(kWave), 0, stream, b);
@@ -236,26 +285,30 @@ static void launch_dispatch_nv(const DispatchArgs &a, int cus, hipStream_t strea
     }
     const int64_t nchunk = (a.T + round - 1) / round;
     const int64_t size = (a.T + nchunk - 1) / nchunk;
-    b.sweep_bpt = a.sweep_bpt * 9 / 10 > 0 ? a.sweep_bpt * 9 / 10 : 1;
+    b.sweep_bpt = a.sweep_bpt * kChunkRatePermille / 1000 > 0
+                      ? a.sweep_bpt * kChunkRatePermille / 1000 : 1;
     for (int64_t t0 = 0; t0 < a.T; t0 += size) {
         b.t_begin = (int)t0;
         b.t_count = (int)(a.T - t0 < size ? a.T - t0 : size);
+        if (t0 > 0)
+            b.stamp_slot = next_stamp_slot(seq);
         hipLaunchKernelGGL((dispatch_kernel<FP8, NV, true>), dim3((unsigned)b.t_count), dim3(kWave),
                            0, stream, b);
     }
 }
 
-hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, hipStream_t stream)
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, std::atomic<unsigned> *seq,
+                           hipStream_t stream)
 {
     if (a.T == 0)
         return hipSuccess;
     switch (pick_nv(a.h, fp8) + (fp8 ? 100 : 0)) {
-    case 8: launch_dispatch_nv<false, 8>(a, cus, stream); break;
-    case 14: launch_dispatch_nv<false, 14>(a, cus, stream); break;
-    case 16: launch_dispatch_nv<false, 16>(a, cus, stream); break;
-    case 104: launch_dispatch_nv<true, 4>(a, cus, stream); break;
-    case 107: launch_dispatch_nv<true, 7>(a, cus, stream); break;
-    default: launch_dispatch_nv<true, 8>(a, cus, stream); break;
+    case 8: launch_dispatch_nv<false, 8>(a, cus, seq, stream); break;
+    case 14: launch_dispatch_nv<false, 14>(a, cus, seq, stream); break;
+    case 16: launch_dispatch_nv<false, 16>(a, cus, seq, stream); break;
+    case 104: launch_dispatch_nv<true, 4>(a, cus, seq, stream); break;
+    case 107: launch_dispatch_nv<true, 7>(a, cus, seq, stream); break;
+    default: launch_dispatch_nv<true, 8>(a, cus, seq, stream); break;
     }
     return hipGetLastError();
 }
@@ -263,9 +316,10 @@ hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, hipStream_t
 template <bool FP8>
 static void launch_ll(const LLArgs &a, hipStream_t stream)
 {
-    const dim3 grid(a.T > 0 ? a.T : 1);
-    const size_t lds = sizeof(int) * 2 * (size_t)a.E;
-    hipLaunchKernelGGL((ll_dispatch_kernel<FP8>), grid, dim3(kLLWaves * kWave), lds, stream, a);
+    const int G = ll_tokens_per_block(a.T);
+    const dim3 grid(a.T > 0 ? (a.T + G - 1) / G : 1);
+    const size_t lds = sizeof(int) * (2 * (size_t)a.E + (size_t)G * a.K);
+    hipLaunchKernelGGL((ll_dispatch_kernel<FP8>), grid, dim3(kLLWaves * kWave), lds, stream, a, G);
 }
 
 hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream)
@@ -274,6 +328,18 @@ hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream)
         launch_ll<true>(a, stream);
     else
         launch_ll<false>(a, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_lines(void *p, size_t n, uint32_t v, hipStream_t stream)
+{
+    const size_t blocks = n / kFillBlockBytes;
+    if (blocks == 0)
+        return hipSuccess;
+    if (blocks > 0x7FFFFFFFu)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fill_lines_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<u32x4 *>(p), v);
     return hipGetLastError();
 }
 

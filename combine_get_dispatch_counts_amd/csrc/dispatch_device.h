@@ -97,16 +97,73 @@ __device__ __forceinline__ uint32_t seg_abs_max_bits(const uint32_t (&p)[8])
     return m.x > m.y ? m.x : m.y;
 }
 
+// The e4m3 codes of one 16-channel segment (lo: channels 0..7, hi: 8..15)
+// and the scale of its 128-channel group, whose 8 segments sit on 8 adjacent
+// lanes and are reduced with xor shuffles. Codes: e4m3 of x / s with
+// s = max(amax, 1e-4) / 448 (IEEE), |x / s| <= 448 up to one rounding. A
+// group holding an Inf or NaN takes a separate branch (uniform over the
+// wave, almost never taken) that divides outright: amax over the non-NaN
+// values, NaN quotients coded 0x7F.
+__device__ __forceinline__ void quantise_segment(const u32x4 &lo, const u32x4 &hi, u32x4 &q,
+                                                 float &s)
+{
+    const uint32_t p[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[2 * i] = bf16_lo(p[i]);
+        f[2 * i + 1] = bf16_hi(p[i]);
+    }
+    uint32_t abits = seg_abs_max_bits(p);
+    abits = max(abits, (uint32_t)__shfl_xor((int)abits, 1, kWave));
+    abits = max(abits, (uint32_t)__shfl_xor((int)abits, 2, kWave));
+    abits = max(abits, (uint32_t)__shfl_xor((int)abits, 4, kWave));
+    uint32_t wd[4];
+    if (__builtin_expect(__ballot(abits >= 0x7F80u) == 0, 1)) {
+        s = fmaxf(__uint_as_float(abits << 16), 1e-4f) / 448.0f;
+        const float rs = 1.0f / s;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int w = cvt2_e4m3<false>(quotient(f[4 * j], s, rs),
+                                           quotient(f[4 * j + 1], s, rs), 0);
+            wd[j] = (uint32_t)cvt2_e4m3<true>(quotient(f[4 * j + 2], s, rs),
+                                              quotient(f[4 * j + 3], s, rs), w);
+        }
+    } else {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float a = fabsf(f[i]);
+            amax = (a > amax) ? a : amax;  // a NaN never wins
+        }
+#pragma unroll
+        for (int d = 1; d < 8; d <<= 1) {
+            const float o = __shfl_xor(amax, d, kWave);
+            amax = (o > amax) ? o : amax;
+        }
+        s = fmaxf(amax, 1e-4f) / 448.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float v = f[4 * j + b] / s;
+                const uint32_t c = (v != v) ? 0x7Fu
+                                            : ((uint32_t)cvt2_e4m3<false>(v, 0.0f, 0) & 0xFFu);
+                word |= c << (8 * b);
+            }
+            wd[j] = word;
+        }
+    }
+    q = u32x4{wd[0], wd[1], wd[2], wd[3]};
+}
+
 // One pass of an FP8 row: segment sg = s0 + lane + 64*u covers channels
-// [16 sg, 16 sg + 16); a 128-channel group is 8 adjacent lanes, reduced with
-// xor shuffles. Codes: e4m3 of x / s with s = max(amax, 1e-4) / 448 (IEEE),
-// |x / s| <= 448 up to one rounding. A group holding an Inf or NaN takes a
-// separate branch (uniform over the wave, almost never taken) that divides
-// outright: amax over the non-NaN values, NaN quotients coded 0x7F.
-// Scale rows are scale_stride(h) floats apart, a whole number of 128-byte
-// lines, and written in full (zeros past the last group): a scattered row
-// that ends inside a line leaves that line to be merged in memory with a
-// neighbour written at another time, which costs far more than the pad.
+// [16 sg, 16 sg + 16), quantised by quantise_segment. Scale rows are
+// scale_stride(h) floats apart, a whole number of 128-byte lines, and
+// written in full (zeros past the last group): a scattered row that ends
+// inside a line leaves that line to be merged in memory with a neighbour
+// written at another time, which costs far more than the pad.
 template <int NV>
 struct RowFp8 {
     static constexpr int kPerPass = NV * kWave;
@@ -130,60 +187,8 @@ struct RowFp8 {
     {
         float sc[NV];
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const uint32_t p[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w,
-                                   hi[u].x, hi[u].y, hi[u].z, hi[u].w};
-            float f[16];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                f[2 * i] = bf16_lo(p[i]);
-                f[2 * i + 1] = bf16_hi(p[i]);
-            }
-            uint32_t abits = seg_abs_max_bits(p);
-            abits = max(abits, (uint32_t)__shfl_xor((int)abits, 1, kWave));
-            abits = max(abits, (uint32_t)__shfl_xor((int)abits, 2, kWave));
-            abits = max(abits, (uint32_t)__shfl_xor((int)abits, 4, kWave));
-            uint32_t wd[4];
-            float s;
-            if (__builtin_expect(__ballot(abits >= 0x7F80u) == 0, 1)) {
-                s = fmaxf(__uint_as_float(abits << 16), 1e-4f) / 448.0f;
-                const float rs = 1.0f / s;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int w = cvt2_e4m3<false>(quotient(f[4 * j], s, rs),
-                                                   quotient(f[4 * j + 1], s, rs), 0);
-                    wd[j] = (uint32_t)cvt2_e4m3<true>(quotient(f[4 * j + 2], s, rs),
-                                                      quotient(f[4 * j + 3], s, rs), w);
-                }
-            } else {
-                float amax = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float a = fabsf(f[i]);
-                    amax = (a > amax) ? a : amax;  // a NaN never wins
-                }
-#pragma unroll
-                for (int d = 1; d < 8; d <<= 1) {
-                    const float o = __shfl_xor(amax, d, kWave);
-                    amax = (o > amax) ? o : amax;
-                }
-                s = fmaxf(amax, 1e-4f) / 448.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const float v = f[4 * j + b] / s;
-                        const uint32_t c = (v != v) ? 0x7Fu
-                                                    : ((uint32_t)cvt2_e4m3<false>(v, 0.0f, 0) & 0xFFu);
-                        word |= c << (8 * b);
-                    }
-                    wd[j] = word;
-                }
-            }
-            q[u] = u32x4{wd[0], wd[1], wd[2], wd[3]};
-            sc[u] = s;
-        }
+        for (int u = 0; u < NV; ++u)
+            quantise_segment(lo[u], hi[u], q[u], sc[u]);
         // Group gl = 4L + j of the pass sits in pass item u = L/2, on the
         // lanes 8*(gl % 8) .. +7; collect four per lane for one store.
         const int L = lane_id(), g0 = s0 >> 3, ngrp = nseg >> 3;
@@ -268,6 +273,41 @@ struct Sweep {
             __builtin_amdgcn_s_sleep(1);
     }
 };
+
+// Launch stamps (see DispatchArgs::stamps): device-coherent vector store and
+// load of one 64-bit word.
+__device__ __forceinline__ void stamp_store(unsigned long long *p, uint64_t v)
+{
+    __hip_atomic_store(p, (unsigned long long)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t stamp_load(const unsigned long long *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block 0 of a paced launch stamps the wall clock at its start (workgroups
+// are dispatched in index order, so no wave of the launch starts much
+// before it); call from one lane.
+__device__ __forceinline__ void stamp_launch(const DispatchArgs &a, uint64_t t_entry)
+{
+    if (a.sweep_bpt && a.stamps)
+        stamp_store(a.stamps + a.stamp_slot, t_entry | 1ull);
+}
+
+// True when a wave that entered the kernel at t_entry is late: more than
+// a.late_ticks after block 0 did, i.e. it only found a place after waves of
+// the first round had ended. Read well after the wave's start (once its row
+// has arrived), when block 0's stamp has long been stored; a word left by an
+// earlier launch is older still, so it can only make a wave look late (its
+// stores then go out unpaced: the same bytes, only not on the sweep).
+__device__ __forceinline__ bool wave_is_late(const DispatchArgs &a, uint64_t t_entry)
+{
+    if (!a.stamps)
+        return false;
+    const uint64_t s = uniform64(stamp_load(a.stamps + a.stamp_slot));
+    return (int64_t)(t_entry - s) > (int64_t)a.late_ticks;
+}
 
 // The sweep of one chunk of a dispatch launched in chunks of consecutive
 // tokens (too many tokens for one round of waves). Rows sit in token order
@@ -395,7 +435,7 @@ __device__ __forceinline__ Dests token_dests(const DispatchArgs &a, int t, int64
         a.send_src[row_i] = t;
         for (int k = 0; k < a.K; ++k) {
             const int64_t ek = a.topk_idx[tk + k];
-            const bool on_r = ek >= 0 && ek < a.E && (int)ek / a.L == lane;
+            const bool on_r = ek >= 0 && ek < a.E && div_by_magic((int)ek, a.L_mul) == lane;
             a.send_topk_idx[row_i * a.K + k] = on_r ? ek - (int64_t)lane * a.L : -1;
             a.send_topk_w[row_i * a.K + k] = on_r ? a.topk_w[tk + k] : 0.0f;
         }
@@ -407,13 +447,15 @@ __device__ __forceinline__ Dests token_dests(const DispatchArgs &a, int t, int64
 // token t's row (first pass loaded, not yet quantised) and its lanes as in
 // token_dests: checks, handle and metadata, then the row to every
 // destination. nsend: the number of send rows (the receive rows' place in
-// the sweep; 0 without a send buffer). The wave's sweep starts now. CHUNKED:
-// the launch is one chunk [a.t_begin, a.t_begin + a.t_count) of the tokens,
-// and the lanes' segments are read from the layout offsets.
+// the sweep; 0 without a send buffer). The wave's sweep starts now, unless
+// the wave is late (it entered the kernel at t_entry, more than a.late_ticks
+// after block 0): then it stores unpaced. CHUNKED: the launch is one chunk
+// [a.t_begin, a.t_begin + a.t_count) of the tokens, and the lanes' segments
+// are read from the layout offsets.
 template <bool FP8, bool CHUNKED = false, typename Row>
 __device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row &row,
                                                const uint16_t *xrow, int64_t e, int64_t send_r,
-                                               int64_t recv_r, int64_t nsend)
+                                               int64_t recv_r, int64_t nsend, uint64_t t_entry)
 {
     typename std::conditional<CHUNKED, SweepChunk, Sweep>::type sw;
     sw.t0 = wall_clock64();
@@ -421,6 +463,8 @@ __device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row
     sw.nsend = nsend;
     sw.row_bytes = FP8 ? (int64_t)a.h + 4 * (int64_t)scale_stride(a.h) : 2 * (int64_t)a.h;
     Dests d = token_dests(a, t, e, send_r, recv_r, true);
+    if (sw.bpt && wave_is_late(a, t_entry))
+        sw.bpt = 0;
     if constexpr (CHUNKED) {
         sw.tb = a.t_begin;
         sw.cnt = a.t_count;

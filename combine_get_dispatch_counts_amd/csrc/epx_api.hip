@@ -1,9 +1,11 @@
 // epx_api.hip -- the C ABI declared in include/epx.h: argument checks, then
 // kernel launches on the caller's stream. No call here allocates device
-// memory except epx_create (the 4-byte device error word), and no call waits
-// for the GPU except epx_get_error.
+// memory except epx_create (the context's error word and stamp ring), and no
+// call waits for the GPU except epx_get_error and epx_calibrate_sweep_rate.
 #include <stdint.h>
 #include <stdlib.h>
+
+#include <new>
 
 #include <hip/hip_runtime.h>
 
@@ -48,6 +50,7 @@ int launched(hipError_t e) { return e == hipSuccess ? EPX_OK : EPX_EHIP; }
 
 }  // namespace
 
+
 extern "C" {
 
 int epx_create(epx_ctx **out, int device)
@@ -63,7 +66,7 @@ int epx_create(epx_ctx **out, int device)
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess)
         return EPX_EHIP;
-    epx_ctx *c = static_cast<epx_ctx *>(calloc(1, sizeof(epx_ctx)));
+    epx_ctx *c = new (std::nothrow) epx_ctx();
     int rc = EPX_OK;
     if (!c) {
         rc = EPX_EHIP;
@@ -71,17 +74,20 @@ int epx_create(epx_ctx **out, int device)
         c->device = device;
         c->sweep_gbps[0] = epx::kSweepGBpsBf16;
         c->sweep_gbps[1] = epx::kSweepGBpsFp8;
+        c->stamp_seq.store(0u);
         if (hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, device) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&c->wclk_khz, hipDeviceAttributeWallClockRate, device) !=
                 hipSuccess ||
-            hipMalloc(reinterpret_cast<void **>(&c->d_err), sizeof(int)) != hipSuccess ||
-            hipMemset(c->d_err, 0, sizeof(int)) != hipSuccess) {
-            if (c->d_err)
-                (void)hipFree(c->d_err);
-            free(c);
+            hipMalloc(reinterpret_cast<void **>(&c->dev), sizeof(epx::CtxDev)) != hipSuccess ||
+            hipMemset(c->dev, 0, sizeof(epx::CtxDev)) != hipSuccess) {
+            if (c->dev)
+                (void)hipFree(c->dev);
+            delete c;
             c = nullptr;
             rc = EPX_EHIP;
+        } else {
+            c->d_err = &c->dev->err;
         }
     }
     (void)hipSetDevice(prev);
@@ -96,9 +102,9 @@ int epx_destroy(epx_ctx *ctx)
     int prev = 0;
     (void)hipGetDevice(&prev);
     (void)hipSetDevice(ctx->device);
-    const hipError_t e = hipFree(ctx->d_err);
+    const hipError_t e = hipFree(ctx->dev);
     (void)hipSetDevice(prev);
-    free(ctx);
+    delete ctx;
     return e == hipSuccess ? EPX_OK : EPX_EHIP;
 }
 
@@ -178,6 +184,7 @@ static int layout_args(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int 
     a = epx::LayoutArgs{};
     a.topk_idx = topk_idx;
     a.T = T; a.K = K; a.E = E; a.R = R; a.L = E / R;
+    a.L_mul = epx::div_magic(E / R);
     a.C = channel_prefix ? C : 0;
     a.ntiles = (T + epx::kLayoutTile - 1) / epx::kLayoutTile;
     a.hdr = static_cast<epx::LayoutHdr *>(ws);
@@ -252,6 +259,7 @@ static int dispatch_args(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *
     a = epx::DispatchArgs{};
     a.x = x; a.topk_idx = topk_idx; a.topk_w = topk_w;
     a.h = h; a.T = T; a.K = K; a.E = E; a.R = R; a.L = E / R;
+    a.L_mul = epx::div_magic(E / R);
     a.rank_off = rank_off; a.exp_off = exp_off;
     a.pos_in_rank = pos_in_rank; a.slot_in_expert = slot_in_expert;
     a.send_x = send_x; a.send_scales = send_scales; a.send_src = send_src;
@@ -268,9 +276,22 @@ static int dispatch_args(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *
         a.sweep_bpt = 1;
     // at most T*min(K,R) send rows and T*K receive rows
     const int64_t row_bytes = fp8 ? (int64_t)h + 4 * (int64_t)epx::scale_stride(h) : 2 * (int64_t)h;
-    if ((int64_t)T * (K + (K < R ? K : R)) * row_bytes <=
-        (fp8 ? epx::kSweepMinBytesFp8 : epx::kSweepMinBytesBf16))
+    const int64_t bound = (int64_t)T * (K + (K < R ? K : R)) * row_bytes;
+    if (bound <= (fp8 ? epx::kSweepMinBytesFp8 : epx::kSweepMinBytesBf16))
         a.sweep_bpt = 0;
+    // a row longer than one register pass is stored a slice per pass, and
+    // only the first pass could keep to the schedule: such rows go unpaced
+    if (h > epx::kSweepMaxChannels)
+        a.sweep_bpt = 0;
+    // late waves: an eighth of the longest sweep the call can have, kept
+    // within [4, 16] microseconds of the wall clock
+    a.stamps = ctx->dev->stamp;
+    if (a.sweep_bpt) {
+        const int64_t lo = (int64_t)ctx->wclk_khz * 4 / 1000, hi = (int64_t)ctx->wclk_khz * 16 / 1000;
+        int64_t lt = bound / a.sweep_bpt / 8;
+        lt = lt < lo ? lo : (lt > hi ? hi : lt);
+        a.late_ticks = (uint32_t)lt;
+    }
     return EPX_OK;
 }
 
@@ -289,7 +310,7 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
                                  recv_src, recv_cap_rows, pos_exp, a);
     if (rc != EPX_OK)
         return rc;
-    return launched(epx::launch_dispatch(a, fp8 != 0, ctx->cus, stream));
+    return launched(epx::launch_dispatch(a, fp8 != 0, ctx->cus, &ctx->stamp_seq, stream));
 }
 
 int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps)
@@ -299,6 +320,66 @@ int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps)
         return EPX_EINVAL;
     ctx->sweep_gbps[0] = bf16_gbps;
     ctx->sweep_gbps[1] = fp8_gbps;
+    return EPX_OK;
+}
+
+int epx_get_sweep_rate(epx_ctx *ctx, int *bf16_gbps, int *fp8_gbps)
+{
+    if (!ctx || !bf16_gbps || !fp8_gbps)
+        return EPX_EINVAL;
+    *bf16_gbps = ctx->sweep_gbps[0];
+    *fp8_gbps = ctx->sweep_gbps[1];
+    return EPX_OK;
+}
+
+int epx_calibrate_sweep_rate(epx_ctx *ctx, void *scratch, size_t bytes, int *fill_gbps,
+                             hipStream_t stream)
+{
+    int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if (!scratch || !aligned16(scratch) || bytes < epx::kCalibMinBytes)
+        return EPX_EINVAL;
+    const size_t n = bytes / epx::kFillBlockBytes * epx::kFillBlockBytes;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) {
+        for (hipEvent_t e : ev)
+            if (e)
+                (void)hipEventDestroy(e);
+        return EPX_EHIP;
+    }
+    // two warm-up fills, then the median of five timed ones
+    float ms[5];
+    rc = EPX_OK;
+    for (int i = 0; i < 7 && rc == EPX_OK; ++i) {
+        const bool timed = i >= 2;
+        if (timed && hipEventRecord(ev[0], stream) != hipSuccess)
+            rc = EPX_EHIP;
+        if (rc == EPX_OK && epx::launch_fill_lines(scratch, n, (uint32_t)i, stream) != hipSuccess)
+            rc = EPX_EHIP;
+        if (rc == EPX_OK && timed &&
+            (hipEventRecord(ev[1], stream) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess ||
+             hipEventElapsedTime(&ms[i - 2], ev[0], ev[1]) != hipSuccess))
+            rc = EPX_EHIP;
+    }
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (rc != EPX_OK)
+        return rc;
+    for (int i = 1; i < 5; ++i)  // insertion sort of five
+        for (int j = i; j > 0 && ms[j] < ms[j - 1]; --j) {
+            const float t = ms[j];
+            ms[j] = ms[j - 1];
+            ms[j - 1] = t;
+        }
+    if (!(ms[2] > 0.0f))
+        return EPX_EHIP;
+    const double gbps = (double)n / (ms[2] * 1e-3) / 1e9;
+    const double b = gbps * epx::kCalibBf16Permille / 1000.0, f = gbps * epx::kCalibFp8Permille / 1000.0;
+    ctx->sweep_gbps[0] = b > EPX_MAX_SWEEP_GBPS ? EPX_MAX_SWEEP_GBPS : (int)b;
+    ctx->sweep_gbps[1] = f > EPX_MAX_SWEEP_GBPS ? EPX_MAX_SWEEP_GBPS : (int)f;
+    if (fill_gbps)
+        *fill_gbps = gbps > INT32_MAX ? INT32_MAX : (int)gbps;
     return EPX_OK;
 }
 
@@ -362,7 +443,7 @@ int epx_dispatch_fused(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *to
     if (ws_bytes < epx::fused_workspace_bytes(T, K, E, R))
         return EPX_ECAPACITY;
     f.cus = ctx->cus;
-    return launched(epx::launch_fused(f, fp8 != 0, stream));
+    return launched(epx::launch_fused(f, fp8 != 0, &ctx->stamp_seq, stream));
 }
 
 int epx_combine(epx_ctx *ctx, const uint16_t *expert_out, int64_t n_rows, int h,

@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include "epx.h"
+#include "epx_internal.h"
 
 namespace epx {
 
@@ -28,6 +29,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float v)
     if ((u & 0x7FFFFFFFu) > 0x7F800000u)
         return 0x7FC0u;
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// floor(e / L) for 0 <= e < 512, with m = div_magic(L) (epx_internal.h): a
+// multiply and shift in place of a 25-instruction division sequence.
+__device__ __forceinline__ int div_by_magic(int e, uint32_t m)
+{
+    return (int)(((uint32_t)e * m) >> 20);
 }
 
 __device__ __forceinline__ void flag_error(int *err, int bits)

@@ -6,12 +6,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
+namespace epx {
+
+// Launch stamps of the paced sweep: a paced launch takes the next slot of a
+// ring of this many 64-bit words in the context's device memory (a chunked
+// dispatch one slot per chunk), where its first block stores the wall clock
+// at its start.
+constexpr int kStampSlots = 64;
+
+// Device memory of a context: the error word (EPX_DEV_* bits) on a line of
+// its own, then the stamp ring.
+struct CtxDev {
+    int err;
+    int pad[31];
+    unsigned long long stamp[kStampSlots];
+};
+
+}  // namespace epx
+
 struct epx_ctx {
     int device;
-    int cus;            // compute units of the device
-    int *d_err;         // device error word (EPX_DEV_* bits)
-    int wclk_khz;       // rate of the device's constant wall clock (wall_clock64)
-    int sweep_gbps[2];  // paced row-store sweep rate for bf16 and FP8 rows (0: off)
+    int cus;                 // compute units of the device
+    epx::CtxDev *dev;        // device memory of the context
+    int *d_err;              // &dev->err
+    int wclk_khz;            // rate of the device's constant wall clock (wall_clock64)
+    int sweep_gbps[2];       // paced row-store sweep rate for bf16 and FP8 rows (0: off)
+    std::atomic<unsigned> stamp_seq;  // next slot of the stamp ring
 };
 
 namespace epx {
@@ -32,6 +54,27 @@ constexpr int kSweepGBpsFp8 = 6000;
 // T = 1536 (182 MB: 42.3 against 43.4; 243 MB: 50.6 against 55.4).
 constexpr int64_t kSweepMinBytesBf16 = 256ll << 20;
 constexpr int64_t kSweepMinBytesFp8 = 128ll << 20;
+// Channels of one register pass of the dispatch kernels' largest row
+// (bf16: 16 vectors of 8 channels per lane; FP8: 8 segments of 16): a
+// longer row is stored one pass at a time and is left unpaced.
+constexpr int kSweepMaxChannels = 8192;
+
+// Calibration (epx_calibrate_sweep_rate): the sweep rates as a fraction of
+// the same device's sequential fill rate, measured with launch_fill_lines
+// over a buffer larger than the memory-side cache.
+constexpr int kCalibBf16Permille = 915;
+constexpr int kCalibFp8Permille = 870;
+constexpr size_t kCalibMinBytes = 512ull << 20;
+
+// The multiplier of floor(e / L) = e * m >> 20 for 0 <= e < 512 and
+// 1 <= L <= 512 (an expert and the experts per rank, within
+// EPX_MAX_EXPERTS): with m = ceil(2^20 / L) = (2^20 + d) / L, 0 <= d < L,
+// e * m / 2^20 exceeds e / L by e * d / (L * 2^20) < 1 / L, because
+// e * L < 2^18, so the floor is unchanged; e * m < 2^29 fits in 32 bits.
+__host__ __device__ constexpr uint32_t div_magic(int L)
+{
+    return (uint32_t)(((1u << 20) + (uint32_t)L - 1u) / (uint32_t)L);
+}
 
 // fp32 entries per row of an FP8 scale array for hidden size h: the h/128
 // group scales rounded up to a multiple of 32, so every row is a whole
@@ -49,17 +92,20 @@ constexpr int kLayoutThreads = 2 * kLayoutTile;  // two threads per token of a t
 // Head of the layout workspace (the rest: published words [ntiles, E + R]).
 // Zero before the first call; every call leaves it ready for the next.
 struct LayoutHdr {
-    unsigned long long calls;  // calls completed << 32 | layout blocks of this call arrived;
-                               // the call's tag (in published words) is calls >> 32, + 1
+    unsigned long long calls;  // calls completed << 32 (the low half stays 0); the
+                               // call's tag (in published words) is calls >> 32, + 1
     int pad[14];
-    unsigned int done;  // blocks of the current fused call that have finished
+    unsigned int done;  // blocks of the current call that have finished
     int pad2[15];
 };
 
 struct LayoutArgs {
     const int64_t *topk_idx;
     int T, K, E, R, L, C;
-    int ntiles;
+    uint32_t L_mul;   // div_magic(L): rank of an expert as a multiply and shift
+    int ntiles;       // 256-token tiles (the layout kernel's launcher sets its own)
+    int subs;         // blocks per tile of the layout kernel (set by its launcher)
+    int tile_tokens;  // tokens per tile of the layout kernel (set by its launcher)
     LayoutHdr *hdr;
     uint64_t *pub;  // [ntiles, E + R]
     int32_t *num_tokens_per_expert, *num_tokens_per_rank;
@@ -77,6 +123,7 @@ struct DispatchArgs {
     const int64_t *topk_idx;
     const float *topk_w;
     int h, T, K, E, R, L;
+    uint32_t L_mul;   // div_magic(L)
     const int32_t *rank_off, *exp_off, *pos_in_rank, *slot_in_expert;
     void *send_x;
     float *send_scales;
@@ -99,13 +146,29 @@ struct DispatchArgs {
     // large for one round of waves is launched in chunks (t_count 0: one
     // launch takes all T); each chunk sweeps its own rows.
     int t_begin, t_count;
+    // Late waves of a paced launch: block 0 stores the wall clock at its
+    // start in stamps[stamp_slot]; a wave that starts more than late_ticks
+    // after it did not find a place in the launch's first round of waves
+    // and stores its rows unpaced, so it holds no place waiting for rows
+    // that were due long ago (null: no check).
+    unsigned long long *stamps;
+    int stamp_slot;
+    uint32_t late_ticks;
 };
 
 // Launch the dispatch (cus: compute units of the device). The sweep is paced
 // when every token's wave is on the chip at once; with more tokens than that,
 // the dispatch is launched in chunks of consecutive tokens that each fit one
 // round, each chunk pacing its own rows.
-hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, hipStream_t stream);
+// The next slot of a context's stamp ring (0 without a ring counter).
+inline int next_stamp_slot(std::atomic<unsigned> *seq)
+{
+    return seq ? (int)(seq->fetch_add(1u, std::memory_order_relaxed) % kStampSlots) : 0;
+}
+
+// The paced launches take consecutive slots of the stamp ring from *seq.
+hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, std::atomic<unsigned> *seq,
+                           hipStream_t stream);
 
 struct LLArgs {
     const uint16_t *x;
@@ -131,9 +194,16 @@ struct FusedArgs {
 };
 
 size_t fused_workspace_bytes(int T, int K, int E, int R);
-hipError_t launch_fused(const FusedArgs &f, bool fp8, hipStream_t stream);
+hipError_t launch_fused(const FusedArgs &f, bool fp8, std::atomic<unsigned> *seq,
+                        hipStream_t stream);
 hipError_t fused_launches(const FusedArgs &f, bool fp8, int *launches);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
+
+// A sequential fill of n bytes (a multiple of kFillBlockBytes) with the
+// word v: each block of 256 threads writes one contiguous kFillBlockBytes
+// chunk with 16-byte stores, chunks in block order.
+constexpr size_t kFillBlockBytes = 16384;
+hipError_t launch_fill_lines(void *p, size_t n, uint32_t v, hipStream_t stream);
 
 struct CombineArgs {
     const uint16_t *y;

@@ -74,8 +74,11 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const LayoutArgs &l = f.lay;
     const DispatchArgs &a = f.disp;
+    const uint64_t t_entry = wall_clock64();
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
     const int E = a.E, R = a.R, K = a.K, T = a.T, ER = E + R;
+    if (blockIdx.x == 0 && tid == 0)
+        stamp_launch(a, t_entry);
     uint64_t *tmask = reinterpret_cast<uint64_t *>(lds);                // [kFusedTokens]
     int *tent = reinterpret_cast<int *>(tmask + kFusedTokens);          // [kFusedTokens][KMAX]
     int *bef = tent + kFusedTokens * KMAX;  // [E + R] the tile's tokens before t0
@@ -108,10 +111,9 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     // before t0, the others (publishers only) the tokens of tile blockIdx;
     // lane k < K the token's entry k; then the token's row.
     if (tid == 0) {
-        const unsigned long long v =
-            __hip_atomic_load(&l.hdr->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_tag = (uint32_t)(v >> 32) + 1u;
-        s_go = (uint32_t)v == 0u;  // no layout call was left unfinished
+        uint32_t tg;
+        s_go = read_call_tag(l.hdr, &tg);  // false: the workspace was not left ready
+        s_tag = tg;
     }
     const bool pub_thread = tid >= kLayoutTile;
     const int u = pub_thread ? (int)blockIdx.x * kLayoutTile + (tid - kLayoutTile)
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
 
     // the token's rank bits and entries, for the tokens after it in the block
     const bool valid = lane < K && e >= 0 && e < E;
-    const uint64_t mt = uniform64(wave_or(valid ? 1ull << ((int)e / l.L) : 0ull));
+    const uint64_t mt = uniform64(wave_or(valid ? 1ull << div_by_magic((int)e, l.L_mul) : 0ull));
     if (lane == 0)
         tmask[w] = have ? mt : 0ull;
     if (lane < K)
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
             if (ek < 0)
                 continue;
             atomicAdd(&cnt[ek], 1);
-            m |= 1ull << (ek / l.L);
+            m |= 1ull << div_by_magic(ek, l.L_mul);
         }
         for (; m; m &= m - 1)
             atomicAdd(&cnt[E + __builtin_ctzll(m)], 1);
@@ -178,30 +180,8 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     if (go) {
         for (int c = tid; c < ER; c += blockDim.x) {
             int all = 0, before = 0;
-            for (int j0 = 0; j0 < l.ntiles; j0 += 16) {
-                // 16 tiles' words in flight together, then each polled on
-                // its own until it carries the call's tag
-                const int nq = min(16, l.ntiles - j0);
-                const uint64_t *col = l.pub + (int64_t)j0 * ER + c;
-                uint64_t wv[16];
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    wv[q] = q < nq ? pub_load(col + (int64_t)q * ER) : 0;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    if (q >= nq)
-                        break;
-                    for (int polls = 0; (uint32_t)(wv[q] >> 32) != tag && ok;) {
-                        if (++polls > kSpinLimit)
-                            ok = false;
-                        __builtin_amdgcn_s_sleep(2);
-                        wv[q] = pub_load(col + (int64_t)q * ER);
-                    }
-                    const int v = (int)(uint32_t)wv[q];
-                    all += v;
-                    before += j0 + q < tile ? v : 0;
-                }
-            }
+            if (ok)
+                ok = sum_tile_words(l.pub, ER, l.ntiles, c, tile, tag, &all, &before);
             tot[c] = all;
             pre[c] = before;
         }
@@ -261,18 +241,13 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
         }
         if (lane < K)
             l.slot_in_expert[(int64_t)t * K + lane] = slot;
-        dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r, off[E + 1 + R]);
+        dispatch_token<FP8>(a, t, row, xrow, e, send_r, recv_r, off[E + 1 + R], t_entry);
     }
 
     // this block is done: the last block of the grid opens the next call
     __syncthreads();
-    if (tid == 0) {
-        const unsigned int n = atomicAdd(&l.hdr->done, 1u);
-        if (n == gridDim.x - 1) {
-            __hip_atomic_store(&l.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            atomicAdd(&l.hdr->calls, 1ull << 32);
-        }
-    }
+    if (tid == 0)
+        finish_call(l.hdr);
 }
 
 // Small batches (T <= kSmallMaxT): one block of kLayoutThreads per token,
@@ -335,7 +310,7 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_small_kernel(FusedArgs f
             atomicAdd(&cnt[e], 1);
             if (u < t)
                 atomicAdd(&before[e], 1);
-            m |= 1ull << (e / l.L);
+            m |= 1ull << div_by_magic(e, l.L_mul);
         }
         mask[u] = m;
         for (uint64_t mm = m; mm; mm &= mm - 1) {
@@ -428,7 +403,8 @@ int64_t fused_grid(const FusedArgs &f)
 
 // With launch false, only say how many launches the call takes (1 or 2).
 template <int KMAX, bool FP8, int NV>
-hipError_t launch_fused_k(const FusedArgs &f, hipStream_t stream, bool launch, int *launches)
+hipError_t launch_fused_k(const FusedArgs &f, std::atomic<unsigned> *seq, hipStream_t stream,
+                          bool launch, int *launches)
 {
     const size_t lds = fused_lds_bytes(f.lay.E, f.lay.R, KMAX);
     const int64_t blocks = fused_grid(f);
@@ -448,24 +424,26 @@ hipError_t launch_fused_k(const FusedArgs &f, hipStream_t stream, bool launch, i
     }
     if (!one) {
         const hipError_t e = launch_layout(f.lay, stream);
-        return e != hipSuccess ? e : launch_dispatch(f.disp, FP8, f.cus, stream);
+        return e != hipSuccess ? e : launch_dispatch(f.disp, FP8, f.cus, seq, stream);
     }
+    FusedArgs g = f;
+    g.disp.stamp_slot = next_stamp_slot(seq);
     hipLaunchKernelGGL((fused_kernel<KMAX, FP8, NV>), dim3((unsigned)blocks),
-                       dim3(kLayoutThreads), lds, stream, f);
+                       dim3(kLayoutThreads), lds, stream, g);
     return hipGetLastError();
 }
 
 template <int KMAX>
-hipError_t launch_fused_kmax(const FusedArgs &f, bool fp8, hipStream_t stream, bool launch,
-                             int *launches)
+hipError_t launch_fused_kmax(const FusedArgs &f, bool fp8, std::atomic<unsigned> *seq,
+                             hipStream_t stream, bool launch, int *launches)
 {
     switch (pick_nv(f.disp.h, fp8) + (fp8 ? 100 : 0)) {
-    case 8: return launch_fused_k<KMAX, false, 8>(f, stream, launch, launches);
-    case 14: return launch_fused_k<KMAX, false, 14>(f, stream, launch, launches);
-    case 16: return launch_fused_k<KMAX, false, 16>(f, stream, launch, launches);
-    case 104: return launch_fused_k<KMAX, true, 4>(f, stream, launch, launches);
-    case 107: return launch_fused_k<KMAX, true, 7>(f, stream, launch, launches);
-    default: return launch_fused_k<KMAX, true, 8>(f, stream, launch, launches);
+    case 8: return launch_fused_k<KMAX, false, 8>(f, seq, stream, launch, launches);
+    case 14: return launch_fused_k<KMAX, false, 14>(f, seq, stream, launch, launches);
+    case 16: return launch_fused_k<KMAX, false, 16>(f, seq, stream, launch, launches);
+    case 104: return launch_fused_k<KMAX, true, 4>(f, seq, stream, launch, launches);
+    case 107: return launch_fused_k<KMAX, true, 7>(f, seq, stream, launch, launches);
+    default: return launch_fused_k<KMAX, true, 8>(f, seq, stream, launch, launches);
     }
 }
 
@@ -477,16 +455,17 @@ size_t fused_workspace_bytes(int T, int K, int E, int R)
     return layout_workspace_bytes(T, E, R);  // the head and the tiles' words
 }
 
-hipError_t launch_fused(const FusedArgs &f, bool fp8, hipStream_t stream)
+hipError_t launch_fused(const FusedArgs &f, bool fp8, std::atomic<unsigned> *seq,
+                        hipStream_t stream)
 {
-    return f.lay.K <= 8 ? launch_fused_kmax<8>(f, fp8, stream, true, nullptr)
-                        : launch_fused_kmax<EPX_MAX_TOPK>(f, fp8, stream, true, nullptr);
+    return f.lay.K <= 8 ? launch_fused_kmax<8>(f, fp8, seq, stream, true, nullptr)
+                        : launch_fused_kmax<EPX_MAX_TOPK>(f, fp8, seq, stream, true, nullptr);
 }
 
 hipError_t fused_launches(const FusedArgs &f, bool fp8, int *launches)
 {
-    return f.lay.K <= 8 ? launch_fused_kmax<8>(f, fp8, nullptr, false, launches)
-                        : launch_fused_kmax<EPX_MAX_TOPK>(f, fp8, nullptr, false, launches);
+    return f.lay.K <= 8 ? launch_fused_kmax<8>(f, fp8, nullptr, nullptr, false, launches)
+                        : launch_fused_kmax<EPX_MAX_TOPK>(f, fp8, nullptr, nullptr, false, launches);
 }
 
 }  // namespace epx

@@ -16,7 +16,8 @@
  * Conventions shared by every call
  *   - Pointers are device memory unless a comment says "host". Every array is
  *     dense row-major. The caller allocates and owns every buffer; no call
- *     allocates device memory (epx_create allocates one 4-byte error word).
+ *     allocates device memory (epx_create allocates the context's error word
+ *     and a 512-byte ring of launch stamps).
  *   - bf16 data is passed as uint16 bit patterns; FP8 data as uint8 codes in
  *     OCP E4M3FN (max 448, no infinities).
  *   - Hidden-state buffers (x, send_x, recv_x, ll_x, expert_out, out) and the
@@ -68,12 +69,13 @@ extern "C" {
 
 typedef struct epx_ctx epx_ctx;
 
-/* Context: binds a device and owns its device error word. [P2] "Buffer 与内存
- * 视角" / "内存生命周期": a Buffer is built once, used by every call and
- * destroyed at the end; here it holds no communication state (there is no
- * peer). `device` is a HIP device ordinal; the calls below must be issued
- * with that device current. Returns EPX_EINVAL for a bad ordinal, EPX_EHIP if
- * the error word cannot be allocated. */
+/* Context: binds a device and owns its device error word and the stamps of
+ * its paced launches (epx_set_sweep_rate). [P2] "Buffer 与内存视角" /
+ * "内存生命周期": a Buffer is built once, used by every call and destroyed at
+ * the end; here it holds no communication state (there is no peer).
+ * `device` is a HIP device ordinal; the calls below must be issued with that
+ * device current. Returns EPX_EINVAL for a bad ordinal, EPX_EHIP if the
+ * context's device memory cannot be allocated. */
 int epx_create(epx_ctx **out, int device);
 int epx_destroy(epx_ctx *ctx);
 const char *epx_strerror(int code);
@@ -91,20 +93,43 @@ const char *epx_strerror(int code);
  * front, which HBM absorbs at sequential-write speed, where the same rows in
  * routing order arrive as random writes. A larger epx_dispatch is launched
  * as chunks of consecutive tokens that each fit, each sweeping its own rows
- * at 9/10 of the rate. The permute alone (epx_dispatch with send_x = NULL),
- * which reads as many rows as it writes, is not paced, nor is a call whose
- * row bound (T*(K + min(K,R)) rows) is at most 256 MiB for bf16 or 128 MiB
- * for FP8: such rows mostly stay in the memory-side cache during the launch,
- * and the pacing delay would cost more than the ordering saves. A rate above what the memory sustains lets the front
- * spread back toward random order (in one launch measured no slower than
- * unpaced); a lower one leaves bandwidth idle. Pacing assumes the launch has
- * the device's compute units to itself: with kernels of other streams
- * running alongside, some waves may find no place until paced waves end,
- * and the call can take up to about twice as long (set the rates to 0 for
- * such use). Defaults, measured on MI355X: 6300 (bf16) and 6000 (FP8). The
+ * at 9/10 of the rate. Left unpaced: the permute alone (epx_dispatch with
+ * send_x = NULL), which reads as many rows as it writes; a call whose row
+ * bound (T*(K + min(K,R)) rows) is at most 256 MiB for bf16 or 128 MiB for
+ * FP8 (such rows mostly stay in the memory-side cache during the launch, and
+ * the pacing delay would cost more than the ordering saves); rows of more
+ * than 8192 channels (stored one register pass at a time). A rate above
+ * what the memory sustains lets the front spread back toward random order
+ * (in one launch measured no slower than unpaced); a lower one leaves
+ * bandwidth idle. Late waves: a paced launch's first block stamps its start,
+ * and a wave that starts more than an eighth of the launch's longest sweep
+ * (at least 4, at most 16 microseconds) after it -- a wave that found no
+ * place until others ended, e.g. beside kernels of other streams, or when
+ * the device holds fewer waves than its occupancy query reported -- stores
+ * its rows unpaced instead of waiting for times already past, so such a
+ * wave costs at most that much plus its own unpaced stores (outputs are
+ * unaffected either way). Defaults, measured on MI355X: 6300 (bf16) and 6000 (FP8);
+ * epx_calibrate_sweep_rate derives them from the device instead. The
  * setting is per context and read at each call. EPX_EINVAL for a NULL
  * context or a rate outside [0, EPX_MAX_SWEEP_GBPS]. */
 int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps);
+
+/* The context's current sweep rates (host out), as epx_set_sweep_rate or
+ * epx_calibrate_sweep_rate left them. EPX_EINVAL for a NULL argument. */
+int epx_get_sweep_rate(epx_ctx *ctx, int *bf16_gbps, int *fp8_gbps);
+
+/* Set the sweep rates from this device's own memory: times a sequential
+ * fill of `scratch` (device memory of `bytes` >= 512 MiB, larger than the
+ * memory-side cache, 16-byte aligned; its contents are overwritten) on
+ * `stream` -- two untimed fills, then the median of five -- and sets the
+ * bf16 and FP8 rates to 91.5% and 87% of that fill rate (the ratios of the
+ * defaults above to the fill rate of the GPU they were measured on).
+ * *fill_gbps (host, may be NULL) receives the measured fill rate in GB/s.
+ * Unlike every other call, this one waits for the stream; call it once,
+ * outside any graph capture. EPX_EINVAL for a bad scratch, EPX_EHIP if a
+ * launch or event fails (the rates are then left as they were). */
+int epx_calibrate_sweep_rate(epx_ctx *ctx, void *scratch, size_t bytes, int *fill_gbps,
+                             hipStream_t stream);
 
 /* Workspace bytes epx_get_dispatch_layout needs for (T, K, E, R) (host out):
  * a 128-byte head plus 8 bytes per (256-token tile, expert or rank).

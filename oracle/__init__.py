@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.orc_dispatch.argtypes = ([P, i32, P, P, i32, i32, i32, i32] + [P] * 5 + [i32]
                                    + [P] * 5 + [i64] + [P] * 3 + [i64, P])
         L.orc_dispatch.restype = i32
+        L.orc_dispatch_tokens.argtypes = L.orc_dispatch.argtypes + [i32, i32]
+        L.orc_dispatch_tokens.restype = i32
         L.orc_ll_dispatch.argtypes = [P, i32, P] + [i32] * 8 + [P] * 5
         L.orc_ll_dispatch.restype = i32
         L.orc_combine.argtypes = [P, i64, i32, P, P, i32, i32, P]
@@ -159,9 +161,29 @@ def layout(topk_idx: np.ndarray, E: int, R: int, C: int | None = None) -> dict:
 
 # ---------------------------------------------------------------- dispatch
 
+def _slices(T: int, threads: int) -> list[tuple[int, int]]:
+    """[0, T) cut into `threads` contiguous token ranges."""
+    n = max(1, min(threads, T))
+    step = -(-T // n) if T else 0
+    return [(a, min(a + step, T)) for a in range(0, T, step)] if T else [(0, 0)]
+
+
+def _run_threads(fn, ranges, threads: int) -> list:
+    """fn over the token ranges, side by side when threads > 1 (ctypes drops
+    the interpreter lock during each call)."""
+    if threads <= 1 or len(ranges) == 1:
+        return [fn(a, b) for a, b in ranges]
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(lambda r: fn(*r), ranges))
+
+
 def dispatch(x: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, E: int, R: int,
-             fp8: bool = False, lay: dict | None = None) -> dict:
-    """Layout (if not given), then the rank-deduplicated pack and the expert-major permute."""
+             fp8: bool = False, lay: dict | None = None, threads: int = 1) -> dict:
+    """Layout (if not given), then the rank-deduplicated pack and the
+    expert-major permute. threads > 1 runs the pack and permute of disjoint
+    token ranges side by side (same outputs; the layout stays sequential)."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
     topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
@@ -188,14 +210,18 @@ def dispatch(x: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray, E: int, R:
         recv_src=np.empty(n_exp, np.int32),
         pos_exp=np.empty((T, K), np.int32),
     )
-    rc = lib().orc_dispatch(
-        _p(x), h, _p(topk_idx), _p(topk_w), T, K, E, R,
-        _p(lay["is_token_in_rank"]), _p(lay["rank_off"]), _p(lay["exp_off"]),
-        _p(lay["pos_in_rank"]), _p(lay["slot_in_expert"]), int(bool(fp8)),
-        _p(send_x), _p(send_scales), _p(out["send_src"]), _p(out["send_topk_idx"]),
-        _p(out["send_topk_w"]), n_rank,
-        _p(recv_x), _p(recv_scales), _p(out["recv_src"]), n_exp, _p(out["pos_exp"]))
-    _check(rc, "dispatch")
+    def run(t0: int, t1: int) -> int:
+        return lib().orc_dispatch_tokens(
+            _p(x), h, _p(topk_idx), _p(topk_w), T, K, E, R,
+            _p(lay["is_token_in_rank"]), _p(lay["rank_off"]), _p(lay["exp_off"]),
+            _p(lay["pos_in_rank"]), _p(lay["slot_in_expert"]), int(bool(fp8)),
+            _p(send_x), _p(send_scales), _p(out["send_src"]), _p(out["send_topk_idx"]),
+            _p(out["send_topk_w"]), n_rank,
+            _p(recv_x), _p(recv_scales), _p(out["recv_src"]), n_exp, _p(out["pos_exp"]),
+            t0, t1)
+
+    for rc in _run_threads(run, _slices(T, threads), threads):
+        _check(rc, "dispatch")
     out["layout"] = lay
     return out
 
@@ -228,15 +254,23 @@ def ll_dispatch(x: np.ndarray, topk_idx: np.ndarray, E: int, R: int, src_rank: i
                 pos_ll=pos_ll)
 
 
-def combine(expert_out: np.ndarray, topk_w: np.ndarray, pos: np.ndarray) -> np.ndarray:
+def combine(expert_out: np.ndarray, topk_w: np.ndarray, pos: np.ndarray,
+            threads: int = 1) -> np.ndarray:
+    """threads > 1 reduces disjoint token ranges side by side (same outputs:
+    every token is reduced on its own)."""
     expert_out = np.ascontiguousarray(expert_out, dtype=np.uint16)
     topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     n_rows, h = expert_out.shape
     T, K = pos.shape
     out = np.empty((T, h), np.uint16)
-    rc = lib().orc_combine(_p(expert_out), n_rows, h, _p(topk_w), _p(pos), T, K, _p(out))
-    _check(rc, "combine")
+
+    def run(t0: int, t1: int) -> int:
+        return lib().orc_combine(_p(expert_out), n_rows, h, _p(topk_w[t0:t1]), _p(pos[t0:t1]),
+                                 t1 - t0, K, _p(out[t0:t1]))
+
+    for rc in _run_threads(run, _slices(T, threads), threads):
+        _check(rc, "combine")
     return out
 
 

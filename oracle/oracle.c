@@ -327,10 +327,31 @@ int orc_dispatch(const uint16_t *x, int h, const int64_t *topk_idx, const float 
                  void *recv_x, float *recv_scales, int32_t *recv_src,
                  int64_t recv_cap_rows, int32_t *pos_exp)
 {
+    return orc_dispatch_tokens(x, h, topk_idx, topk_w, T, K, E, R, is_token_in_rank, rank_off,
+                               exp_off, pos_in_rank, slot_in_expert, fp8, send_x, send_scales,
+                               send_src, send_topk_idx, send_topk_w, send_cap_rows, recv_x,
+                               recv_scales, recv_src, recv_cap_rows, pos_exp, 0, T);
+}
+
+/* The same for the tokens [t_begin, t_end) only: their pack rows, then their
+ * permute rows. Every row a token writes is fixed by the layout, and its
+ * permute reads only rows its own pack wrote, so disjoint token ranges can
+ * run side by side (the benchmark's threaded timing of the oracle does);
+ * orc_dispatch is the range [0, T). */
+int orc_dispatch_tokens(const uint16_t *x, int h, const int64_t *topk_idx, const float *topk_w,
+                        int T, int K, int E, int R,
+                        const uint8_t *is_token_in_rank, const int32_t *rank_off,
+                        const int32_t *exp_off, const int32_t *pos_in_rank,
+                        const int32_t *slot_in_expert, int fp8,
+                        void *send_x, float *send_scales, int32_t *send_src,
+                        int64_t *send_topk_idx, float *send_topk_w, int64_t send_cap_rows,
+                        void *recv_x, float *recv_scales, int32_t *recv_src,
+                        int64_t recv_cap_rows, int32_t *pos_exp, int t_begin, int t_end)
+{
     int rc = check_shape(T, K, E, R);
     if (rc != ORC_OK)
         return rc;
-    if (h < 1)
+    if (h < 1 || t_begin < 0 || t_end > T || t_begin > t_end)
         return ORC_EINVAL;
     if (fp8 && h % 128 != 0)
         return ORC_EUNSUPPORTED;
@@ -347,7 +368,7 @@ int orc_dispatch(const uint16_t *x, int h, const int64_t *topk_idx, const float 
     }
 
     /* pack: t ascending, then r ascending; an FP8 row is quantised once per token */
-    for (int t = 0; t < T; ++t) {
+    for (int t = t_begin; t < t_end; ++t) {
         const void *payload;
         const float *pscales;
         token_payload(x, h, fp8, t, q_tmp, s_tmp, &payload, &pscales);
@@ -367,7 +388,7 @@ int orc_dispatch(const uint16_t *x, int h, const int64_t *topk_idx, const float 
     }
 
     /* permute: t ascending, then k ascending, reading the packed buffer */
-    for (int t = 0; t < T; ++t) {
+    for (int t = t_begin; t < t_end; ++t) {
         for (int k = 0; k < K; ++k) {
             int64_t e = topk_idx[(size_t)t * K + k];
             if (e == -1) {

@@ -85,6 +85,17 @@ int orc_dispatch(const uint16_t *x, int h, const int64_t *topk_idx, const float 
                  void *recv_x, float *recv_scales, int32_t *recv_src,
                  int64_t recv_cap_rows, int32_t *pos_exp);
 
+/* orc_dispatch for the tokens [t_begin, t_end) only (see oracle.c). */
+int orc_dispatch_tokens(const uint16_t *x, int h, const int64_t *topk_idx, const float *topk_w,
+                        int T, int K, int E, int R,
+                        const uint8_t *is_token_in_rank, const int32_t *rank_off,
+                        const int32_t *exp_off, const int32_t *pos_in_rank,
+                        const int32_t *slot_in_expert, int fp8,
+                        void *send_x, float *send_scales, int32_t *send_src,
+                        int64_t *send_topk_idx, float *send_topk_w, int64_t send_cap_rows,
+                        void *recv_x, float *recv_scales, int32_t *recv_src,
+                        int64_t recv_cap_rows, int32_t *pos_exp, int t_begin, int t_end);
+
 /* Low-latency fixed-slot dispatch ([P1] "低延迟模式：固定缓冲区与信号槽机制";
  * [P3] 4.2). Region rho = e*R + src_rank (R_buf == R, all destinations'
  * buffers side by side) or rho = e (R_buf == 1, this source's slice only);

@@ -131,3 +131,10 @@ def test_set_sweep_rate_needs_a_context(lib):
     """Argument checks come first: no context, no setting."""
     assert lib.epx_set_sweep_rate(None, 6200, 6000) == -1
     assert lib.epx_set_sweep_rate(None, 0, 0) == -1
+
+
+def test_sweep_rate_calls_need_a_context(lib):
+    b, f = ctypes.c_int(), ctypes.c_int()
+    assert lib.epx_get_sweep_rate(None, ctypes.byref(b), ctypes.byref(f)) == -1
+    fill = ctypes.c_int()
+    assert lib.epx_calibrate_sweep_rate(None, None, 1 << 30, ctypes.byref(fill), None) == -1

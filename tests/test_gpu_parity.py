@@ -356,6 +356,9 @@ def _ll_gpu(x, topk, E, R, src, cap, R_buf, fp8):
 @pytest.mark.parametrize("cfg,T,src,R_buf_full,fp8,cap", [
     (1, None, 0, True, True, 64), (1, None, 3, True, False, 64), (1, None, 2, False, True, 80),
     (2, 24, 31, False, False, 32), (2, None, 0, False, True, 128), (2, 1, 5, False, True, 1),
+    # larger decode batches: several tokens per block (2, 4 and 8), the last
+    # block ragged at T = 600
+    (2, 300, 31, False, False, 300), (2, 600, 0, False, True, 600), (2, 1024, 7, False, True, 1024),
 ])
 def test_ll_dispatch_small(cfg, T, src, R_buf_full, fp8, cap):
     inp = synth.make_inputs(cfg, T=T)
@@ -372,6 +375,23 @@ def test_ll_dispatch_small(cfg, T, src, R_buf_full, fp8, cap):
     _eq(host_bits(buf.ll_x), o["ll_x"], "ll_x")
     if fp8:
         _check_ll_scales(host_bits(buf.ll_scales), o["ll_scales"], o["ll_src"], "ll_scales")
+
+
+def test_ll_dispatch_eight_tokens_per_block():
+    """A decode batch of 2000 tokens (eight tokens per block, one wave each,
+    the last block ragged) on the decode routing at a narrower hidden size."""
+    inp = synth.make_inputs(2, T=2000)
+    wl = inp["workload"]
+    x = np.ascontiguousarray(inp["x"][:, :1024])
+    topk = inp["topk_idx"]
+    say(f"ll_dispatch T=2000 h=1024 E={wl.E} R={wl.R} cap=2000")
+    buf = _ll_gpu(x, topk, wl.E, wl.R, 3, 2000, 1, True)
+    o = oracle.ll_dispatch(x, topk, wl.E, wl.R, 3, 2000, 1, fp8=True)
+    _eq(host_bits(buf.pos_ll), o["pos_ll"], "pos_ll")
+    _eq(host_bits(buf.ll_count), o["ll_count"], "ll_count")
+    _eq(host_bits(buf.ll_src), o["ll_src"], "ll_src")
+    _eq(host_bits(buf.ll_x), o["ll_x"], "ll_x")
+    _check_ll_scales(host_bits(buf.ll_scales), o["ll_scales"], o["ll_src"], "ll_scales")
 
 
 @pytest.mark.parametrize("h,fp8,K", [(1152, True, 4), (1152, False, 4), (9216, True, 8),
@@ -463,6 +483,62 @@ def test_ll_combine(cfg):
     y = synth.expert_outputs(buf.ll_x.shape[0], wl.h, seed=5 + cfg, device="cuda")
     out = _gpu_combine(y, host_bits(buf.pos_ll), inp["topk_w"])
     _eq(out, oracle.combine(host_bits(y), inp["topk_w"], o["pos_ll"]), "ll combined_x")
+
+
+@pytest.mark.parametrize("cfg,src", [(1, 0), (1, 3), (2, 17)])
+def test_ll_combine_full_layout(cfg, src):
+    """Combine through the handle of a low-latency dispatch into the full
+    layout (R_buf = R: region e*R + src of every destination's buffer side by
+    side), over expert outputs covering all E*R*cap rows: the rows of other
+    sources' regions are never read, so the result equals the oracle's
+    combine through its own full-layout handle."""
+    inp = synth.make_inputs(cfg)
+    wl = inp["workload"]
+    T = wl.T if cfg == 1 else 8   # the decode shape's full layout at cap 8: 65 536 rows
+    x, topk, w = (np.ascontiguousarray(inp[k][:T]) for k in ("x", "topk_idx", "topk_w"))
+    cap = max(wl.cap, T) if cfg == 1 else 8
+    say(f"ll combine, full layout: {wl.describe()} T={T} src={src} cap={cap}")
+    buf = _ll_gpu(x, topk, wl.E, wl.R, src, cap, wl.R, True)
+    o = oracle.ll_dispatch(x, topk, wl.E, wl.R, src, cap, wl.R, fp8=True)
+    _eq(host_bits(buf.pos_ll), o["pos_ll"], "pos_ll")
+    assert buf.ll_x.shape[0] == wl.E * wl.R * cap
+    y = synth.expert_outputs(buf.ll_x.shape[0], wl.h, seed=40 + cfg, device="cuda")
+    out = _gpu_combine(y, host_bits(buf.pos_ll), w)
+    # the oracle gets only the rows the handle names (a relabelling of row
+    # indices, no arithmetic), not the whole E*R*cap buffer
+    p = o["pos_ll"]
+    used = np.unique(p[p >= 0])
+    relabel = np.where(p >= 0, np.searchsorted(used, np.maximum(p, 0)), -1).astype(np.int32)
+    y_used = host_bits(y[torch.from_numpy(used).cuda()])
+    _eq(out, oracle.combine(y_used, w, relabel), "full-layout ll combined_x")
+
+
+def test_totals_host_mapped():
+    """The totals also land in a caller's pinned host int32[2] (the CPU-
+    mapped receive counter the host polls before allocating, [P2] "Buffer
+    与内存视角"): after a stream synchronisation they equal the oracle's, from
+    the layout call and from the fused call (one launch, and two)."""
+    import combine_get_dispatch_counts_amd as epx
+
+    for cfg, T in ((3, None), (1, None), (4, None), (3, 2048)):
+        inp = synth.make_inputs(cfg, T=T)
+        wl = inp["workload"]
+        o = oracle.layout(inp["topk_idx"], wl.E, wl.R)
+        tk = torch.from_numpy(inp["topk_idx"]).cuda()
+        host = torch.full((2,), -7, dtype=torch.int32).pin_memory()
+        say(f"host-mapped totals, layout call: {wl.describe()}")
+        epx.get_dispatch_layout(tk, wl.E, wl.R, totals_host=host)
+        torch.cuda.synchronize()
+        _eq(host.numpy(), o["totals"], "host totals (layout)")
+        host.fill_(-7)
+        say(f"host-mapped totals, fused call ({epx.fused_launches(wl.T, wl.h, wl.K, wl.E, wl.R)} "
+            "launch(es))")
+        x = torch.from_numpy(inp["x"].view(np.int16)).cuda().view(torch.bfloat16)
+        epx.dispatch_fused(x, tk, torch.from_numpy(inp["topk_w"]).cuda(), wl.E, wl.R,
+                           totals_host=host)
+        torch.cuda.synchronize()
+        _eq(host.numpy(), o["totals"], "host totals (fused)")
+        assert epx.get_error() == 0
 
 
 # ------------------------------------------------------------------ errors

@@ -28,14 +28,31 @@ def _eq(a, b, what):
 
 @pytest.mark.parametrize("fp8", [False, True])
 def test_multi_source_receive_permute(fp8):
-    import combine_get_dispatch_counts_amd as epx
-
     T, h, E, R, K = 512, 1024, 64, 8, 6
-    L, per = E // R, T // R
     rng = np.random.default_rng(77)
     x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
     topk = synth.random_routing(T, K, E, seed=78, p_drop=0.05)
     w = rng.random((T, K)).astype(np.float32)
+    _check_receive(x, topk, w, E, R, fp8)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_multi_source_receive_prefill_shape(fp8):
+    """The prefill shape: 32 logical sources of 128 tokens each (T = 4096,
+    h = 7168, E = 256, top-8 on the prefill routing), every one of the 32
+    destinations' permuted blocks -- rows, FP8 scales and source rows --
+    against the oracle's expert-major buffer over that destination's experts."""
+    inp = synth.make_inputs(3)
+    wl = inp["workload"]
+    _check_receive(inp["x"], inp["topk_idx"], inp["topk_w"], wl.E, wl.R, fp8)
+
+
+def _check_receive(x, topk, w, E, R, fp8):
+    import combine_get_dispatch_counts_amd as epx
+
+    T, h = x.shape
+    K = topk.shape[1]
+    L, per = E // R, T // R
     say(f"multi-source receive T={T} h={h} E={E} R={R} K={K} fp8={fp8}")
 
     # every source: layout + dispatch over its own tokens

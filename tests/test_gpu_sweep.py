@@ -16,7 +16,7 @@ from _gpu import host_bits, say
 
 pytestmark = pytest.mark.gpu
 
-DEFAULTS = (6300, 6000)
+DEFAULTS = (6300, 6000)  # the rates a new context starts with (include/epx.h)
 
 
 def _run(epx, inp, fused, fp8, bufs, lay_buf, ws):
@@ -73,13 +73,14 @@ def _check_rates(cfg, fused, fp8, T_override=None):
     lay_buf = epx.alloc_layout(T, K, E, R, None, dev)
     ws = torch.zeros(epx.fused_workspace_size(T, K, E, R), dtype=torch.uint8, device=dev)
     runs = {}
+    prior = epx.get_sweep_rate()
     try:
         for rate in (DEFAULTS, (0, 0), (1500, 1500), (60000, 60000)):
             say(f"config {cfg} T={T} {'fused' if fused else 'dispatch'} fp8={fp8} sweep rate {rate}")
             epx.set_sweep_rate(*rate)
             runs[rate] = _run(epx, inp, fused, fp8, bufs, lay_buf, ws)
     finally:
-        epx.set_sweep_rate(*DEFAULTS)
+        epx.set_sweep_rate(*prior)
     ref = runs[(0, 0)]
     for rate, got in runs.items():
         for k in ref:
@@ -114,6 +115,7 @@ def test_sweep_rate_receive_permute():
                      torch.from_numpy(inp["topk_w"]).cuda(), E, R)
     rows, idx = d.send_x, d.send_topk_idx
     got = {}
+    prior = epx.get_sweep_rate()
     try:
         for rate in (DEFAULTS, (0, 0)):
             say(f"receive permute of {rows.shape[0]} rows, sweep rate {rate}")
@@ -123,7 +125,7 @@ def test_sweep_rate_receive_permute():
             n = int(rec.layout.totals[1].item())  # rows past the total are not written
             got[rate] = (host_bits(rec.x)[:n], host_bits(rec.src_row)[:n], host_bits(rec.pos))
     finally:
-        epx.set_sweep_rate(*DEFAULTS)
+        epx.set_sweep_rate(*prior)
     for a, b in zip(got[DEFAULTS], got[(0, 0)]):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
@@ -178,9 +180,41 @@ def test_chunked_dispatch_in_graph():
 def test_sweep_rate_argument_checks():
     import combine_get_dispatch_counts_amd as epx
 
-    with pytest.raises(epx.EpxError):
-        epx.set_sweep_rate(-1, 6000)
-    with pytest.raises(epx.EpxError):
-        epx.set_sweep_rate(6200, 100001)
-    epx.set_sweep_rate(100000, 0)
-    epx.set_sweep_rate(*DEFAULTS)
+    prior = epx.get_sweep_rate()
+    try:
+        with pytest.raises(epx.EpxError):
+            epx.set_sweep_rate(-1, 6000)
+        with pytest.raises(epx.EpxError):
+            epx.set_sweep_rate(6200, 100001)
+        assert epx.get_sweep_rate() == prior  # a rejected call changes nothing
+        epx.set_sweep_rate(100000, 0)
+        assert epx.get_sweep_rate() == (100000, 0)
+    finally:
+        epx.set_sweep_rate(*prior)
+    assert epx.get_sweep_rate() == prior
+
+
+def test_calibrated_sweep_rate():
+    """The calibration times a fill of a 1 GiB scratch and sets both rates
+    to their fixed fractions of it; a scratch smaller than the memory-side
+    cache is refused and leaves the rates alone. Outputs at the calibrated
+    rates are those at the defaults (checked for the prefill dispatch)."""
+    import combine_get_dispatch_counts_amd as epx
+
+    prior = epx.get_sweep_rate()
+    try:
+        small = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        with pytest.raises(epx.EpxError):
+            epx.calibrate_sweep_rate(small)
+        assert epx.get_sweep_rate() == prior
+        del small
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        fill = epx.calibrate_sweep_rate(scratch)
+        del scratch
+        b, f = epx.get_sweep_rate()
+        say(f"calibration: fill {fill} GB/s -> sweep rates {b} (bf16), {f} (FP8)")
+        assert 2000 < fill < 20000, fill
+        assert b == int(fill * 0.915) or abs(b - fill * 0.915) <= 1
+        assert f == int(fill * 0.870) or abs(f - fill * 0.870) <= 1
+    finally:
+        epx.set_sweep_rate(*prior)

@@ -166,3 +166,26 @@ def test_two_level_pack_equals_rank_level_pack(orc, fp8):
     # has two ranks in one node
     n1 = int(orc.layout(topk, E, N)["totals"][0])
     assert n1 < int(flat["layout"]["totals"][0])
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_threaded_oracle_equals_sequential(orc, fp8):
+    """The oracle run over token ranges side by side (the benchmark's
+    threaded CPU timing) gives exactly the sequential run's outputs, for the
+    dispatch and the combine, with ragged ranges."""
+    T, h, E, R, K = 301, 256, 32, 8, 4
+    rng = np.random.default_rng(12)
+    x = synth.to_bf16_bits(rng.standard_normal((T, h)).astype(np.float32))
+    topk = synth.random_routing(T, K, E, seed=13, p_drop=0.05)
+    w = rng.random((T, K)).astype(np.float32)
+    seq = orc.dispatch(x, topk, w, E, R, fp8=fp8)
+    for threads in (2, 7):
+        par = orc.dispatch(x, topk, w, E, R, fp8=fp8, threads=threads)
+        for k in ("send_x", "send_src", "send_topk_idx", "send_topk_w", "recv_x", "recv_src",
+                  "pos_exp") + (("send_scales", "recv_scales") if fp8 else ()):
+            assert np.array_equal(np.asarray(par[k]).view(np.uint8),
+                                  np.asarray(seq[k]).view(np.uint8)), (threads, k)
+    y = synth.to_bf16_bits(rng.standard_normal((T * K, h)).astype(np.float32))
+    c1 = orc.combine(y, w, seq["pos_exp"])
+    for threads in (3, 16):
+        assert np.array_equal(orc.combine(y, w, seq["pos_exp"], threads=threads), c1)
