@@ -25,6 +25,7 @@ from .api import (  # noqa: E402
     fused_launches,
     fused_workspace_size,
     get_dispatch_layout,
+    get_dispatch_layout_noalloc,
     get_error,
     get_sweep_rate,
     ll_dispatch,
@@ -38,7 +39,8 @@ from .api import (  # noqa: E402
 )
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
-           "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
+           "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout",
+           "get_dispatch_layout_noalloc", "alloc_dispatch",
            "dispatch", "combine", "combine_partial", "combine_final", "ll_reset", "alloc_ll",
            "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
            "fused_launches", "dispatch_fused", "set_sweep_rate", "get_sweep_rate",

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libepx.so")
 EPX_OK, EPX_EINVAL, EPX_ECAPACITY, EPX_EUNSUPPORTED, EPX_EHIP, EPX_EDEVICE = 0, -1, -2, -3, -4, -5
 DEV_BAD_ROUTE, DEV_OVERFLOW, DEV_BAD_HANDLE, DEV_WORKSPACE = 1, 2, 4, 8
 MAX_TOPK, MAX_EXPERTS, MAX_RANKS, MAX_SWEEP_GBPS = 32, 512, 64, 100000
+NOALLOC_SCRATCH_BYTES = 1 << 20
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -31,6 +32,7 @@ SIGNATURES = {
     "epx_ll_size_hint": (_SZ, [_I, _I, _I, _I, _I]),
     "epx_scale_stride": (_I, [_I]),
     "epx_get_dispatch_layout": (_I, [_P, _P, _I, _I, _I, _I, _I] + [_P] * 11 + [_SZ, _P]),
+    "epx_get_dispatch_layout_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I] + [_P] * 10 + [_P]),
     "epx_dispatch": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I] + [_P] * 4 + [_I]
                      + [_P] * 5 + [_I64] + [_P] * 3 + [_I64, _P, _P]),
     "epx_fused_workspace_size": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),

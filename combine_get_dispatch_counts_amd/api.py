@@ -237,6 +237,32 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
     return lay
 
 
+def get_dispatch_layout_noalloc(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                                num_channels: int | None = None,
+                                totals_host: torch.Tensor | None = None,
+                                out: Layout | None = None) -> Layout:
+    """get_dispatch_layout with the library's own fixed device scratch as
+    the workspace (no allocation by the library; with ``out`` given, none
+    here either). Calls on one GPU share that scratch and must not overlap."""
+    _need(topk_idx, torch.int64, "topk_idx", 2)
+    dev = topk_idx.device
+    T, K = topk_idx.shape
+    E, R = num_experts, num_ranks
+    lay = out if out is not None else alloc_layout(T, K, E, R, num_channels, dev)
+    _check_layout(lay, T, K, E, R, num_channels, dev)
+    if totals_host is not None and not (totals_host.is_pinned() and totals_host.numel() >= 2
+                                        and totals_host.dtype == torch.int32):
+        raise ValueError("totals_host must be a pinned int32 tensor of >= 2 elements")
+    cp = lay.channel_prefix if num_channels else None
+    rc = _lib.load().epx_get_dispatch_layout_noalloc(
+        _ctx(dev), _p(topk_idx), T, K, E, R, num_channels or 0,
+        _p(lay.num_tokens_per_expert), _p(lay.num_tokens_per_rank), _p(lay.is_token_in_rank),
+        _p(lay.rank_off), _p(lay.exp_off), _p(lay.pos_in_rank), _p(lay.slot_in_expert),
+        _p(cp), _p(lay.totals), _p(totals_host), _stream(dev))
+    check(rc, "epx_get_dispatch_layout_noalloc")
+    return lay
+
+
 def scale_stride(h: int) -> int:
     """fp32 entries per FP8 scale row: h/128 rounded up to whole 128-byte
     lines; the entries past h/128 are written as +0.0."""
@@ -572,7 +598,7 @@ def ll_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_r
 
 __all__ = ["EpxError", "Layout", "Dispatched", "LowLatency", "workspace_size", "ll_size_hint",
            "scale_stride", "get_error", "alloc_layout", "get_dispatch_layout", "alloc_dispatch",
-           "dispatch", "combine", "combine_partial",
+           "get_dispatch_layout_noalloc", "dispatch", "combine", "combine_partial",
            "combine_final", "ll_reset", "alloc_ll",
            "ll_dispatch", "Received", "recv_permute", "fused_workspace_size",
            "fused_launches", "dispatch_fused", "set_sweep_rate", "get_sweep_rate",

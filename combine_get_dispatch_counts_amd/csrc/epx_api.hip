@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <new>
 
 #include <hip/hip_runtime.h>
@@ -50,6 +51,37 @@ int launched(hipError_t e) { return e == hipSuccess ? EPX_OK : EPX_EHIP; }
 
 }  // namespace
 
+// The workspace of epx_get_dispatch_layout_noalloc, for callers that cannot
+// allocate: a device array that each GPU the library runs on holds (its own
+// copy) until the process ends. In host code its name stands for no device
+// address: kernels and fills only ever get the address from
+// hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[EPX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on `device` (the current device), found
+// on the first call for that device and kept.
+int noalloc_scratch_setup(int device, void **ptr)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return EPX_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return EPX_EHIP;
+        g_scratch_ptr[device] = p;
+    }
+    *ptr = g_scratch_ptr[device];
+    return EPX_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -80,7 +112,8 @@ int epx_create(epx_ctx **out, int device)
             hipDeviceGetAttribute(&c->wclk_khz, hipDeviceAttributeWallClockRate, device) !=
                 hipSuccess ||
             hipMalloc(reinterpret_cast<void **>(&c->dev), sizeof(epx::CtxDev)) != hipSuccess ||
-            hipMemset(c->dev, 0, sizeof(epx::CtxDev)) != hipSuccess) {
+            hipMemset(c->dev, 0, sizeof(epx::CtxDev)) != hipSuccess ||
+            noalloc_scratch_setup(device, &c->scratch) != EPX_OK) {
             if (c->dev)
                 (void)hipFree(c->dev);
             delete c;
@@ -221,6 +254,37 @@ int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K,
         return rc;
     if (ws_bytes < epx::layout_workspace_bytes(T, E, R))
         return EPX_ECAPACITY;
+    return launched(epx::launch_layout(a, stream));
+}
+
+int epx_get_dispatch_layout_noalloc(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int E,
+                                    int R, int C, int32_t *num_tokens_per_expert,
+                                    int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank,
+                                    int32_t *rank_off, int32_t *exp_off, int32_t *pos_in_rank,
+                                    int32_t *slot_in_expert, int32_t *channel_prefix,
+                                    int32_t *totals, int32_t *totals_host_mapped,
+                                    hipStream_t stream)
+{
+    if (!ctx)
+        return EPX_EINVAL;
+    epx::LayoutArgs a;
+    const int rc = layout_args(ctx, topk_idx, T, K, E, R, C, num_tokens_per_expert,
+                               num_tokens_per_rank, is_token_in_rank, rank_off, exp_off,
+                               pos_in_rank, slot_in_expert, channel_prefix, totals,
+                               totals_host_mapped, ctx->scratch, a);
+    if (rc != EPX_OK)
+        return rc;
+    const size_t need = epx::layout_workspace_bytes(T, E, R);
+    if (need > EPX_NOALLOC_SCRATCH_BYTES)
+        return EPX_ECAPACITY;
+    // the array keeps what the last call left: the part this call uses
+    // starts from zero (a fill kernel, so a captured graph may hold it)
+    if (a.ntiles > 1) {
+        const hipError_t e = epx::launch_fill_i32(static_cast<int32_t *>(ctx->scratch),
+                                                  (int64_t)(need / sizeof(int32_t)), 0, stream);
+        if (e != hipSuccess)
+            return EPX_EHIP;
+    }
     return launched(epx::launch_layout(a, stream));
 }
 

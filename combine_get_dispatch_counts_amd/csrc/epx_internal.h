@@ -34,6 +34,7 @@ struct epx_ctx {
     int wclk_khz;            // rate of the device's constant wall clock (wall_clock64)
     int sweep_gbps[2];       // paced row-store sweep rate for bf16 and FP8 rows (0: off)
     std::atomic<unsigned> stamp_seq;  // next slot of the stamp ring
+    void *scratch;           // device address of this device's no-alloc scratch array
 };
 
 namespace epx {

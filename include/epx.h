@@ -66,6 +66,7 @@ extern "C" {
 #define EPX_MAX_EXPERTS 512
 #define EPX_MAX_RANKS 64
 #define EPX_MAX_SWEEP_GBPS 100000
+#define EPX_NOALLOC_SCRATCH_BYTES (1u << 20) /* see epx_get_dispatch_layout_noalloc */
 
 typedef struct epx_ctx epx_ctx;
 
@@ -190,6 +191,29 @@ int epx_get_dispatch_layout(epx_ctx *ctx, const int64_t *topk_idx, int T, int K,
                             int32_t *slot_in_expert, int32_t *channel_prefix,
                             int32_t *totals, int32_t *totals_host_mapped, void *ws,
                             size_t ws_bytes, hipStream_t stream);
+
+/* epx_get_dispatch_layout with no workspace argument, for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Arguments and outputs are those of
+ * epx_get_dispatch_layout without ws / ws_bytes; nothing is allocated: the
+ * workspace is a fixed array of EPX_NOALLOC_SCRATCH_BYTES bytes in device
+ * memory that each GPU holds from the library's load until the process
+ * ends, its address found once per device by epx_create. Each call first
+ * clears the part it uses (a fill kernel on `stream`, so the pair may be
+ * captured in a graph), so an earlier call's state, even one that set
+ * EPX_DEV_WORKSPACE, never carries over. A shape whose workspace
+ * (epx_workspace_size) exceeds the array returns EPX_ECAPACITY with nothing
+ * launched: 1 MiB covers about 116 000 tokens at E = 256, R = 32. Every call
+ * on one GPU shares the array: calls that overlap on one GPU (other
+ * streams, other threads, other contexts) race and their outputs are not
+ * valid. */
+int epx_get_dispatch_layout_noalloc(epx_ctx *ctx, const int64_t *topk_idx, int T, int K, int E,
+                                    int R, int C, int32_t *num_tokens_per_expert,
+                                    int32_t *num_tokens_per_rank, uint8_t *is_token_in_rank,
+                                    int32_t *rank_off, int32_t *exp_off, int32_t *pos_in_rank,
+                                    int32_t *slot_in_expert, int32_t *channel_prefix,
+                                    int32_t *totals, int32_t *totals_host_mapped,
+                                    hipStream_t stream);
 
 /* High-throughput dispatch: the rank-deduplicated pack and the local permute
  * into expert-contiguous blocks, reading x once. [P2] "dispatch 过程" (each
