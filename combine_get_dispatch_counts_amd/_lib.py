@@ -35,6 +35,7 @@ SIGNATURES = {
     "epx_get_dispatch_layout_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I] + [_P] * 10 + [_P]),
     "epx_dispatch": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I] + [_P] * 4 + [_I]
                      + [_P] * 5 + [_I64] + [_P] * 3 + [_I64, _P, _P]),
+    "epx_permute": (_I, [_P, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _I64, _P, _P]),
     "epx_fused_workspace_size": (_I, [_I, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "epx_fused_launches": (_I, [_P] + [_I] * 6 + [ctypes.POINTER(_I)]),
     "epx_dispatch_fused": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _I] + [_P] * 11 + [_SZ, _I]

@@ -363,34 +363,34 @@ def recv_permute(rows: torch.Tensor, local_topk_idx: torch.Tensor, num_local_exp
     bf16 [N, h], or FP8 codes uint8 [N, h] with ``scales`` [N, stride] fp32;
     ``local_topk_idx`` [N, K] int64 holds each row's local expert indices
     (-1 for entries of other ranks), as dispatch's send_topk_idx does. The
-    payload is copied bit for bit by the dispatch kernel's permute."""
+    layout of those indices, then one epx_permute launch that moves each row
+    and its scale row, bit for bit."""
     dev = rows.device
     _need(local_topk_idx, torch.int64, "local_topk_idx", 2, device=dev)
     N, K = local_topk_idx.shape
-    if scales is not None and scales.device != dev:
-        raise ValueError(f"scales are on {scales.device}, the rows on {dev}")
     L = num_local_experts
+    for name, pl in (("rows", rows), ("scales", scales)):
+        if pl is None:
+            continue
+        if not pl.is_cuda or pl.device != dev or not pl.is_contiguous() or pl.dim() != 2 \
+                or pl.shape[0] != N:
+            raise ValueError(f"{name} must be a contiguous 2-d tensor on {dev} with one row "
+                             "per received row")
     lay = get_dispatch_layout(local_topk_idx, L, 1)
     cap = N * K
-    payloads = [rows] + ([scales] if scales is not None else [])
-    outs = []
+    row_bytes = rows.shape[1] * rows.element_size()
+    side_bytes = scales.shape[1] * scales.element_size() if scales is not None else 0
+    out = torch.empty((cap, rows.shape[1]), dtype=rows.dtype, device=dev)
+    out_side = (torch.empty((cap, scales.shape[1]), dtype=scales.dtype, device=dev)
+                if scales is not None else None)
     pos = torch.empty((N, K), dtype=torch.int32, device=dev)
     src_row = torch.empty(cap, dtype=torch.int32, device=dev)
-    for pl in payloads:
-        if not pl.is_cuda or not pl.is_contiguous() or pl.dim() != 2 or pl.shape[0] != N:
-            raise ValueError("payload rows must be a contiguous 2-d GPU tensor with one row "
-                             "per received row")
-        v = pl.view(torch.uint8).view(N, -1).view(torch.bfloat16)
-        hh = v.shape[1]
-        out = torch.empty((cap, hh), dtype=torch.bfloat16, device=dev)
-        rc = _lib.load().epx_dispatch(
-            _ctx(dev), _p(v), hh, _p(local_topk_idx), None, N, K, L, 1, None,
-            _p(lay.exp_off), None, _p(lay.slot_in_expert), 0, None, None, None, None, None, 0,
-            _p(out), None, _p(src_row), cap, _p(pos), _stream(dev))
-        check(rc, "epx_dispatch (permute)")
-        outs.append(out.view(torch.uint8).view(cap, -1).view(pl.dtype))
-    return Received(x=outs[0], scales=outs[1] if scales is not None else None, src_row=src_row,
-                    pos=pos, layout=lay)
+    rc = _lib.load().epx_permute(
+        _ctx(dev), _p(rows), row_bytes, _p(scales), side_bytes, _p(local_topk_idx), N, K, L,
+        _p(lay.exp_off), _p(lay.slot_in_expert), _p(out), _p(out_side), _p(src_row), cap,
+        _p(pos), _stream(dev))
+    check(rc, "epx_permute")
+    return Received(x=out, scales=out_side, src_row=src_row, pos=pos, layout=lay)
 
 
 def fused_workspace_size(T: int, K: int, E: int, R: int) -> int:

@@ -205,13 +205,69 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a,
     }
 }
 
-__global__ __launch_bounds__(256) void fill_lines_kernel(u32x4 *p, uint32_t v)
+// The receiver's local permute in one launch: one wave per received row n,
+// which loads the row (16 bytes per lane per vector) and its side row (at
+// most 64 vectors, e.g. its FP8 scales), works out its destinations from
+// lane k < K -- entry k's local expert e, row exp_off[e] + slot[n, k] --
+// and stores both to every destination, with the handle and the source row.
+// Rows are copied bit for bit (any payload); nontemporal stores: nothing
+// here reads them back.
+template <int NV>
+__global__ __launch_bounds__(kWave) void permute_kernel(PermuteArgs a)
+{
+    const int n = blockIdx.x, lane = threadIdx.x;
+    const int64_t nk = (int64_t)n * a.K;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.rows) +
+                                                        (size_t)n * a.row_vecs * 16);
+    RowBf16<NV> row;
+    row.load(src, 0, a.row_vecs);
+    const u32x4 side = lane < a.side_vecs
+                           ? load16_stream(static_cast<const char *>(a.side) +
+                                           ((size_t)n * a.side_vecs + lane) * 16)
+                           : u32x4{0u, 0u, 0u, 0u};
+    const int64_t e = lane < a.K ? a.idx[nk + lane] : -1;
+    int dst = -1;
+    if (lane < a.K) {
+        if (e >= 0 && e < a.L) {
+            const int64_t r = (int64_t)a.exp_off[(int)e] + a.slot[nk + lane];
+            if (r >= 0 && r < a.cap)
+                dst = (int)r;
+            else
+                flag_error(a.err, EPX_DEV_OVERFLOW);
+        } else if (e != -1) {
+            flag_error(a.err, EPX_DEV_BAD_ROUTE);
+        }
+        a.pos[nk + lane] = dst;
+        if (dst >= 0)
+            a.src_row[dst] = n;
+    }
+    const uint64_t dbits = uniform64(__ballot(dst >= 0));
+    char *out = static_cast<char *>(a.out_rows);
+    for (int v0 = 0; v0 < a.row_vecs; v0 += RowBf16<NV>::kPerPass) {
+        if (v0 > 0)
+            row.load(src, v0, a.row_vecs);
+        for (uint64_t m = dbits; m; m &= m - 1) {
+            const int r = readlane(dst, __builtin_ctzll(m));
+            row.template store<StorePolicy::NT>(out + (size_t)r * a.row_vecs * 16, v0,
+                                                a.row_vecs);
+        }
+    }
+    if (a.side_vecs > 0)
+        for (uint64_t m = dbits; m; m &= m - 1) {
+            const int r = readlane(dst, __builtin_ctzll(m));
+            if (lane < a.side_vecs)
+                store16_stream(static_cast<char *>(a.out_side) +
+                                   ((size_t)r * a.side_vecs + lane) * 16, side);
+        }
+}
+
+__global__ __launch_bounds__(kWave) void fill_lines_kernel(u32x4 *p, uint32_t v)
 {
     u32x4 *blk = p + (size_t)blockIdx.x * (kFillBlockBytes / 16);
     const u32x4 val = u32x4{v, v, v, v};
 #pragma unroll
-    for (int j = 0; j < (int)(kFillBlockBytes / 16 / 256); ++j)
-        blk[j * 256 + threadIdx.x] = val;
+    for (int j = 0; j < (int)(kFillBlockBytes / 16 / kWave); ++j)
+        blk[j * kWave + threadIdx.x] = val;
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
@@ -331,6 +387,20 @@ hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream)
     return hipGetLastError();
 }
 
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream)
+{
+    if (a.N == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)a.N), block(kWave);
+    if (a.row_vecs <= 8 * kWave)
+        hipLaunchKernelGGL(permute_kernel<8>, grid, block, 0, stream, a);
+    else if (a.row_vecs <= 14 * kWave)
+        hipLaunchKernelGGL(permute_kernel<14>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(permute_kernel<16>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_lines(void *p, size_t n, uint32_t v, hipStream_t stream)
 {
     const size_t blocks = n / kFillBlockBytes;
@@ -338,7 +408,7 @@ hipError_t launch_fill_lines(void *p, size_t n, uint32_t v, hipStream_t stream)
         return hipSuccess;
     if (blocks > 0x7FFFFFFFu)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fill_lines_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(fill_lines_kernel, dim3((unsigned)blocks), dim3(kWave), 0, stream,
                        static_cast<u32x4 *>(p), v);
     return hipGetLastError();
 }

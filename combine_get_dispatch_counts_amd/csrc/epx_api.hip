@@ -377,6 +377,37 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
     return launched(epx::launch_dispatch(a, fp8 != 0, ctx->cus, &ctx->stamp_seq, stream));
 }
 
+int epx_permute(epx_ctx *ctx, const void *rows, int row_bytes, const void *side, int side_bytes,
+                const int64_t *local_topk_idx, int N, int K, int L, const int32_t *exp_off,
+                const int32_t *slot_in_expert, void *out_rows, void *out_side,
+                int32_t *src_row, int64_t cap_rows, int32_t *pos, hipStream_t stream)
+{
+    const int rc = check_ctx(ctx);
+    if (rc != EPX_OK)
+        return rc;
+    if (N < 0 || K < 1 || K > EPX_MAX_TOPK || L < 1 || L > EPX_MAX_EXPERTS || cap_rows < 0 ||
+        cap_rows > INT32_MAX || (int64_t)N * K > INT32_MAX)
+        return EPX_EINVAL;
+    if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > (1 << 20) || side_bytes < 0 ||
+        side_bytes % 16 != 0 || side_bytes > 16 * 64)
+        return EPX_EINVAL;
+    if (N > 0) {
+        if (!rows || !local_topk_idx || !exp_off || !slot_in_expert || !out_rows || !src_row ||
+            !pos || (side_bytes > 0 && (!side || !out_side)))
+            return EPX_EINVAL;
+        if (!aligned16(rows) || !aligned16(out_rows) ||
+            (side_bytes > 0 && (!aligned16(side) || !aligned16(out_side))))
+            return EPX_EINVAL;
+    }
+    epx::PermuteArgs a{};
+    a.rows = rows; a.side = side; a.row_vecs = row_bytes / 16; a.side_vecs = side_bytes / 16;
+    a.idx = local_topk_idx; a.N = N; a.K = K; a.L = L;
+    a.exp_off = exp_off; a.slot = slot_in_expert;
+    a.out_rows = out_rows; a.out_side = out_side; a.src_row = src_row; a.pos = pos;
+    a.cap = cap_rows; a.err = ctx->d_err;
+    return launched(epx::launch_permute(a, stream));
+}
+
 int epx_set_sweep_rate(epx_ctx *ctx, int bf16_gbps, int fp8_gbps)
 {
     if (!ctx || bf16_gbps < 0 || fp8_gbps < 0 || bf16_gbps > EPX_MAX_SWEEP_GBPS ||
@@ -412,33 +443,35 @@ int epx_calibrate_sweep_rate(epx_ctx *ctx, void *scratch, size_t bytes, int *fil
                 (void)hipEventDestroy(e);
         return EPX_EHIP;
     }
-    // two warm-up fills, then the median of five timed ones
-    float ms[5];
+    // three warm-up fills, then the median of nine timed ones
+    constexpr int kWarm = 3, kTimed = 9;
+    float ms[kTimed];
     rc = EPX_OK;
-    for (int i = 0; i < 7 && rc == EPX_OK; ++i) {
-        const bool timed = i >= 2;
+    for (int i = 0; i < kWarm + kTimed && rc == EPX_OK; ++i) {
+        const bool timed = i >= kWarm;
         if (timed && hipEventRecord(ev[0], stream) != hipSuccess)
             rc = EPX_EHIP;
         if (rc == EPX_OK && epx::launch_fill_lines(scratch, n, (uint32_t)i, stream) != hipSuccess)
             rc = EPX_EHIP;
         if (rc == EPX_OK && timed &&
             (hipEventRecord(ev[1], stream) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess ||
-             hipEventElapsedTime(&ms[i - 2], ev[0], ev[1]) != hipSuccess))
+             hipEventElapsedTime(&ms[i - kWarm], ev[0], ev[1]) != hipSuccess))
             rc = EPX_EHIP;
     }
     (void)hipEventDestroy(ev[0]);
     (void)hipEventDestroy(ev[1]);
     if (rc != EPX_OK)
         return rc;
-    for (int i = 1; i < 5; ++i)  // insertion sort of five
+    for (int i = 1; i < kTimed; ++i)  // insertion sort
         for (int j = i; j > 0 && ms[j] < ms[j - 1]; --j) {
             const float t = ms[j];
             ms[j] = ms[j - 1];
             ms[j - 1] = t;
         }
-    if (!(ms[2] > 0.0f))
+    const float med = ms[kTimed / 2];
+    if (!(med > 0.0f))
         return EPX_EHIP;
-    const double gbps = (double)n / (ms[2] * 1e-3) / 1e9;
+    const double gbps = (double)n / (med * 1e-3) / 1e9;
     const double b = gbps * epx::kCalibBf16Permille / 1000.0, f = gbps * epx::kCalibFp8Permille / 1000.0;
     ctx->sweep_gbps[0] = b > EPX_MAX_SWEEP_GBPS ? EPX_MAX_SWEEP_GBPS : (int)b;
     ctx->sweep_gbps[1] = f > EPX_MAX_SWEEP_GBPS ? EPX_MAX_SWEEP_GBPS : (int)f;

@@ -40,10 +40,13 @@ struct epx_ctx {
 namespace epx {
 
 // Default rates of the paced sweep of the high-throughput dispatch's row
-// stores (GB/s of destination rows), measured on MI355X at the prefill shape:
-// just below the rate at which the paced front outruns the memory system.
+// stores (GB/s of destination rows), measured on MI355X at the prefill
+// shapes: just below the rate at which the paced front outruns the memory
+// system (bf16, T = 4096: 153.6 us at 6300, 166 at 6400; FP8: T = 4096
+// best at 6000-6100, T = 16384 in chunks 401.5-402.3 us at 6100, 407.5 at
+// 6000).
 constexpr int kSweepGBpsBf16 = 6300;
-constexpr int kSweepGBpsFp8 = 6000;
+constexpr int kSweepGBpsFp8 = 6100;
 // Pacing delays every wave from its own start, which costs a few
 // microseconds; it repays that only once the rows no longer fit in the
 // memory-side cache (256 MiB on MI355X) and must reach HBM within the launch.
@@ -62,9 +65,10 @@ constexpr int kSweepMaxChannels = 8192;
 
 // Calibration (epx_calibrate_sweep_rate): the sweep rates as a fraction of
 // the same device's sequential fill rate, measured with launch_fill_lines
-// over a buffer larger than the memory-side cache.
-constexpr int kCalibBf16Permille = 915;
-constexpr int kCalibFp8Permille = 870;
+// over a buffer larger than the memory-side cache: the defaults above over
+// the 6.75 TB/s that fill reached on the GPU they were measured on.
+constexpr int kCalibBf16Permille = 933;
+constexpr int kCalibFp8Permille = 904;
 constexpr size_t kCalibMinBytes = 512ull << 20;
 
 // The multiplier of floor(e / L) = e * m >> 20 for 0 <= e < 512 and
@@ -171,6 +175,22 @@ inline int next_stamp_slot(std::atomic<unsigned> *seq)
 hipError_t launch_dispatch(const DispatchArgs &a, bool fp8, int cus, std::atomic<unsigned> *seq,
                            hipStream_t stream);
 
+// The receiver's permute (epx_permute): N rows of row_vecs 16-byte vectors
+// and side rows of side_vecs vectors into per-local-expert blocks.
+struct PermuteArgs {
+    const void *rows, *side;
+    int row_vecs, side_vecs;
+    const int64_t *idx;  // [N, K] local expert indices
+    int N, K, L;
+    const int32_t *exp_off, *slot;
+    void *out_rows, *out_side;
+    int32_t *src_row, *pos;
+    int64_t cap;
+    int *err;
+};
+
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream);
+
 struct LLArgs {
     const uint16_t *x;
     const int64_t *topk_idx;
@@ -201,9 +221,11 @@ hipError_t fused_launches(const FusedArgs &f, bool fp8, int *launches);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t stream);
 
 // A sequential fill of n bytes (a multiple of kFillBlockBytes) with the
-// word v: each block of 256 threads writes one contiguous kFillBlockBytes
-// chunk with 16-byte stores, chunks in block order.
-constexpr size_t kFillBlockBytes = 16384;
+// word v: each one-wave block writes one contiguous kFillBlockBytes chunk
+// with 16-byte stores, chunks in block order (of the fill patterns measured
+// on MI355X, 4 KB per wave is the fastest: 6.75-6.79 TB/s, against 6.0-6.1
+// for 16 KB per 256-thread block and 6.5-6.6 for hipMemsetD32).
+constexpr size_t kFillBlockBytes = 4096;
 hipError_t launch_fill_lines(void *p, size_t n, uint32_t v, hipStream_t stream);
 
 struct CombineArgs {

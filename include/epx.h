@@ -109,7 +109,7 @@ const char *epx_strerror(int code);
  * the device holds fewer waves than its occupancy query reported -- stores
  * its rows unpaced instead of waiting for times already past, so such a
  * wave costs at most that much plus its own unpaced stores (outputs are
- * unaffected either way). Defaults, measured on MI355X: 6300 (bf16) and 6000 (FP8);
+ * unaffected either way). Defaults, measured on MI355X: 6300 (bf16) and 6100 (FP8);
  * epx_calibrate_sweep_rate derives them from the device instead. The
  * setting is per context and read at each call. EPX_EINVAL for a NULL
  * context or a rate outside [0, EPX_MAX_SWEEP_GBPS]. */
@@ -122,9 +122,9 @@ int epx_get_sweep_rate(epx_ctx *ctx, int *bf16_gbps, int *fp8_gbps);
 /* Set the sweep rates from this device's own memory: times a sequential
  * fill of `scratch` (device memory of `bytes` >= 512 MiB, larger than the
  * memory-side cache, 16-byte aligned; its contents are overwritten) on
- * `stream` -- two untimed fills, then the median of five -- and sets the
- * bf16 and FP8 rates to 91.5% and 87% of that fill rate (the ratios of the
- * defaults above to the fill rate of the GPU they were measured on).
+ * `stream` -- three untimed fills, then the median of nine -- and sets the
+ * bf16 and FP8 rates to 93.3% and 90.4% of that fill rate (the ratios of
+ * the defaults above to the fill rate of the GPU they were measured on).
  * *fill_gbps (host, may be NULL) receives the measured fill rate in GB/s.
  * Unlike every other call, this one waits for the stream; call it once,
  * outside any graph capture. EPX_EINVAL for a bad scratch, EPX_EHIP if a
@@ -262,6 +262,31 @@ int epx_dispatch(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *topk_idx
                  int64_t send_cap_rows, void *recv_x, float *recv_scales,
                  int32_t *recv_src, int64_t recv_cap_rows, int32_t *pos_exp,
                  hipStream_t stream);
+
+/* The receiver's local permute, in one launch. [P1] "高吞吐量模式：协调阶段
+ * 与紧凑缓冲区": a destination receives exact-size rows from its sources
+ * and arranges them locally into contiguous per-expert blocks for the
+ * grouped GEMM. N received rows (row n: the token's payload, copied bit for
+ * bit -- bf16 or FP8 codes alike) go, for each entry k of local_topk_idx
+ * [N,K] (local expert index in [0, L), or -1 = the entry belongs to another
+ * rank), to row exp_off[e] + slot_in_expert[n,k] of out_rows, where
+ * exp_off / slot_in_expert come from epx_get_dispatch_layout over
+ * local_topk_idx with E = L, R = 1 (rows in received order inside each
+ * expert's block); a side row per received row (e.g. its FP8 scale row, 0
+ * to 1024 bytes) travels with it to out_side.
+ * In:  rows [N, row_bytes] (row_bytes a multiple of 16, at most 1 MiB),
+ *      side [N, side_bytes] (side_bytes a multiple of 16, or 0: side and
+ *      out_side may be NULL), both 16-byte aligned; 1 <= K <= 32,
+ *      1 <= L <= 512.
+ * Out: out_rows [cap_rows, row_bytes], out_side [cap_rows, side_bytes],
+ *      src_row [cap_rows] (the received row each output row holds),
+ *      pos [N,K] (the output row of (n,k), or -1). A row index outside
+ *      [0, cap_rows) is not written and sets EPX_DEV_OVERFLOW; an entry
+ *      outside [-1, L) sets EPX_DEV_BAD_ROUTE and is skipped. */
+int epx_permute(epx_ctx *ctx, const void *rows, int row_bytes, const void *side, int side_bytes,
+                const int64_t *local_topk_idx, int N, int K, int L, const int32_t *exp_off,
+                const int32_t *slot_in_expert, void *out_rows, void *out_side,
+                int32_t *src_row, int64_t cap_rows, int32_t *pos, hipStream_t stream);
 
 /* Workspace bytes epx_dispatch_fused needs for (T, K, E, R) (host out): the
  * same as the layout's (epx_workspace_size), whose head and per-tile words

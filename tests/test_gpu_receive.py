@@ -181,3 +181,65 @@ def test_two_level_dedup_node_then_rank(fp8):
             _eq(got, o["send_x"][fa:fb], f"rank {r} rows")
             _eq(host_bits(d2.send_topk_idx)[a2:b2], o["send_topk_idx"][fa:fb], f"rank {r} indices")
             _eq(host_bits(d2.send_topk_w)[a2:b2], o["send_topk_w"][fa:fb], f"rank {r} weights")
+
+
+def test_permute_side_rows_and_errors():
+    """epx_permute on its own: rows of an odd width (48 bytes) with 64-byte
+    side rows, every entry to its local-expert block in received order, the
+    side row with it; an entry outside [-1, L) sets EPX_DEV_BAD_ROUTE and is
+    skipped, and a capacity one row short sets EPX_DEV_OVERFLOW and writes
+    nothing past it."""
+    import ctypes
+
+    import combine_get_dispatch_counts_amd as epx
+    from combine_get_dispatch_counts_amd import _lib
+
+    N, K, L = 300, 3, 5
+    rng = np.random.default_rng(5)
+    idx = rng.integers(-1, L, (N, K)).astype(np.int64)
+    rows = rng.integers(0, 256, (N, 48), dtype=np.uint8)
+    side = rng.integers(0, 256, (N, 64), dtype=np.uint8)
+    o = oracle.layout(idx, L, 1)
+    n_out = int(o["totals"][1])
+    dev = torch.device("cuda")
+    lib = _lib.load()
+
+    def run(idx_np, cap):
+        tk = torch.from_numpy(idx_np).to(dev)
+        lay = epx.get_dispatch_layout(tk, L, 1)
+        out = torch.full((cap + 2, 48), CANARY, dtype=torch.uint8, device=dev)
+        out_side = torch.full((cap + 2, 64), CANARY, dtype=torch.uint8, device=dev)
+        src = torch.full((cap + 2,), -9, dtype=torch.int32, device=dev)
+        pos = torch.empty((N, K), dtype=torch.int32, device=dev)
+        r = torch.from_numpy(rows).to(dev)
+        sd = torch.from_numpy(side).to(dev)
+        rc = lib.epx_permute(epx.api._ctx(dev), ctypes.c_void_p(r.data_ptr()), 48,
+                             ctypes.c_void_p(sd.data_ptr()), 64, ctypes.c_void_p(tk.data_ptr()),
+                             N, K, L, ctypes.c_void_p(lay.exp_off.data_ptr()),
+                             ctypes.c_void_p(lay.slot_in_expert.data_ptr()),
+                             ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(out_side.data_ptr()),
+                             ctypes.c_void_p(src.data_ptr()), cap, ctypes.c_void_p(pos.data_ptr()),
+                             epx.api._stream(dev))
+        assert rc == 0
+        return epx.get_error(), host_bits(out), host_bits(out_side), host_bits(src), host_bits(pos)
+
+    say(f"epx_permute N={N} K={K} L={L}, 48-byte rows, 64-byte side rows")
+    flags, out, out_side, src, pos = run(idx, n_out)
+    assert flags == 0
+    order = np.argsort(np.where(idx >= 0, idx, L).ravel(), kind="stable")[:n_out]
+    want_src = (order // K).astype(np.int32)
+    _eq(src[:n_out], want_src, "src_row")
+    _eq(out[:n_out], rows[want_src], "rows")
+    _eq(out_side[:n_out], side[want_src], "side rows")
+    assert (out[n_out:] == CANARY).all() and (src[n_out:] == -9).all()
+    want_pos = np.full(N * K, -1, np.int32)
+    want_pos[order] = np.arange(n_out, dtype=np.int32)
+    _eq(pos.ravel(), want_pos, "pos")
+
+    bad = idx.copy()
+    bad[7, 1] = L  # outside [-1, L): skipped and flagged by the layout and the permute
+    flags, *_ = run(bad, n_out)
+    assert flags & _lib.DEV_BAD_ROUTE
+    flags, out, _, src, _ = run(idx, n_out - 1)
+    assert flags & _lib.DEV_OVERFLOW
+    assert (out[n_out - 1:] == CANARY).all() and (src[n_out - 1:] == -9).all()

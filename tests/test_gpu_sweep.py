@@ -16,7 +16,7 @@ from _gpu import host_bits, say
 
 pytestmark = pytest.mark.gpu
 
-DEFAULTS = (6300, 6000)  # the rates a new context starts with (include/epx.h)
+DEFAULTS = (6300, 6100)  # the rates a new context starts with (include/epx.h)
 
 
 def _run(epx, inp, fused, fp8, bufs, lay_buf, ws):
@@ -214,7 +214,7 @@ def test_calibrated_sweep_rate():
         b, f = epx.get_sweep_rate()
         say(f"calibration: fill {fill} GB/s -> sweep rates {b} (bf16), {f} (FP8)")
         assert 2000 < fill < 20000, fill
-        assert b == int(fill * 0.915) or abs(b - fill * 0.915) <= 1
-        assert f == int(fill * 0.870) or abs(f - fill * 0.870) <= 1
+        assert abs(b - fill * 0.933) <= 2, (b, fill)
+        assert abs(f - fill * 0.904) <= 2, (f, fill)
     finally:
         epx.set_sweep_rate(*prior)
