@@ -107,8 +107,7 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a,
     constexpr int per = decltype(row)::kPerPass;  // 1024 channels
     const int nitems = FP8 ? a.h >> 4 : a.h >> 3;
     const int nslices = (nitems + per - 1) / per;
-    if (have_token && wj < nslices)
-        row.load(src, wj * per, nitems);
+    row.load(src, wj * per, have_token ? nitems : 0);  // zeros past the row
 
     for (int i = tid; i < 2 * a.E; i += nthreads)
         hist[i] = 0;

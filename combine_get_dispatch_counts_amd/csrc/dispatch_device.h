@@ -39,13 +39,13 @@ template <int NV>
 struct RowBf16 {
     static constexpr int kPerPass = NV * kWave;
     u32x4 r[NV];
+    // vectors v0 + u * 64 + lane of a row of nvec vectors; zeros past its end
     __device__ __forceinline__ void load(const u32x4 *src, int v0, int nvec)
     {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, (uint32_t)nvec * 16u);
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int v = v0 + u * kWave + lane_id();
-            r[u] = (v < nvec) ? load16_stream(src + v) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < NV; ++u)
+            r[u] = load16_row(rs, (uint32_t)(v0 + u * kWave + lane_id()) * 16u);
     }
     __device__ __forceinline__ void quantise(int, int) {}
     template <StorePolicy POL = StorePolicy::WT>
@@ -173,14 +173,16 @@ struct RowFp8 {
     int n_sv;   // lanes holding a slice of the (padded) scale row in this pass
     // Issue the pass's loads; quantise() consumes them, so work placed in
     // between overlaps their latency.
+    // segments s0 + u * 64 + lane of a row of nseg segments; zeros past its
+    // end (whole 8-lane groups, as nseg is a multiple of 8)
     __device__ __forceinline__ void load(const u32x4 *src, int s0, int nseg)
     {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, (uint32_t)nseg * 32u);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int sg = s0 + u * kWave + lane_id();
-            const bool active = sg < nseg;  // uniform over each 8-lane group
-            lo[u] = active ? load16_stream(src + 2 * sg) : u32x4{0u, 0u, 0u, 0u};
-            hi[u] = active ? load16_stream(src + 2 * sg + 1) : u32x4{0u, 0u, 0u, 0u};
+            const uint32_t off = (uint32_t)(s0 + u * kWave + lane_id()) * 32u;
+            lo[u] = load16_row(rs, off);
+            hi[u] = load16_row(rs, off + 16u);
         }
     }
     __device__ __forceinline__ void quantise(int s0, int nseg)

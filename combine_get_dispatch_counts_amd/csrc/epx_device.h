@@ -60,6 +60,22 @@ __device__ __forceinline__ u32x4 load16_stream(const void *p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// Loads of a row of `bytes` bytes (a multiple of 16) through a raw buffer
+// descriptor built from the row base: a 16-byte load at an offset at or past
+// the end returns zeros without touching memory, so the loads of a row need
+// no branches, and with none the compiler counts them exactly when it places
+// its waits (a guarded load per vector made it wait for the whole row before
+// the first use of anything loaded earlier). Nontemporal hint.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load16_row(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2 /* nt */);
+}
+
 __device__ __forceinline__ void store16_stream(void *p, u32x4 v)
 {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));

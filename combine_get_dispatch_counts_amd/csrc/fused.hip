@@ -42,12 +42,15 @@
 // query, fits on the chip at once; small batches go to fused_small_kernel
 // below, and everything else runs the layout and the dispatch as two
 // launches, whose 64-thread dispatch blocks spread one wave per token over
-// the chip and free their place wave by wave. Every block issues its
-// counting loads, then its rows' loads, before it waits, so the loads
-// overlap the hand-over. Every wait is bounded. Each wave then stores its
-// token's rows on the paced sweep (dispatch_device.h), its schedule starting
-// when its block's hand-over is complete (a shared start time was measured:
-// the rows due before most blocks are ready go out as one random burst).
+// the chip and free their place wave by wave. A block loads its tokens'
+// rows only once it has counted (and, if it publishes, published): rows
+// loaded at entry went out ahead of the counting loads, and the publishers
+// every block waits for finished counting 5 us later; loaded after the
+// publish, they still overlap the hand-over. Every wait is bounded. Each
+// wave then stores its token's rows on the paced sweep (dispatch_device.h),
+// its schedule starting when its block's hand-over is complete (a shared
+// start time was measured: the rows due before most blocks are ready go out
+// as one random burst).
 #include <atomic>
 
 #include "dispatch_device.h"
@@ -106,10 +109,9 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     const bool have = t < T;
     const bool publisher = (int)blockIdx.x < l.ntiles;
 
-    // Loads first, the counting entries ahead of the row: the call number;
-    // threads below kLayoutTile take the tokens of the block's own tile
-    // before t0, the others (publishers only) the tokens of tile blockIdx;
-    // lane k < K the token's entry k; then the token's row.
+    // Loads first: the call number; threads below kLayoutTile take the
+    // tokens of the block's own tile before t0, the others (publishers only)
+    // the tokens of tile blockIdx; lane k < K the token's entry k.
     if (tid == 0) {
         uint32_t tg;
         s_go = read_call_tag(l.hdr, &tg);  // false: the workspace was not left ready
@@ -128,10 +130,6 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
             eu[k] = -1;
     }
     const int64_t e = (have && lane < K) ? a.topk_idx[(int64_t)t * K + lane] : -1;
-    typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
-    const uint16_t *xrow = a.x + (size_t)(have ? t : 0) * a.h;
-    if (have)
-        row.load(reinterpret_cast<const u32x4 *>(xrow), 0, FP8 ? a.h >> 4 : a.h >> 3);
 
     // the token's rank bits and entries, for the tokens after it in the block
     const bool valid = lane < K && e >= 0 && e < E;
@@ -174,6 +172,13 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
         for (int c = tid; c < ER; c += blockDim.x)
             pub_store(prow + c, ((uint64_t)tag << 32) | (uint32_t)agg[c]);
     }
+
+    // the token's row, only now: rows loaded at entry filled the memory
+    // queues ahead of the counting loads (first touches of topk_idx), and
+    // the publishers, which every block waits for, counted behind them
+    typename std::conditional<FP8, RowFp8<NV>, RowBf16<NV>>::type row;
+    const uint16_t *xrow = a.x + (size_t)(have ? t : 0) * a.h;
+    row.load(reinterpret_cast<const u32x4 *>(xrow), 0, have ? (FP8 ? a.h >> 4 : a.h >> 3) : 0);
 
     // every tile's counts: the totals and this tile's prefix (bounded waits)
     bool ok = true;
@@ -289,8 +294,7 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_small_kernel(FusedArgs f
     const int nslices = (nitems + per - 1) / per;
     const uint16_t *xrow = a.x + (size_t)t * a.h;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(xrow);
-    if (w < nslices)
-        row.load(src, w * per, nitems);
+    row.load(src, w * per, nitems);  // zeros past the row
 
     for (int i = tid; i < 2 * (E + R); i += blockDim.x)
         cnt[i] = 0;  // cnt and before
