@@ -713,12 +713,12 @@ def main():
     assert epx.get_error() == 0
     n_rank, n_exp = (int(v) for v in lay.totals.cpu())
 
-    # The MALL flush: a read of flush_mb MB (a reduction over a scratch
-    # buffer) before each timed step, outside its events; a read leaves the
-    # cache holding clean lines only, so nothing is written back inside the
-    # step.
+    # The MALL flush: a read of flush_mb MB (a float32 sum over a scratch
+    # buffer, the fastest of torch's reductions here) before each timed step,
+    # outside its events; a read leaves the cache holding clean lines only,
+    # so nothing is written back inside the step.
     if args.flush_mb > 0:
-        flush_buf = torch.ones(args.flush_mb << 20, dtype=torch.uint8, device=dev).view(torch.int32)
+        flush_buf = torch.ones(args.flush_mb << 20, dtype=torch.uint8, device=dev).view(torch.float32)
 
         def flush(i):
             flush_buf.sum()
@@ -829,7 +829,6 @@ def main():
         ai, bi = a.view(torch.int32), b.view(torch.int32)
         ceil["rw_kernel_gbs"] = round(
             2 * (1 << 30) / (_loop_us(lambda: torch.add(ai, 0, out=bi), 10) * 1e3), 1)
-        ceil["read_gbs"] = round((1 << 30) / (_loop_us(lambda: ai.sum(), 10) * 1e3), 1)
         del a, b, ai, bi
 
     by = step_bytes(T, h, K, R, n_rank, n_exp)
