@@ -13,12 +13,12 @@
 //     tile into `subs` parts; block (tile, part) writes the output rows of
 //     its part, so the row writes are spread over many compute units. Each
 //     block loads and counts its whole tile, one thread per token.
-//   - Counting uses no returning atomics: each wave ORs its lanes into
-//     per-expert bitmaps and adds per-expert counts in LDS (fire and
-//     forget), and builds its per-rank lane masks with one ballot per rank
-//     (the OR over a token's entries deduplicates ranks). A token's rank in
-//     its wave is a popcount of the bits below it; the earlier waves' counts
-//     give the rest of the tile's prefix.
+//   - Counting is one non-returning LDS OR per entry and per rank: each
+//     wave ORs its lanes into per-expert and per-rank bitmaps (the OR over a
+//     token's entries deduplicates ranks; an expert repeated in a row adds
+//     to a separate per-wave count instead). A count is a popcount of a
+//     bitmap, a token's rank in its wave a popcount of the bits below it,
+//     and the earlier waves' counts give the rest of the tile's prefix.
 //   - Part 0 of each tile publishes the tile's E + R counts; every block
 //     then loads the words of all earlier tiles at once, spread over all of
 //     its threads (tile-major, so the loads are coalesced), and adds them
@@ -67,42 +67,41 @@ __device__ __noinline__ int wave_rank_slow(const LayoutArgs &a, int tile_base, i
 
 // Add the published words of tiles [0, ntiles) into acc[0..ER) (LDS, zeroed
 // before), every thread of the block loading its share of the ntiles * ER
-// words in tile-major order, B at a time; a word that does not yet
-// carry the tag is polled on its own afterwards. Returns false if a word
-// stayed unpublished too long.
+// words in tile-major order, B at a time; the words that do not yet carry
+// the tag are loaded again together until they all do. Returns false if a
+// word stayed unpublished too long.
 template <int B>
 __device__ bool add_tile_words(const uint64_t *pub, int ER, int ntiles, uint32_t tag, int *acc)
 {
     const int n = ntiles * ER, step = (int)blockDim.x;
+    // column of word i0 + q * step: c0 + q * sr, wrapped into [0, ER)
+    const int sr = step % ER;
     for (int i0 = threadIdx.x; i0 < n; i0 += B * step) {
-        uint64_t wv[B];
+        const int c0 = i0 % ER;
+        uint32_t pending = 0;  // this batch's words still to add
 #pragma unroll
         for (int q = 0; q < B; ++q)
-            wv[q] = i0 + q * step < n ? pub_load(pub + i0 + q * step) : 0;
-        // column of word i0 + q * step: c0 + q * sr, wrapped into [0, ER)
-        const int c0 = i0 % ER, sr = step % ER;
-        uint32_t pending = 0;
-        int c = c0;
+            pending |= (i0 + q * step < n) ? 1u << q : 0u;
+        for (int polls = 0;; ++polls) {
+            uint64_t wv[B];
 #pragma unroll
-        for (int q = 0; q < B; ++q) {
-            if (i0 + q * step < n) {
-                if ((uint32_t)(wv[q] >> 32) == tag)
+            for (int q = 0; q < B; ++q)
+                wv[q] = i0 + q * step < n ? pub_load(pub + i0 + q * step) : 0;
+            int c = c0;
+#pragma unroll
+            for (int q = 0; q < B; ++q) {
+                if ((uint32_t)(wv[q] >> 32) == tag && ((pending >> q) & 1u)) {
                     atomicAdd(&acc[c], (int)(uint32_t)wv[q]);
-                else
-                    pending |= 1u << q;
+                    pending &= ~(1u << q);
+                }
+                c += sr;
+                c = c >= ER ? c - ER : c;
             }
-            c += sr;
-            c = c >= ER ? c - ER : c;
-        }
-        for (; pending; pending &= pending - 1) {
-            const int q = __builtin_ctz(pending), i = i0 + q * step;
-            uint64_t v = pub_load(pub + i);
-            for (int polls = 0; (uint32_t)(v >> 32) != tag; v = pub_load(pub + i)) {
-                if (++polls > kSpinLimit)
-                    return false;
-                __builtin_amdgcn_s_sleep(2);
-            }
-            atomicAdd(&acc[(c0 + q * sr) % ER], (int)(uint32_t)v);
+            if (!pending)
+                break;
+            if (polls >= kSpinLimit)
+                return false;
+            __builtin_amdgcn_s_sleep(2);
         }
     }
     return true;
@@ -192,17 +191,20 @@ __global__ __launch_bounds__(kLThreads) void layout_kernel(LayoutArgs a)
         for (int k = 0; k < KMAX; ++k) {
             const int e = ek[k];
             bad |= (e == -2);
+            int rep = 0;  // e already listed earlier in the row
 #pragma unroll
             for (int k2 = 0; k2 < k; ++k2)
-                dup |= (e >= 0 && ek[k2] == e);
-            if (e < 0)
-                continue;
-            __hip_atomic_fetch_or(reinterpret_cast<unsigned long long *>(&emask[w * E + e]), bit,
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_fetch_add(&ecnt[w * E + e], 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_fetch_add(&agg[e], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            rbits |= 1ull << div_by_magic(e, a.L_mul);
+                rep |= (e >= 0 && ek[k2] == e);
+            dup |= rep;
+            if (e >= 0) {
+                if (rep)  // the lane's bit is already set: the repeat is counted apart
+                    __hip_atomic_fetch_add(&ecnt[w * E + e], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                else
+                    __hip_atomic_fetch_or(reinterpret_cast<unsigned long long *>(&emask[w * E + e]),
+                                          bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                rbits |= 1ull << div_by_magic(e, a.L_mul);
+            }
         }
         rb[tid] = rbits;
         if (bad && part == 0)
@@ -211,7 +213,6 @@ __global__ __launch_bounds__(kLThreads) void layout_kernel(LayoutArgs a)
             const int r = __builtin_ctzll(m);
             __hip_atomic_fetch_or(reinterpret_cast<unsigned long long *>(&rmask[w * R + r]), bit,
                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_fetch_add(&agg[E + r], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         const uint64_t anydup = uniform64(__ballot(dup));
         if (lane == 0)
@@ -219,22 +220,40 @@ __global__ __launch_bounds__(kLThreads) void layout_kernel(LayoutArgs a)
     }
     __syncthreads();
 
-    // part 0 publishes the tile's counts at once; then per column the
-    // earlier waves' prefixes
+    // per column the earlier waves' prefixes and the tile's count (a wave's
+    // count: its lanes' bits plus the repeats), which part 0 publishes at once
     const uint32_t tag = s_tag;
     const bool go = !handover || s_go;
-    if (handover && go && part == 0) {
-        const uint64_t hi = (uint64_t)tag << 32;
-        uint64_t *prow = a.pub + (int64_t)tile * ER;
-        for (int c = tid; c < ER; c += blockDim.x)
-            pub_store(prow + c, hi | (uint32_t)agg[c]);
-    }
+    const bool publish = handover && go && part == 0;
+    const uint64_t hi = (uint64_t)tag << 32;
+    uint64_t *prow = a.pub + (int64_t)tile * ER;
     for (int c = tid; c < ER; c += blockDim.x) {
         int run = 0;
         for (int w2 = 0; w2 < cw; ++w2) {
             wpre[w2 * ER + c] = run;
-            run += c < E ? ecnt[w2 * E + c] : __popcll(rmask[w2 * R + (c - E)]);
+            run += c < E ? __popcll(emask[w2 * E + c]) + ecnt[w2 * E + c]
+                         : __popcll(rmask[w2 * R + (c - E)]);
         }
+        agg[c] = run;
+        if (publish)
+            pub_store(prow + c, hi | (uint32_t)run);
+    }
+
+    // is_token_in_rank rows of this block's tokens (contiguous: written as
+    // blocks, 16 bytes per thread per step where R allows); they need only
+    // the rank bits, so they go out before the wait for the earlier tiles
+    const int nt = p_hi - p_lo;
+    const int64_t row0 = (int64_t)(tile_base + p_lo) * R;
+    if ((R & 15) == 0) {
+        const int nq = R >> 4;
+        Walk it(tid, blockDim.x, nq);
+        for (int q = tid; q < nt * nq; q += blockDim.x, it.next())
+            *reinterpret_cast<u32x4 *>(a.is_token_in_rank + row0 + (int64_t)q * 16) =
+                rank_bytes16(rb[p_lo + it.row] >> (it.col * 16));
+    } else {
+        Walk it(tid, blockDim.x, R);
+        for (int i = tid; i < nt * R; i += blockDim.x, it.next())
+            a.is_token_in_rank[row0 + i] = (uint8_t)((rb[p_lo + it.row] >> it.col) & 1ull);
     }
 
     // the earlier tiles' counts (a batch of one tile: its own are the totals)
@@ -282,22 +301,8 @@ __global__ __launch_bounds__(kLThreads) void layout_kernel(LayoutArgs a)
             }
         }
 
-        // is_token_in_rank and pos_in_rank rows of this block's tokens are
-        // contiguous: written as blocks, 16 bytes per thread per step where
-        // R allows
-        const int nt = p_hi - p_lo;
-        const int64_t row0 = (int64_t)(tile_base + p_lo) * R;
-        if ((R & 15) == 0) {
-            const int nq = R >> 4;
-            Walk it(tid, blockDim.x, nq);
-            for (int q = tid; q < nt * nq; q += blockDim.x, it.next())
-                *reinterpret_cast<u32x4 *>(a.is_token_in_rank + row0 + (int64_t)q * 16) =
-                    rank_bytes16(rb[p_lo + it.row] >> (it.col * 16));
-        } else {
-            Walk it(tid, blockDim.x, R);
-            for (int i = tid; i < nt * R; i += blockDim.x, it.next())
-                a.is_token_in_rank[row0 + i] = (uint8_t)((rb[p_lo + it.row] >> it.col) & 1ull);
-        }
+        // pos_in_rank rows of this block's tokens are contiguous: written
+        // as blocks, 16 bytes per thread per step where R allows
         if ((R & 3) == 0) {
             const int nq = R >> 2;
             Walk it(tid, blockDim.x, nq);
