@@ -226,15 +226,23 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
 
     if (go && have) {
         // earlier tokens of the block: per rank lane, the tokens going to
-        // it; per entry lane, the entries with the same expert
+        // it; per entry lane, the entries with the same expert, and the
+        // earlier entries of the token's own row. Each token's entries are
+        // read at once and counted without a branch per entry (a read and
+        // a wait per entry cost the block's last wave ~3 us).
         int cr = 0, ce = 0, rep = 0;
-        for (int w2 = 0; w2 < w; ++w2) {
-            cr += (int)((tmask[w2] >> lane) & 1ull);
-            for (int k2 = 0; k2 < K; ++k2)
-                ce += (valid && tent[w2 * KMAX + k2] == (int)e);
+        const int ev = valid ? (int)e : -3;  // stored entries are >= -1
+        for (int w2 = 0; w2 <= w; ++w2) {
+            const bool earlier = w2 < w;
+            cr += earlier ? (int)((tmask[w2] >> lane) & 1ull) : 0;
+            const int *row = tent + w2 * KMAX;
+#pragma unroll
+            for (int k2 = 0; k2 < KMAX; ++k2) {
+                const int hit = (row[k2] == ev) & (k2 < K);
+                ce += earlier ? hit : 0;
+                rep += (!earlier && k2 < lane) ? hit : 0;
+            }
         }
-        for (int k2 = 0; k2 < K; ++k2)  // earlier entries of the token's own row
-            rep += (valid && k2 < lane && tent[w * KMAX + k2] == (int)e);
         const bool in_r = lane < R && ((mt >> lane) & 1ull);
         const int p = in_r ? pre[E + lane] + bef[E + lane] + cr : -1;
         const int slot = valid ? pre[(int)e] + bef[(int)e] + ce + rep : -1;
