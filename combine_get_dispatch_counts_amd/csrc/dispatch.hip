@@ -302,7 +302,7 @@ static int dispatch_blocks_per_cu()
 // Up to one round of waves, one launch paces the whole sweep; beyond, the
 // tokens go in chunks of consecutive tokens, each its own launch sweeping
 // its own rows, sized to the round the occupancy query reports for the
-// chunked kernel, at 9/10 of the set rate (each chunk's sweep shares HBM
+// chunked kernel, at 93% of the set rate (each chunk's sweep shares HBM
 // with the loads of its own rows). Unpaced, or when the query fails, one
 // launch takes all tokens. (One launch of all chunks' waves, each later
 // round's rows due after the estimated rows of the rounds before it on one
@@ -315,9 +315,11 @@ static int dispatch_blocks_per_cu()
 // check and stores unpaced), and the chunks' sweep rate as a fraction of
 // the set rate. Measured on the FP8 prefill (T = 16384, h = 7168, E = 256,
 // R = 64): four chunks of a full round 402-405 us against 413-414 us for
-// five of 7/8 of it; the best effective chunk rate ~5500 GB/s either way.
+// five of 7/8 of it; with four chunks the best effective chunk rate is
+// ~5670 GB/s (398-401 us; 5490: 402-406, 5850: 418-423), 93% of the FP8
+// default of 6100.
 constexpr int64_t kChunkRoundPermille = 1000;
-constexpr int64_t kChunkRatePermille = 900;
+constexpr int64_t kChunkRatePermille = 930;
 
 template <bool FP8, int NV>
 static void launch_dispatch_nv(const DispatchArgs &a, int cus, std::atomic<unsigned> *seq,

@@ -94,7 +94,7 @@ const char *epx_strerror(int code);
  * front, which HBM absorbs at sequential-write speed, where the same rows in
  * routing order arrive as random writes. A larger epx_dispatch is launched
  * as chunks of consecutive tokens that each fit, each sweeping its own rows
- * at 9/10 of the rate. Left unpaced: the permute alone (epx_dispatch with
+ * at 93% of the rate. Left unpaced: the permute alone (epx_dispatch with
  * send_x = NULL), which reads as many rows as it writes; a call whose row
  * bound (T*(K + min(K,R)) rows) is at most 256 MiB for bf16 or 128 MiB for
  * FP8 (such rows mostly stay in the memory-side cache during the launch, and
