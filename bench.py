@@ -16,10 +16,10 @@ the step's median time: each of the K timed steps runs right after a 512 MB
 read that flushes the memory-side cache (outside its HIP events), and the
 median of the K event-timed steps is ``ms_per_step`` / ``us_per_layer``; the
 same K steps launched back to back with no flush are reported as
-``warm_us_per_layer``. The sweep rates of the paced dispatch come from a
-calibration against this GPU's own fill rate (``--sweep-gbps`` sets them
-instead), and the step at the library's hand-tuned defaults is reported
-beside it. ``roofline`` covers the dominant kernel (the fused layout +
+``warm_us_per_layer``. The paced dispatch sweeps at the library's
+hand-tuned default rates (``--sweep-gbps`` sets others, or 'calibrate'),
+and the step at rates calibrated against this GPU's own fill rate is
+reported beside it (``calibrated_rates``). ``roofline`` covers the dominant kernel (the fused layout +
 dispatch) timed with HIP events on its stream; ``cpu_baseline`` times the
 CPU oracle on the same workload, single-threaded and with its token-parallel
 phases on the host's cores.
@@ -155,12 +155,14 @@ def cpu_baseline_record(inp, wl):
                                    f"{med_t * 1e3:.0f} ms each"}}
 
 
-def _loop_us(fn, n):
+def _loop_us(fn, n, warm=3):
     """Average microseconds per call of fn launched n times back to back on
-    the current stream (one event pair around all of them)."""
+    the current stream (one event pair around all of them), after `warm`
+    untimed calls."""
     import torch
 
-    fn()
+    for _ in range(warm):
+        fn()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -235,12 +237,15 @@ def other_workloads(n=20):
     comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
     row8 = h + 4 * (h // 128)
     lay_us = _graph_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay), n)
-    d_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs), n)
+    # measured on this workload: the first dozen or so launches in a process
+    # run up to 5% slower than later ones, so ten untimed calls first
+    d_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs), n,
+                    warm=10)
     d = epx.dispatch(x, tk, w, E, R, fp8=True, layout=lay, out=bufs)
-    c_us = _loop_us(lambda: epx.combine(y, d.pos_exp, w, out=comb), n)
+    c_us = _loop_us(lambda: epx.combine(y, d.pos_exp, w, out=comb), n, warm=10)
     fws = torch.zeros(max(epx.fused_workspace_size(T, K, E, R), 1), dtype=torch.uint8, device=dev)
     f_us = _loop_us(lambda: epx.dispatch_fused(x, tk, w, E, R, fp8=True, layout=lay, out=bufs,
-                                               workspace=fws), n)
+                                               workspace=fws), n, warm=10)
     assert epx.get_error() == 0
     d_bytes = (T * 2 * h + 12 * T * K + (n_rank + n_exp) * row8 + 4 * (n_rank + n_exp)
                + 12 * n_rank * K + 8 * T * K)
@@ -439,15 +444,15 @@ def other_workloads(n=20):
 # /tmp with TMPDIR=/tmp, <R> the repository root, <P> the output folder):
 PROFILE_RUNS = {
     "tr": "rocprofv3 --kernel-trace --stats --output-format csv -d <P>/tr -o run -- "
-          "python3 <R>/bench.py --steps 20 --warmup 5 --no-cpu-baseline --flush-mb 0 --other 0",
+          "python3 <R>/bench.py --steps 20 --warmup 5 --no-cpu-baseline --calibrated 0 --flush-mb 0 --other 0",
     "tro": "rocprofv3 --kernel-trace --stats --output-format csv -d <P>/tro -o run -- "
-           "python3 <R>/bench.py --steps 2 --warmup 1 --no-cpu-baseline --flush-mb 0 --graph 0 "
+           "python3 <R>/bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrated 0 --flush-mb 0 --graph 0 "
            "--other 1",
     "pf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <P>/pf -o run -- "
-          "python3 <R>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --flush-mb 0 --graph 0 "
+          "python3 <R>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrated 0 --flush-mb 0 --graph 0 "
           "--other 1 --calib-copy-mb 1024",
     "pw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <P>/pw -o run -- "
-          "python3 <R>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --flush-mb 0 --graph 0 "
+          "python3 <R>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrated 0 --flush-mb 0 --graph 0 "
           "--other 1 --calib-copy-mb 1024",
 }
 # the prefill launches the traffic record covers: (kernel, grid in threads)
@@ -624,14 +629,17 @@ def main():
                     help="also time a 1 GiB device copy and fill (the same run's ceilings)")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="MALL flush: a read of this many MB before every timed step (0: none)")
-    ap.add_argument("--sweep-gbps", default="calibrate",
-                    help="paced store sweep rates: 'calibrate' (from a fill of this GPU), "
-                         "'bf16,fp8' in GB/s, or 0,0 (unpaced)")
+    ap.add_argument("--sweep-gbps", default="default",
+                    help="paced store sweep rates: 'default' (the library's hand-tuned "
+                         "rates), 'calibrate' (from a fill of this GPU), 'bf16,fp8' in GB/s, "
+                         "or 0,0 (unpaced)")
+    ap.add_argument("--calibrated", type=int, default=1,
+                    help="with the default rates, also time the step at calibrated rates")
     args = ap.parse_args()
-    if args.sweep_gbps != "calibrate":
+    if args.sweep_gbps not in ("default", "calibrate"):
         sweep = tuple(int(v) for v in args.sweep_gbps.split(","))
         if len(sweep) != 2:
-            raise SystemExit("--sweep-gbps takes 'calibrate' or two rates: bf16,fp8")
+            raise SystemExit("--sweep-gbps takes 'default', 'calibrate' or two rates: bf16,fp8")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the path; runs on more than one GPU "
               "are not supported (use --gpus 1)", file=sys.stderr)
@@ -647,11 +655,18 @@ def main():
     dev = torch.device("cuda", 0)
     default_rates = epx.get_sweep_rate()
     fill_gbps = None
-    if args.sweep_gbps == "calibrate":
+
+    def calibrate():
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        fill_gbps = epx.calibrate_sweep_rate(scratch)
+        gbps = epx.calibrate_sweep_rate(scratch)
         del scratch
+        return gbps
+
+    if args.sweep_gbps == "calibrate":
+        fill_gbps = calibrate()
         sweep = epx.get_sweep_rate()
+    elif args.sweep_gbps == "default":
+        sweep = default_rates
     else:
         epx.set_sweep_rate(*sweep)
     inp = synth.make_inputs(3)
@@ -775,13 +790,21 @@ def main():
                                                                 out=lay_buf))
     assert epx.get_error() == 0
 
-    # the same step at the hand-tuned default rates, for comparison with the
-    # calibrated ones (flushed median, as the headline)
-    hand = None
+    # the same step at the other kind of rates (flushed median, as the
+    # headline): the hand-tuned defaults beside calibrated rates, or rates
+    # calibrated on this GPU beside the defaults (a fill timed with events,
+    # which a profiler's per-launch work slows down: profiled runs skip it)
+    hand = calib = None
     if args.sweep_gbps == "calibrate":
         epx.set_sweep_rate(*default_rates)
         hand = {"bf16": default_rates[0], "fp8": default_rates[1],
                 "us_per_layer": round(_median_us(_flushed_steps(step, args.steps, flush, 3)), 2)}
+        epx.set_sweep_rate(*sweep)
+    elif args.sweep_gbps == "default" and args.calibrated:
+        cal_fill = calibrate()
+        cal = epx.get_sweep_rate()
+        calib = {"bf16": cal[0], "fp8": cal[1], "calibration_fill_gbps": cal_fill,
+                 "us_per_layer": round(_median_us(_flushed_steps(step, args.steps, flush, 3)), 2)}
         epx.set_sweep_rate(*sweep)
 
     # the step captured in a HIP graph (GRAPH_STEPS steps per graph, as a
@@ -892,9 +915,11 @@ def main():
         "frac_of_rw_kernel_ceiling": round(gbs / ceil["rw_kernel_gbs"], 4) if ceil else None,
         "graph_us_per_layer": round(graph_us, 2) if graph_us else None,
         "fused_kernel_us": round(fused_us, 2),
-        "sweep_gbps": {"mode": "calibrated" if fill_gbps else "set", "bf16": sweep[0],
-                       "fp8": sweep[1], "calibration_fill_gbps": fill_gbps},
+        "sweep_gbps": {"mode": {"calibrate": "calibrated", "default": "default"}.get(
+                           args.sweep_gbps, "set"),
+                       "bf16": sweep[0], "fp8": sweep[1], "calibration_fill_gbps": fill_gbps},
         "hand_tuned_rates": hand,
+        "calibrated_rates": calib,
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("fused_kernel"),
