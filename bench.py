@@ -460,7 +460,7 @@ PREFILL_KERNELS = {
     "dispatch_kernel": ("dispatch_kernel<false, 14, false>", 4096 * 64),
     "fused_kernel": ("fused_kernel<8, false, 14>", (4096 // 8) * 512),
 }
-_KERNEL_PREFIXES = ("dispatch", "combine", "layout", "ll_", "fill", "fused")
+_KERNEL_PREFIXES = ("dispatch", "combine", "layout", "ll_", "fill", "fused", "permute")
 
 
 def _short_name(name: str) -> str:
