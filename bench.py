@@ -425,6 +425,15 @@ def other_workloads(n=20):
     comb = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
     lay_us = _graph_us(lambda: epx.get_dispatch_layout(tk, E, R, workspace=ws, out=lay), n)
     d_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs), n)
+    # the same dispatch unpaced: this workload holds exactly one round of
+    # waves (8 per SIMD), where a wave that found no place would wait behind
+    # paced ones; paced must stay the faster
+    rates = epx.get_sweep_rate()
+    epx.set_sweep_rate(0, 0)
+    try:
+        du_us = _loop_us(lambda: epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs), n)
+    finally:
+        epx.set_sweep_rate(*rates)
     d = epx.dispatch(x, tk, w, E, R, layout=lay, out=bufs)
     c_us = _loop_us(lambda: epx.combine(y, d.pos_exp, w, out=comb), n)
     assert epx.get_error() == 0
@@ -434,6 +443,8 @@ def other_workloads(n=20):
         "n_rank_rows": n_rank, "n_expert_rows": n_exp,
         "max_tokens_per_expert": int(lay.num_tokens_per_expert.max()),
         "layout_us": round(lay_us, 2), "dispatch": rec(d_us, by["dispatch"]),
+        "dispatch_unpaced": rec(du_us, by["dispatch"]),
+        "paced_not_slower": d_us <= du_us,
         "combine": rec(c_us, by["combine"]), "step_us": round(lay_us + d_us + c_us, 2),
         "step_gbs": round(compulsory_step_bytes(T, h, K, R, n_rank, n_exp) / ((lay_us + d_us + c_us) * 1e-6) / 1e9, 1)}
     return out
