@@ -15,8 +15,8 @@
 // for anything; every block then reads all tiles' words -- their sum is the
 // totals, from which it scans the offsets, and the tiles before its own give
 // its prefix -- while it counts its own tile's tokens before its first token
-// in LDS, and the entries of its earlier tokens from the rows its waves
-// hold. No ordering between different addresses is relied on, and words
+// in LDS, and the entries of its own earlier tokens from the rank bits and
+// entries its waves leave in LDS. No ordering between different addresses is relied on, and words
 // left in the workspace by earlier calls, of any shape, carry older tags.
 // Blocks write their own tokens' rows of is_token_in_rank, pos_in_rank and
 // slot_in_expert, and the channel_prefix columns whose channel ends in their

@@ -20,9 +20,11 @@
 //     bitmap, a token's rank in its wave a popcount of the bits below it,
 //     and the earlier waves' counts give the rest of the tile's prefix.
 //   - Part 0 of each tile publishes the tile's E + R counts; every block
-//     then loads the words of all earlier tiles at once, spread over all of
-//     its threads (tile-major, so the loads are coalesced), and adds them
-//     into LDS; one more block does the same over all tiles for the totals,
+//     writes its is_token_in_rank rows (they need only the rank bits), then
+//     loads the words of all earlier tiles at once, spread over all of its
+//     threads (tile-major, so the loads are coalesced; words still stale are
+//     loaded again together), and adds them into LDS; one more block does
+//     the same over all tiles for the totals,
 //     and writes the counts, offsets and totals while the tiles write rows.
 //     A batch of one tile needs no hand-over: its part 0 writes the totals
 //     from its own counts and the workspace is not touched.
