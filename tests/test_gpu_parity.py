@@ -57,6 +57,9 @@ def _edge_cases():
     cases.append(("one_expert", 1000, 1, 64, 8, 10, 0.0))
     cases.append(("max_experts", 600, 8, 512, 64, 3, 0.0))
     cases.append(("repeats", 300, 4, 16, 4, 4, 0.0))
+    # 512-token tiles (T > 4096) with eight counting waves each, every row
+    # likely to repeat an expert
+    cases.append(("repeats", 5000, 8, 32, 8, 7, 0.0))
     cases.append(("many_channels", 100, 2, 8, 4, 1000, 0.0))
     return cases
 
