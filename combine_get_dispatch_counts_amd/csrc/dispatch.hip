@@ -75,6 +75,7 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(DispatchArgs a)
 // once, each element is quantised once, and a decode batch's few tokens
 // still spread their work over many waves.
 constexpr int kLLWaves = 8;
+constexpr int kLLHistBatch = 2;
 
 // Tokens per block of the low-latency kernel for a batch of T tokens.
 inline int ll_tokens_per_block(int T)
@@ -114,19 +115,30 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a,
     if (wj == 0 && lane < a.K)
         blk_e[j * a.K + lane] = (int)ek;  // -1 past the last token
     __syncthreads();
+    // kLLHistBatch entries per thread in flight together (clamped, always
+    // valid addresses, masked afterwards) instead of a load and a wait per
+    // entry: T = 128 / 512 / 1024 take 5.42 / 9.33 / 15.8 us against 5.48 /
+    // 9.6 / 16.2 (four at a time, with redundant clamped loads at T = 128,
+    // was slower)
     const int64_t n_ent = (int64_t)a.T * a.K, before = (int64_t)t0 * a.K;
-    for (int64_t i = tid; i < n_ent; i += nthreads) {
-        const int64_t e = a.topk_idx[i];
-        if (e == -1)
-            continue;
-        if (e < 0 || e >= a.E) {
-            if (blockIdx.x == 0)
-                flag_error(a.err, EPX_DEV_BAD_ROUTE);
-            continue;
+    for (int64_t i0 = tid; i0 < n_ent; i0 += (int64_t)kLLHistBatch * nthreads) {
+        int64_t ev[kLLHistBatch];
+#pragma unroll
+        for (int q = 0; q < kLLHistBatch; ++q)
+            ev[q] = a.topk_idx[min(i0 + (int64_t)q * nthreads, n_ent - 1)];
+#pragma unroll
+        for (int q = 0; q < kLLHistBatch; ++q) {
+            const int64_t i = i0 + (int64_t)q * nthreads, e = ev[q];
+            if (i < n_ent && e != -1) {
+                if (e >= 0 && e < a.E) {
+                    atomicAdd(&hist_all[e], 1);
+                    if (i < before)
+                        atomicAdd(&hist_before[e], 1);
+                } else if (blockIdx.x == 0) {
+                    flag_error(a.err, EPX_DEV_BAD_ROUTE);
+                }
+            }
         }
-        atomicAdd(&hist_all[e], 1);
-        if (i < before)
-            atomicAdd(&hist_before[e], 1);
     }
     __syncthreads();
 
