@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kLayoutThreads) void fused_kernel(FusedArgs f)
     // this block is done: the last block of the grid opens the next call
     __syncthreads();
     if (tid == 0)
-        finish_call(l.hdr);
+        leave_call(l.hdr);
 }
 
 // Small batches (T <= kSmallMaxT): one block of kLayoutThreads per token,

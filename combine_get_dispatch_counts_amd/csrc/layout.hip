@@ -138,14 +138,19 @@ __global__ __launch_bounds__(kLThreads) void layout_kernel(LayoutArgs a)
         return;
     }
     const bool handover = a.ntiles > 1;
-    if (handover && tid == 0) {
-        uint32_t tag;
-        s_go = read_call_tag(a.hdr, &tag);
-        s_tag = tag;
-    }
+    unsigned long long head = 0;
+    unsigned int arrival = 0;
+    if (handover && tid == 0)
+        head = load_call(a.hdr);
 
-    // the totals block: every tile's published counts
+    // the totals block (there is one only with a hand-over): every tile's
+    // published counts
     if ((int)blockIdx.x == a.ntiles * a.subs) {
+        if (tid == 0) {
+            uint32_t tag;
+            s_go = enter_call(a.hdr, head, &tag, &arrival);
+            s_tag = tag;
+        }
         for (int c = tid; c < ER; c += blockDim.x)
             agg[c] = 0;
         __syncthreads();
@@ -156,9 +161,8 @@ __global__ __launch_bounds__(kLThreads) void layout_kernel(LayoutArgs a)
         } else {
             write_totals(a, agg, off);
         }
-        __syncthreads();
         if (tid == 0)
-            finish_call(a.hdr);
+            close_call(a.hdr, arrival);
         return;
     }
 
@@ -170,6 +174,11 @@ __global__ __launch_bounds__(kLThreads) void layout_kernel(LayoutArgs a)
     const bool counter = tid < tt_n;
     int ek[KMAX];
     load_row_experts<KMAX>(a, counter ? tile_base + tid : a.T, ek);  // -1 past the last token
+    if (handover && tid == 0) {  // after the tile's loads are out
+        uint32_t tag;
+        s_go = enter_call(a.hdr, head, &tag, &arrival);
+        s_tag = tag;
+    }
 
     for (int i = tid; i < cw * E; i += blockDim.x) {
         emask[i] = 0;
@@ -355,11 +364,8 @@ __global__ __launch_bounds__(kLThreads) void layout_kernel(LayoutArgs a)
             }
         }
     }
-    if (handover) {
-        __syncthreads();
-        if (tid == 0)
-            finish_call(a.hdr);
-    }
+    if (handover && tid == 0)
+        close_call(a.hdr, arrival);
 }
 
 }  // namespace

@@ -14,10 +14,10 @@
 // it carries the current call's tag, so a word left by an earlier call, of
 // any shape, reads as "not yet". The call tag is the call number in the
 // workspace head plus one; every block reads it with one plain load at its
-// start, and the last block of the grid to finish moves the number on (a
-// second counter in the head counts finished blocks), so the number is fixed
-// for the whole launch. Every wait is bounded: a word that stays unpublished
-// too long sets EPX_DEV_WORKSPACE and the kernel ends anyway.
+// start, and a second counter in the head makes sure the number moves on
+// only once every block of the launch holds it (two ways, below), so the
+// next launch sees the new one. Every wait is bounded: a word that stays
+// unpublished too long sets EPX_DEV_WORKSPACE and the kernel ends anyway.
 #pragma once
 
 #include "epx_device.h"
@@ -38,6 +38,20 @@ __device__ __forceinline__ uint64_t pub_load(const uint64_t *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Two ways to move the call number on, which leave the head alike between
+// calls (second counter 0, low half 0), so launches of either kind can
+// share a workspace:
+//  - count out (read_call_tag at the start, leave_call at the end): the
+//    last block of the grid to finish moves the number on. Each block's
+//    count goes out at its own end, spread over the launch; used by the
+//    fused launch, whose hundreds of blocks counting at once would queue
+//    on the word while their rows load.
+//  - count in (load_call, enter_call once the block's loads are out,
+//    close_call at the end): the last block to count in moves the number
+//    on when it ends. No block ends waiting for a round trip on the word;
+//    used by the layout kernel (a few dozen blocks), where that round trip
+//    was on the critical path.
+
 // The call's tag from the workspace head; false if the head was not left
 // by a finished call (its low half is always 0 between calls).
 __device__ __forceinline__ bool read_call_tag(const LayoutHdr *hdr, uint32_t *tag)
@@ -48,12 +62,45 @@ __device__ __forceinline__ bool read_call_tag(const LayoutHdr *hdr, uint32_t *ta
     return (uint32_t)v == 0u;
 }
 
-// Called by one thread of every block when the block is done: the last one
-// of the grid opens the next call.
-__device__ __forceinline__ void finish_call(LayoutHdr *hdr)
+// Counting out: called by one thread of every block when the block is done;
+// the last one of the grid opens the next call.
+__device__ __forceinline__ void leave_call(LayoutHdr *hdr)
 {
     const unsigned int n = atomicAdd(&hdr->done, 1u);
     if (n == gridDim.x - 1) {
+        __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        atomicAdd(&hdr->calls, 1ull << 32);
+    }
+}
+
+// Counting in: the workspace head, loaded once by one thread of a block at
+// its start.
+__device__ __forceinline__ unsigned long long load_call(const LayoutHdr *hdr)
+{
+    return __hip_atomic_load(&hdr->calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The call's tag from the loaded head; false if the head was not left by a
+// finished call (its low half is always 0 between calls). The block is then
+// counted in: *arrival is how many blocks of the grid counted in before it.
+// The increment is made from the loaded value (its low half, 0 in every
+// state a finished call leaves), so it cannot go out before the head's load
+// has returned: once the count reaches the grid, every block holds its tag.
+__device__ __forceinline__ bool enter_call(LayoutHdr *hdr, unsigned long long head,
+                                           uint32_t *tag, unsigned int *arrival)
+{
+    *tag = (uint32_t)(head >> 32) + 1u;
+    *arrival = atomicAdd(&hdr->done, 1u + ((uint32_t)head & 1u));
+    return (uint32_t)head == 0u;
+}
+
+// Called by the block's counting-in thread when the block is done: the last
+// block to have counted in moves the call number on (every block of the grid
+// read it before). The count's round trip has long completed by then, so no
+// block ends waiting for it.
+__device__ __forceinline__ void close_call(LayoutHdr *hdr, unsigned int arrival)
+{
+    if (arrival == gridDim.x - 1) {
         __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         atomicAdd(&hdr->calls, 1ull << 32);
     }

@@ -196,8 +196,10 @@ def test_fused_kernel_many_channels(C_kind):
 def test_fused_shares_workspace_with_layout():
     """One workspace for fused calls (small batches, which do not touch it,
     and one-launch / two-launch ones, which do) and two-launch layout calls
-    in turn. After every call the counters are ready: no arrival pending,
-    no finished-block count left, the call number never going back."""
+    in turn (the fused launch counts its blocks out as they finish, the
+    layout kernel counts them in as they read the call number). After every
+    call the counters are ready: no arrival pending, the second counter back
+    at zero, the call number never going back."""
     import combine_get_dispatch_counts_amd as epx
 
     E, R, K, h = 64, 8, 6, 512
@@ -206,10 +208,10 @@ def test_fused_shares_workspace_with_layout():
 
     def counters(what):
         nonlocal last
-        head = ws[:128].cpu().numpy()  # calls << 32 | arrivals at byte 0; finished blocks at 64
+        head = ws[:128].cpu().numpy()  # calls << 32 | arrivals at byte 0; second counter at 64
         calls = int(head[:8].view(np.uint64)[0])
         assert calls & 0xFFFFFFFF == 0, f"arrivals pending after {what}: {calls:#x}"
-        assert int(head[64:68].view(np.uint32)[0]) == 0, f"finished-block count left by {what}"
+        assert int(head[64:68].view(np.uint32)[0]) == 0, f"block count left by {what}"
         assert calls >> 32 >= last, f"call number went back after {what}"
         last = calls >> 32
 
