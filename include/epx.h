@@ -176,9 +176,9 @@ size_t epx_ll_size_hint(int max_tokens_per_rank, int h, int R, int E, int fp8);
  *      totals_host_mapped          optional host-pinned int32[2]
  *                                  (hipHostMalloc) that also receives totals;
  *                                  valid once the stream has been synchronised
- * ws:  device workspace of epx_workspace_size bytes (0 when T = 0): tile
- *      tickets and the per-tile counts that later tiles read for their
- *      prefix. Zero-fill it before its first use; every call leaves it
+ * ws:  device workspace of epx_workspace_size bytes (0 when T = 0): a
+ *      call number and a block counter, then the per-tile counts that
+ *      later tiles read for their prefix (tagged with the call number). Zero-fill it before its first use; every call leaves it
  *      ready for the next one (also across graph replays), so it is
  *      allocated and cleared once. Calls that share a workspace must not
  *      overlap. A workspace found in another state sets EPX_DEV_WORKSPACE,
