@@ -60,6 +60,18 @@ def test_sweep_size_threshold_edges(T, fp8):
     _check_rates(3, False, fp8, T)
 
 
+@pytest.mark.parametrize("cfg,fp8,T", [
+    (5, True, 10000),   # FP8, 64 ranks: three chunks of 3334, 3334 and 3332 tokens
+    (3, False, 6001),   # bf16, h = 7168: two chunks of 3001 and 3000 tokens
+])
+def test_sweep_ragged_chunks(cfg, fp8, T):
+    """Dispatches launched in chunks of unequal size (T not a multiple of
+    the chunk count, so the last chunk's rows are placed by the estimate
+    with its own token count): the same bytes at every rate, and the
+    oracle's."""
+    _check_rates(cfg, False, fp8, T)
+
+
 def _check_rates(cfg, fused, fp8, T_override=None):
     import combine_get_dispatch_counts_amd as epx
 
