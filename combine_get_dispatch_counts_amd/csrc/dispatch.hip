@@ -400,17 +400,29 @@ hipError_t launch_ll_dispatch(const LLArgs &a, bool fp8, hipStream_t stream)
     return hipGetLastError();
 }
 
+// LDS reserved by each one-wave block of the permute (the kernel uses none),
+// capping the blocks that share a compute unit's 160 KB and so the rows in
+// flight. Measured on MI355X: bf16 rows of h = 7168 (29 811 rows into 8
+// experts) 161 us at the 20 blocks per CU their registers allow, 154 us at
+// five (three: 160 us); rows of h = 4096 (40 960 rows) 124 us at 32, 119 us
+// at eight. FP8 rows, which carry scale rows, are fastest uncapped (81 us;
+// 85 at five).
+constexpr size_t kPermuteLdsLarge = 32768;  // rows over 512 vectors: 5 per CU
+constexpr size_t kPermuteLdsSmall = 20480;  // rows up to 512 vectors: 8 per CU
+
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream)
 {
     if (a.N == 0)
         return hipSuccess;
     const dim3 grid((unsigned)a.N), block(kWave);
-    if (a.row_vecs <= 8 * kWave)
-        hipLaunchKernelGGL(permute_kernel<8>, grid, block, 0, stream, a);
+    const bool small = a.row_vecs <= 8 * kWave;
+    const size_t lds = a.side_vecs > 0 ? 0 : small ? kPermuteLdsSmall : kPermuteLdsLarge;
+    if (small)
+        hipLaunchKernelGGL(permute_kernel<8>, grid, block, lds, stream, a);
     else if (a.row_vecs <= 14 * kWave)
-        hipLaunchKernelGGL(permute_kernel<14>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL(permute_kernel<14>, grid, block, lds, stream, a);
     else
-        hipLaunchKernelGGL(permute_kernel<16>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL(permute_kernel<16>, grid, block, lds, stream, a);
     return hipGetLastError();
 }
 
