@@ -110,22 +110,29 @@ __global__ __launch_bounds__(kLLWaves * kWave) void ll_dispatch_kernel(LLArgs a,
     const int nslices = (nitems + per - 1) / per;
     row.load(src, wj * per, have_token ? nitems : 0);  // zeros past the row
 
+    // kLLHistBatch entries per thread in flight together (clamped, always
+    // valid addresses, masked afterwards) instead of a load and a wait per
+    // entry: T = 128 / 512 / 1024 take 5.42 / 9.33 / 15.8 us against 5.48 /
+    // 9.6 / 16.2 (four at a time, with redundant clamped loads at T = 128,
+    // was slower). The first batch goes out with the token's own entries,
+    // before the LDS is cleared, so both loads' latencies overlap.
+    const int64_t n_ent = (int64_t)a.T * a.K, before = (int64_t)t0 * a.K;
+    int64_t ev[kLLHistBatch];
+#pragma unroll
+    for (int q = 0; q < kLLHistBatch; ++q)
+        ev[q] = n_ent > 0 ? a.topk_idx[min((int64_t)tid + (int64_t)q * nthreads, n_ent - 1)] : -1;
+
     for (int i = tid; i < 2 * a.E; i += nthreads)
         hist[i] = 0;
     if (wj == 0 && lane < a.K)
         blk_e[j * a.K + lane] = (int)ek;  // -1 past the last token
     __syncthreads();
-    // kLLHistBatch entries per thread in flight together (clamped, always
-    // valid addresses, masked afterwards) instead of a load and a wait per
-    // entry: T = 128 / 512 / 1024 take 5.42 / 9.33 / 15.8 us against 5.48 /
-    // 9.6 / 16.2 (four at a time, with redundant clamped loads at T = 128,
-    // was slower)
-    const int64_t n_ent = (int64_t)a.T * a.K, before = (int64_t)t0 * a.K;
     for (int64_t i0 = tid; i0 < n_ent; i0 += (int64_t)kLLHistBatch * nthreads) {
-        int64_t ev[kLLHistBatch];
+        if (i0 != tid) {
 #pragma unroll
-        for (int q = 0; q < kLLHistBatch; ++q)
-            ev[q] = a.topk_idx[min(i0 + (int64_t)q * nthreads, n_ent - 1)];
+            for (int q = 0; q < kLLHistBatch; ++q)
+                ev[q] = a.topk_idx[min(i0 + (int64_t)q * nthreads, n_ent - 1)];
+        }
 #pragma unroll
         for (int q = 0; q < kLLHistBatch; ++q) {
             const int64_t i = i0 + (int64_t)q * nthreads, e = ev[q];
