@@ -106,7 +106,12 @@ __device__ __forceinline__ void reduce_rows(const uint16_t *y, int h, int p, flo
 
 // Slices per wave and entries per load batch of each kernel.
 constexpr int kCombP = 1, kCombB = 8;        // one-stage: K entries per token
-constexpr int kPartP = 4, kPartB = 2;        // stage 1: about K/R entries per row
+// Stage 1 (about K/R entries per row): two slices per wave, one entry at a
+// time, 35 registers and the full 32 waves per CU. Measured at the prefill
+// shape: 144.9 us against 151.5 us for four slices of two entries (83
+// registers, 20 waves per CU); one slice per wave 181 us (each wave's chain
+// of metadata loads dominates); fewer waves per CU always slower.
+constexpr int kPartP = 2, kPartB = 1;
 constexpr int kFinalP = 1, kFinalB = 8;      // stage 2: up to R partial rows per token
 
 __global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a, int split)
@@ -188,8 +193,8 @@ __global__ __launch_bounds__(kWave) void combine_final_kernel(FinalArgs a, int s
 // gather faster; measured on MI355X at h = 7168: the combine 87.8 against
 // 86.7 us (T = 4096) and 356-363 against 349-358 us (T = 16384), the final
 // stage 80.0 against 78.6 us; level at h = 4096; 12 blocks or fewer slower.
-// The first stage (83 registers, 20 blocks) loses with any cap (12 blocks:
-// 152 -> 178 us).
+// The first stage, one entry per load batch, wants every wave it can hold
+// (20 blocks per CU: 146 -> 169 us).
 constexpr size_t kCombLdsBytes = 9216;
 
 // Waves per output row when each covers P slices of 64 column vectors.
