@@ -243,3 +243,48 @@ def test_permute_side_rows_and_errors():
     flags, out, _, src, _ = run(idx, n_out - 1)
     assert flags & _lib.DEV_OVERFLOW
     assert (out[n_out - 1:] == CANARY).all() and (src[n_out - 1:] == -9).all()
+
+
+@pytest.mark.parametrize("width", [8192, 14336, 16400, 32768])
+def test_permute_row_widths(width):
+    """epx_permute on rows with no side rows at the widths that pick each
+    row register shape (up to 512 vectors, up to 896, more, and rows that
+    take two register passes, one of them ragged): every row to each of its
+    local-expert blocks in received order, bit for bit, with its handle."""
+    import ctypes
+
+    import combine_get_dispatch_counts_amd as epx
+    from combine_get_dispatch_counts_amd import _lib
+
+    N, K, L = 700, 4, 6
+    rng = np.random.default_rng(width)
+    idx = rng.integers(-1, L, (N, K)).astype(np.int64)
+    rows = rng.integers(0, 256, (N, width), dtype=np.uint8)
+    o = oracle.layout(idx, L, 1)
+    n_out = int(o["totals"][1])
+    dev = torch.device("cuda")
+    say(f"epx_permute N={N} K={K} L={L}, {width}-byte rows")
+    tk = torch.from_numpy(idx).to(dev)
+    lay = epx.get_dispatch_layout(tk, L, 1)
+    out = torch.full((n_out + 2, width), CANARY, dtype=torch.uint8, device=dev)
+    src = torch.full((n_out + 2,), -9, dtype=torch.int32, device=dev)
+    pos = torch.empty((N, K), dtype=torch.int32, device=dev)
+    r = torch.from_numpy(rows).to(dev)
+    rc = _lib.load().epx_permute(epx.api._ctx(dev), ctypes.c_void_p(r.data_ptr()), width, None, 0,
+                                 ctypes.c_void_p(tk.data_ptr()), N, K, L,
+                                 ctypes.c_void_p(lay.exp_off.data_ptr()),
+                                 ctypes.c_void_p(lay.slot_in_expert.data_ptr()),
+                                 ctypes.c_void_p(out.data_ptr()), None,
+                                 ctypes.c_void_p(src.data_ptr()), n_out,
+                                 ctypes.c_void_p(pos.data_ptr()), epx.api._stream(dev))
+    assert rc == 0
+    assert epx.get_error() == 0
+    out, src, pos = host_bits(out), host_bits(src), host_bits(pos)
+    order = np.argsort(np.where(idx >= 0, idx, L).ravel(), kind="stable")[:n_out]
+    want_src = (order // K).astype(np.int32)
+    _eq(src[:n_out], want_src, "src_row")
+    _eq(out[:n_out], rows[want_src], "rows")
+    assert (out[n_out:] == CANARY).all() and (src[n_out:] == -9).all()
+    want_pos = np.full(N * K, -1, np.int32)
+    want_pos[order] = np.arange(n_out, dtype=np.int32)
+    _eq(pos.ravel(), want_pos, "pos")
