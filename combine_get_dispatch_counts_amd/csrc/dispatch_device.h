@@ -451,7 +451,9 @@ __device__ __forceinline__ Dests token_dests(const DispatchArgs &a, int t, int64
 // destination. nsend: the number of send rows (the receive rows' place in
 // the sweep; 0 without a send buffer). The wave's sweep starts now, unless
 // the wave is late (it entered the kernel at t_entry, more than a.late_ticks
-// after block 0): then it stores unpaced. CHUNKED: the launch is one chunk
+// after block 0): then it stores unpaced. The schedule starts when the wave
+// gets here, but no earlier than a.start_ticks after its entry. CHUNKED: the
+// launch is one chunk
 // [a.t_begin, a.t_begin + a.t_count) of the tokens, and the lanes' segments
 // are read from the layout offsets.
 template <bool FP8, bool CHUNKED = false, typename Row>
@@ -460,7 +462,8 @@ __device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row
                                                int64_t recv_r, int64_t nsend, uint64_t t_entry)
 {
     typename std::conditional<CHUNKED, SweepChunk, Sweep>::type sw;
-    sw.t0 = wall_clock64();
+    const uint64_t ready = wall_clock64(), start = t_entry + a.start_ticks;
+    sw.t0 = ready > start ? ready : start;
     sw.bpt = a.sweep_bpt;
     sw.nsend = nsend;
     sw.row_bytes = FP8 ? (int64_t)a.h + 4 * (int64_t)scale_stride(a.h) : 2 * (int64_t)a.h;

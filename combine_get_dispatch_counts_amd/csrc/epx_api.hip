@@ -350,6 +350,8 @@ static int dispatch_args(epx_ctx *ctx, const uint16_t *x, int h, const int64_t *
     // late waves: an eighth of the longest sweep the call can have, kept
     // within [4, 16] microseconds of the wall clock
     a.stamps = ctx->dev->stamp;
+    a.start_ticks = 0;
+    a.wclk_per_us = (uint32_t)(ctx->wclk_khz / 1000);
     if (a.sweep_bpt) {
         const int64_t lo = (int64_t)ctx->wclk_khz * 4 / 1000, hi = (int64_t)ctx->wclk_khz * 16 / 1000;
         int64_t lt = bound / a.sweep_bpt / 8;

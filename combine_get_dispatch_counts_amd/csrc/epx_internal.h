@@ -63,6 +63,31 @@ constexpr int64_t kSweepMinBytesFp8 = 128ll << 20;
 // longer row is stored one pass at a time and is left unpaced.
 constexpr int kSweepMaxChannels = 8192;
 
+// The fused launch's schedule. A paced wave holds each row until its place
+// in the sweep falls due, counted from the start of its schedule. A fused
+// wave is ready only once its block's layout hand-over is complete, 12-20 us
+// in at the prefill shape, and waves whose schedules start at such different
+// times blur the front; a schedule started before the wave is ready makes
+// its first rows overdue, and they go out together as random writes. So a
+// fused wave starts its schedule when it is ready but no earlier than
+// kFusedStartUs plus the time the launch's x rows take at its sweep rate
+// after its entry (18 us at the prefill shape), by which time most blocks
+// are ready: the front is sharp and the sweep keeps up at a higher rate,
+// kFusedRatePermille of the set one. Measured on MI355X (T = 4096, h = 7168,
+// E = 256, R = 32, top-8; fused step, flushed / back to back): 257.4 /
+// 253.7 us started when ready at 6300 GB/s; 252.1-252.4 / 249.7-250.6 us
+// from 18 us at 6600; at 6700 from 16 us the back-to-back step fell over
+// (270 us) and from 18-20 us held (247-249 / 250-252).
+constexpr int64_t kFusedStartUs = 9;
+constexpr int64_t kFusedRatePermille = 1048;
+
+// Ticks for n_tokens rows of h bf16 channels at bpt bytes per tick (0 when
+// unpaced).
+inline uint32_t load_ticks(int64_t n_tokens, int h, uint32_t bpt)
+{
+    return bpt ? (uint32_t)(n_tokens * 2 * (int64_t)h / bpt) : 0u;
+}
+
 // Calibration (epx_calibrate_sweep_rate): the sweep rates as a fraction of
 // the same device's sequential fill rate, measured with launch_fill_lines
 // over a buffer larger than the memory-side cache: the defaults above over
@@ -159,6 +184,12 @@ struct DispatchArgs {
     unsigned long long *stamps;
     int stamp_slot;
     uint32_t late_ticks;
+    // Where a paced wave's schedule starts: when the wave has its
+    // destinations, but no earlier than start_ticks after it entered the
+    // kernel (0 but for the fused launch). wclk_per_us: wall-clock ticks per
+    // microsecond.
+    uint32_t start_ticks;
+    uint32_t wclk_per_us;
 };
 
 // Launch the dispatch (cus: compute units of the device). The sweep is paced

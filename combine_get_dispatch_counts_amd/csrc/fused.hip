@@ -440,6 +440,12 @@ hipError_t launch_fused_k(const FusedArgs &f, std::atomic<unsigned> *seq, hipStr
     }
     FusedArgs g = f;
     g.disp.stamp_slot = next_stamp_slot(seq);
+    if (g.disp.sweep_bpt) {
+        const uint32_t bpt = (uint32_t)((int64_t)g.disp.sweep_bpt * kFusedRatePermille / 1000);
+        g.disp.sweep_bpt = bpt > 0 ? bpt : 1u;
+        g.disp.start_ticks = (uint32_t)(kFusedStartUs * g.disp.wclk_per_us) +
+                             load_ticks(g.disp.T, g.disp.h, g.disp.sweep_bpt);
+    }
     hipLaunchKernelGGL((fused_kernel<KMAX, FP8, NV>), dim3((unsigned)blocks),
                        dim3(kLayoutThreads), lds, stream, g);
     return hipGetLastError();
