@@ -48,9 +48,13 @@
 // every block waits for finished counting 5 us later; loaded after the
 // publish, they still overlap the hand-over. Every wait is bounded. Each
 // wave then stores its token's rows on the paced sweep (dispatch_device.h),
-// its schedule starting when its block's hand-over is complete (a shared
-// start time was measured: the rows due before most blocks are ready go out
-// as one random burst).
+// its schedule starting when its block's hand-over is complete but no
+// earlier than a fixed offset after its own entry (kFusedStartUs plus the
+// launch's x-row time), at kFusedRatePermille of the set rate: most blocks
+// are ready by then, so the front starts sharp instead of spread over the
+// hand-over's 12-20 us (a start shared by all blocks from block 0's time was
+// measured too: blocks ready after it find rows overdue, which go out as one
+// random burst).
 #include <atomic>
 
 #include "dispatch_device.h"
