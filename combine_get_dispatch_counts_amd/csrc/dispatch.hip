@@ -334,9 +334,10 @@ static int dispatch_blocks_per_cu()
 // check and stores unpaced), and the chunks' sweep rate as a fraction of
 // the set rate. Measured on the FP8 prefill (T = 16384, h = 7168, E = 256,
 // R = 64): four chunks of a full round 402-405 us against 413-414 us for
-// five of 7/8 of it; with four chunks the best effective chunk rate is
-// ~5670 GB/s (398-401 us; 5490: 402-406, 5850: 418-423), 93% of the FP8
-// default of 6100.
+// five of 7/8 of it; with four chunks, their schedules started when ready,
+// the best effective chunk rate was ~5670 GB/s (398-401 us; 5490: 402-406,
+// 5850: 418-423); started 3 us plus the chunk's x-row time after entry,
+// 385-393 us at 93% of 6300-6500 (406 us at 93% of 6700).
 constexpr int64_t kChunkRoundPermille = 1000;
 constexpr int64_t kChunkRatePermille = 930;
 
@@ -349,6 +350,9 @@ static void launch_dispatch_nv(const DispatchArgs &a, int cus, std::atomic<unsig
     b.t_count = 0;
     b.stamp_slot = next_stamp_slot(seq);
     if (a.sweep_bpt == 0 || (int64_t)a.T <= (int64_t)dispatch_blocks_per_cu<FP8, NV, false>() * cus) {
+        if (b.sweep_bpt)
+            b.start_ticks = (uint32_t)(kDispatchStartUs[FP8] * b.wclk_per_us) +
+                            load_ticks(a.T, a.h, b.sweep_bpt);
         hipLaunchKernelGGL((dispatch_kernel<FP8, NV, false>), dim3(a.T), dim3(kWave), 0, stream, b);
         return;
     }
@@ -366,6 +370,8 @@ static void launch_dispatch_nv(const DispatchArgs &a, int cus, std::atomic<unsig
     for (int64_t t0 = 0; t0 < a.T; t0 += size) {
         b.t_begin = (int)t0;
         b.t_count = (int)(a.T - t0 < size ? a.T - t0 : size);
+        b.start_ticks = (uint32_t)(kDispatchStartUs[FP8] * b.wclk_per_us) +
+                        load_ticks(b.t_count, a.h, b.sweep_bpt);
         if (t0 > 0)
             b.stamp_slot = next_stamp_slot(seq);
         hipLaunchKernelGGL((dispatch_kernel<FP8, NV, true>), dim3((unsigned)b.t_count), dim3(kWave),

@@ -40,46 +40,53 @@ struct epx_ctx {
 namespace epx {
 
 // Default rates of the paced sweep of the high-throughput dispatch's row
-// stores (GB/s of destination rows), measured on MI355X at the prefill
-// shapes: just below the rate at which the paced front outruns the memory
-// system (bf16, T = 4096: 153.6 us at 6300, 166 at 6400; FP8: T = 4096
-// best at 6000-6100, T = 16384 in chunks 401.5-402.3 us at 6100, 407.5 at
-// 6000).
-constexpr int kSweepGBpsBf16 = 6300;
-constexpr int kSweepGBpsFp8 = 6100;
+// stores (GB/s of destination rows), with each launch's schedule started as
+// below, measured on MI355X: a step below the rate at which the paced front
+// outruns the memory system on some GPUs (bf16 prefill, T = 4096: 151-153
+// us at 6600-6700, 171 us at 6900 on one of two; FP8 at T = 16384 in chunks
+// 385 us at 6500, 406 at 6700).
+constexpr int kSweepGBpsBf16 = 6600;
+constexpr int kSweepGBpsFp8 = 6400;
 // Pacing delays every wave from its own start, which costs a few
 // microseconds; it repays that only once the rows no longer fit in the
 // memory-side cache (256 MiB on MI355X) and must reach HBM within the launch.
 // Calls whose row bound (T*(K + min(K,R)) rows) is at most this many bytes are
 // left unpaced. Measured at h = 7168, E = 256, R = 32, top-8: bf16 loses with
-// pacing up to T = 1024 (235 MB bound: 39.3 us against 36.7) and gains from
-// T = 1536 (352 MB: 57.7 against 61.7); FP8, whose quantisation keeps its
-// unpaced store rate lower, is level at T = 1024 (122 MB) and gains from
-// T = 1536 (182 MB: 42.3 against 43.4; 243 MB: 50.6 against 55.4).
-constexpr int64_t kSweepMinBytesBf16 = 256ll << 20;
+// pacing up to T = 1280 (235 MB bound: 39.3 us against 36.7 at T = 1024; 294
+// MB: 52.0 against 45.7 at T = 1280) and gains from T = 1536 (352 MB: 60.8
+// against 65.4); FP8, whose quantisation keeps its unpaced store rate lower,
+// gains from T = 1152 (137 MB: 31.2 against 35.1; 182 MB: 38.1 against 43.7
+// at T = 1536).
+constexpr int64_t kSweepMinBytesBf16 = 320ll << 20;
 constexpr int64_t kSweepMinBytesFp8 = 128ll << 20;
 // Channels of one register pass of the dispatch kernels' largest row
 // (bf16: 16 vectors of 8 channels per lane; FP8: 8 segments of 16): a
 // longer row is stored one pass at a time and is left unpaced.
 constexpr int kSweepMaxChannels = 8192;
 
-// The fused launch's schedule. A paced wave holds each row until its place
-// in the sweep falls due, counted from the start of its schedule. A fused
-// wave is ready only once its block's layout hand-over is complete, 12-20 us
-// in at the prefill shape, and waves whose schedules start at such different
-// times blur the front; a schedule started before the wave is ready makes
-// its first rows overdue, and they go out together as random writes. So a
-// fused wave starts its schedule when it is ready but no earlier than
-// kFusedStartUs plus the time the launch's x rows take at its sweep rate
-// after its entry (18 us at the prefill shape), by which time most blocks
-// are ready: the front is sharp and the sweep keeps up at a higher rate,
-// kFusedRatePermille of the set one. Measured on MI355X (T = 4096, h = 7168,
-// E = 256, R = 32, top-8; fused step, flushed / back to back): 257.4 /
-// 253.7 us started when ready at 6300 GB/s; 252.1-252.4 / 249.7-250.6 us
-// from 18 us at 6600; at 6700 from 16 us the back-to-back step fell over
-// (270 us) and from 18-20 us held (247-249 / 250-252).
+// Where a launch's schedule starts. A paced wave holds each row until its
+// place in the sweep falls due, counted from the start of its schedule.
+// Started when the wave is ready, the schedules of a launch's waves begin
+// over the spread of their row loads (and, in the fused kernel, of the
+// layout hand-over, 12-20 us in at the prefill shape): the front is blurred,
+// and a wave whose first rows are due before it is ready sends them out
+// together as random writes. So a wave starts its schedule when it is ready
+// but no earlier than a fixed time after its entry: kDispatchStartUs (the
+// dispatch kernel, one launch or a chunk; FP8 rows are quantised once
+// loaded, so they take longer) or kFusedStartUs (the fused kernel) plus the
+// time the launch's x rows take at its sweep rate. Most waves are ready by
+// then; the front starts sharp and keeps up at higher rates. Measured on
+// MI355X (HIP events, back to back unless flushed): prefill dispatch
+// (T = 4096, h = 7168, E = 256, R = 32, top-8) 154-156 us started when
+// ready at 6300 GB/s, 151-152 us from 1 us + x at 6600 (153 us from 3 us;
+// the front fell behind at 6900 on one of two GPUs: 171 us); fused step
+// flushed / back to back 257 / 254 us against 252-253 / 250 us from 9 us + x
+// at 6600; skewed dispatch (T = 8192, h = 4096, E = 64, R = 8, top-6) 130
+// against 124-125 us at 6600; FP8 at T = 4096 91-92 against 90 us (on the
+// 64-rank routing 97-99 against 92 us; 94 us from 1 us + x), FP8 in chunks
+// at T = 16384 400-403 against 386-392 us at 6400.
+constexpr int64_t kDispatchStartUs[2] = {1, 3};  // bf16, FP8
 constexpr int64_t kFusedStartUs = 9;
-constexpr int64_t kFusedRatePermille = 1048;
 
 // Ticks for n_tokens rows of h bf16 channels at bpt bytes per tick (0 when
 // unpaced).
@@ -91,9 +98,9 @@ inline uint32_t load_ticks(int64_t n_tokens, int h, uint32_t bpt)
 // Calibration (epx_calibrate_sweep_rate): the sweep rates as a fraction of
 // the same device's sequential fill rate, measured with launch_fill_lines
 // over a buffer larger than the memory-side cache: the defaults above over
-// the 6.75 TB/s that fill reached on the GPU they were measured on.
-constexpr int kCalibBf16Permille = 933;
-constexpr int kCalibFp8Permille = 904;
+// the 6.75 TB/s that fill reached on the GPU they were first measured on.
+constexpr int kCalibBf16Permille = 978;
+constexpr int kCalibFp8Permille = 948;
 constexpr size_t kCalibMinBytes = 512ull << 20;
 
 // The multiplier of floor(e / L) = e * m >> 20 for 0 <= e < 512 and

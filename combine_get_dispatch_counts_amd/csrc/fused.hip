@@ -50,9 +50,8 @@
 // wave then stores its token's rows on the paced sweep (dispatch_device.h),
 // its schedule starting when its block's hand-over is complete but no
 // earlier than a fixed offset after its own entry (kFusedStartUs plus the
-// launch's x-row time), at kFusedRatePermille of the set rate: most blocks
-// are ready by then, so the front starts sharp instead of spread over the
-// hand-over's 12-20 us (a start shared by all blocks from block 0's time was
+// launch's x-row time): most blocks are ready by then, so the front starts
+// sharp instead of spread over the hand-over's 12-20 us (a start shared by all blocks from block 0's time was
 // measured too: blocks ready after it find rows overdue, which go out as one
 // random burst).
 #include <atomic>
@@ -444,12 +443,9 @@ hipError_t launch_fused_k(const FusedArgs &f, std::atomic<unsigned> *seq, hipStr
     }
     FusedArgs g = f;
     g.disp.stamp_slot = next_stamp_slot(seq);
-    if (g.disp.sweep_bpt) {
-        const uint32_t bpt = (uint32_t)((int64_t)g.disp.sweep_bpt * kFusedRatePermille / 1000);
-        g.disp.sweep_bpt = bpt > 0 ? bpt : 1u;
+    if (g.disp.sweep_bpt)
         g.disp.start_ticks = (uint32_t)(kFusedStartUs * g.disp.wclk_per_us) +
                              load_ticks(g.disp.T, g.disp.h, g.disp.sweep_bpt);
-    }
     hipLaunchKernelGGL((fused_kernel<KMAX, FP8, NV>), dim3((unsigned)blocks),
                        dim3(kLayoutThreads), lds, stream, g);
     return hipGetLastError();

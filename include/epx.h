@@ -96,7 +96,7 @@ const char *epx_strerror(int code);
  * as chunks of consecutive tokens that each fit, each sweeping its own rows
  * at 93% of the rate. Left unpaced: the permute alone (epx_dispatch with
  * send_x = NULL), which reads as many rows as it writes; a call whose row
- * bound (T*(K + min(K,R)) rows) is at most 256 MiB for bf16 or 128 MiB for
+ * bound (T*(K + min(K,R)) rows) is at most 320 MiB for bf16 or 128 MiB for
  * FP8 (such rows mostly stay in the memory-side cache during the launch, and
  * the pacing delay would cost more than the ordering saves); rows of more
  * than 8192 channels (stored one register pass at a time). A rate above
@@ -109,7 +109,12 @@ const char *epx_strerror(int code);
  * the device holds fewer waves than its occupancy query reported -- stores
  * its rows unpaced instead of waiting for times already past, so such a
  * wave costs at most that much plus its own unpaced stores (outputs are
- * unaffected either way). Defaults, measured on MI355X: 6300 (bf16) and 6100 (FP8);
+ * unaffected either way). A wave's schedule starts when it is ready but no
+ * earlier than a fixed time after its entry -- 1 us (bf16 dispatch), 3 us
+ * (FP8 dispatch) or 9 us (the fused launch, whose waves first wait for the
+ * layout hand-over) plus the time the launch's x rows take at its rate --
+ * so the launch's front starts sharp. Defaults, measured on MI355X: 6600
+ * (bf16) and 6400 (FP8);
  * epx_calibrate_sweep_rate derives them from the device instead. The
  * setting is per context and read at each call. EPX_EINVAL for a NULL
  * context or a rate outside [0, EPX_MAX_SWEEP_GBPS]. */
