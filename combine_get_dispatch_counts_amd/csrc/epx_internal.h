@@ -41,11 +41,14 @@ namespace epx {
 
 // Default rates of the paced sweep of the high-throughput dispatch's row
 // stores (GB/s of destination rows), with each launch's schedule started as
-// below, measured on MI355X: a step below the rate at which the paced front
-// outruns the memory system on some GPUs (bf16 prefill, T = 4096: 151-153
-// us at 6600-6700, 171 us at 6900 on one of two; FP8 at T = 16384 in chunks
-// 385 us at 6500, 406 at 6700).
-constexpr int kSweepGBpsBf16 = 6600;
+// below, measured on MI355X: some 6% below the rate at which the paced
+// front outruns the memory system on some GPUs, where a launch turns into
+// random writes and takes 10-25% longer (bf16 prefill, T = 4096: 151-153 us
+// at 6600-6700 back to back, but 171 us at 6900 on one of two GPUs and
+// 163 us under a kernel-trace profiler at 6600, against 153 us at 6450;
+// FP8 at T = 16384 in chunks 385-389 us at 6400-6500, 394 at 6300, 406 at
+// 6700; FP8 at T = 4096 in one launch 88-90 us at 6400-6700, 96-97 at 6900).
+constexpr int kSweepGBpsBf16 = 6450;
 constexpr int kSweepGBpsFp8 = 6400;
 // Pacing delays every wave from its own start, which costs a few
 // microseconds; it repays that only once the rows no longer fit in the
@@ -99,7 +102,7 @@ inline uint32_t load_ticks(int64_t n_tokens, int h, uint32_t bpt)
 // the same device's sequential fill rate, measured with launch_fill_lines
 // over a buffer larger than the memory-side cache: the defaults above over
 // the 6.75 TB/s that fill reached on the GPU they were first measured on.
-constexpr int kCalibBf16Permille = 978;
+constexpr int kCalibBf16Permille = 956;
 constexpr int kCalibFp8Permille = 948;
 constexpr size_t kCalibMinBytes = 512ull << 20;
 

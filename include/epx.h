@@ -113,7 +113,7 @@ const char *epx_strerror(int code);
  * earlier than a fixed time after its entry -- 1 us (bf16 dispatch), 3 us
  * (FP8 dispatch) or 9 us (the fused launch, whose waves first wait for the
  * layout hand-over) plus the time the launch's x rows take at its rate --
- * so the launch's front starts sharp. Defaults, measured on MI355X: 6600
+ * so the launch's front starts sharp. Defaults, measured on MI355X: 6450
  * (bf16) and 6400 (FP8);
  * epx_calibrate_sweep_rate derives them from the device instead. The
  * setting is per context and read at each call. EPX_EINVAL for a NULL

@@ -16,7 +16,7 @@ from _gpu import host_bits, say
 
 pytestmark = pytest.mark.gpu
 
-DEFAULTS = (6600, 6400)  # the rates a new context starts with (include/epx.h)
+DEFAULTS = (6450, 6400)  # the rates a new context starts with (include/epx.h)
 
 
 def _run(epx, inp, fused, fp8, bufs, lay_buf, ws):
@@ -226,7 +226,7 @@ def test_calibrated_sweep_rate():
         b, f = epx.get_sweep_rate()
         say(f"calibration: fill {fill} GB/s -> sweep rates {b} (bf16), {f} (FP8)")
         assert 2000 < fill < 20000, fill
-        assert abs(b - fill * 0.978) <= 2, (b, fill)
+        assert abs(b - fill * 0.956) <= 2, (b, fill)
         assert abs(f - fill * 0.948) <= 2, (f, fill)
     finally:
         epx.set_sweep_rate(*prior)
