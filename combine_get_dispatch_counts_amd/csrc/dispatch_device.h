@@ -255,13 +255,14 @@ __device__ __forceinline__ int wave_min(int v)
 // in time: each wave stores its rows in ascending order of their place in
 // the output -- all send rows, then all receive rows -- and holds each row
 // back until the wall clock has run (row's byte offset in that order) /
-// sweep_bpt ticks since the wave became ready. All waves then write near
+// sweep_bpt ticks since its schedule started (when the wave became ready,
+// but no earlier than the launch's start offset). All waves then write near
 // one front that moves through the output at the set rate. Only the time of
 // each store changes, never what is stored; every wait is bounded by the
 // clock.
 struct Sweep {
     static constexpr bool kChunked = false;
-    uint64_t t0;        // wall clock when the wave became ready
+    uint64_t t0;        // wall clock at the start of the wave's schedule
     uint32_t bpt;       // bytes per tick (0: no pacing)
     int64_t nsend;      // send rows ahead of the receive rows in the sweep
     int64_t row_bytes;  // bytes of one destination row (FP8: codes and scale row)

@@ -89,10 +89,10 @@ const char *epx_strerror(int code);
  * (the fused call's one-launch shapes; epx_dispatch while T fits the device),
  * each wave stores its token's rows in ascending order of their place in
  * the output -- send rows, then receive rows -- and holds a row back until
- * its byte offset in that order, at this rate, has elapsed since the wave
- * became ready. The waves' stores then move through the output as one
- * front, which HBM absorbs at sequential-write speed, where the same rows in
- * routing order arrive as random writes. A larger epx_dispatch is launched
+ * its byte offset in that order, at this rate, has elapsed since the start
+ * of the wave's schedule (below). The waves' stores then move through the
+ * output as one front, which HBM absorbs at sequential-write speed, where
+ * the same rows in routing order arrive as random writes. A larger epx_dispatch is launched
  * as chunks of consecutive tokens that each fit, each sweeping its own rows
  * at 93% of the rate. Left unpaced: the permute alone (epx_dispatch with
  * send_x = NULL), which reads as many rows as it writes; a call whose row
