@@ -50,8 +50,8 @@ namespace epx {
 // 6700; FP8 at T = 4096 in one launch 88-90 us at 6400-6700, 96-97 at 6900).
 constexpr int kSweepGBpsBf16 = 6450;
 constexpr int kSweepGBpsFp8 = 6400;
-// Pacing delays every wave from its own start, which costs a few
-// microseconds; it repays that only once the rows no longer fit in the
+// Pacing holds every wave to its schedule, which costs a few microseconds;
+// it repays that only once the rows no longer fit in the
 // memory-side cache (256 MiB on MI355X) and must reach HBM within the launch.
 // Calls whose row bound (T*(K + min(K,R)) rows) is at most this many bytes are
 // left unpaced. Measured at h = 7168, E = 256, R = 32, top-8: bf16 loses with
@@ -87,7 +87,8 @@ constexpr int kSweepMaxChannels = 8192;
 // at 6600; skewed dispatch (T = 8192, h = 4096, E = 64, R = 8, top-6) 130
 // against 124-125 us at 6600; FP8 at T = 4096 91-92 against 90 us (on the
 // 64-rank routing 97-99 against 92 us; 94 us from 1 us + x), FP8 in chunks
-// at T = 16384 400-403 against 386-392 us at 6400.
+// at T = 16384 400-403 us started when ready at 6100 against 386-392 us
+// from 3 us + x at 6400.
 constexpr int64_t kDispatchStartUs[2] = {1, 3};  // bf16, FP8
 constexpr int64_t kFusedStartUs = 9;
 
