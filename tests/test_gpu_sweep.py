@@ -230,3 +230,13 @@ def test_calibrated_sweep_rate():
         assert abs(f - fill * 0.948) <= 2, (f, fill)
     finally:
         epx.set_sweep_rate(*prior)
+
+
+@pytest.mark.parametrize("fused,fp8", [(False, False), (False, True), (True, False), (True, True)])
+def test_sweep_widest_one_pass_rows(fused, fp8):
+    """Paced rows of 8192 channels, the widest one register pass holds (the
+    largest row shape of each kernel), on the prefill routing at T = 2048:
+    the same bytes at every rate, and the oracle's."""
+    from dataclasses import replace
+
+    _check_rates(replace(synth.WORKLOADS[3], h=8192), fused, fp8, 2048)
