@@ -450,13 +450,11 @@ __device__ __forceinline__ Dests token_dests(const DispatchArgs &a, int t, int64
 // token t's row (first pass loaded, not yet quantised) and its lanes as in
 // token_dests: checks, handle and metadata, then the row to every
 // destination. nsend: the number of send rows (the receive rows' place in
-// the sweep; 0 without a send buffer). The wave's sweep starts now, unless
-// the wave is late (it entered the kernel at t_entry, more than a.late_ticks
-// after block 0): then it stores unpaced. The schedule starts when the wave
-// gets here, but no earlier than a.start_ticks after its entry. CHUNKED: the
-// launch is one chunk
-// [a.t_begin, a.t_begin + a.t_count) of the tokens, and the lanes' segments
-// are read from the layout offsets.
+// the sweep; 0 without a send buffer). The wave's schedule starts when it
+// gets here, but no earlier than a.start_ticks after its entry (t_entry); a
+// late wave (entered more than a.late_ticks after block 0) stores unpaced.
+// CHUNKED: the launch is one chunk [a.t_begin, a.t_begin + a.t_count) of the
+// tokens, and the lanes' segments are read from the layout offsets.
 template <bool FP8, bool CHUNKED = false, typename Row>
 __device__ __forceinline__ void dispatch_token(const DispatchArgs &a, int t, Row &row,
                                                const uint16_t *xrow, int64_t e, int64_t send_r,

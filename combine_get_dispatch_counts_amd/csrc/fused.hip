@@ -51,9 +51,9 @@
 // its schedule starting when its block's hand-over is complete but no
 // earlier than a fixed offset after its own entry (kFusedStartUs plus the
 // launch's x-row time): most blocks are ready by then, so the front starts
-// sharp instead of spread over the hand-over's 12-20 us (a start shared by all blocks from block 0's time was
-// measured too: blocks ready after it find rows overdue, which go out as one
-// random burst).
+// sharp instead of spread over the hand-over's 12-20 us (a start shared by
+// all blocks, from block 0's entry, was measured too: blocks ready after it
+// find rows overdue, which go out as one random burst).
 #include <atomic>
 
 #include "dispatch_device.h"
